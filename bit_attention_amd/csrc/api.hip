@@ -1,0 +1,110 @@
+// api.hip — the extern "C" boundary of libsage_fp4.so (declared in include/sage_fp4.h).
+// Host-side argument validation happens before anything is enqueued; each entry point then
+// launches exactly one kernel on the caller's stream and reports launch errors.
+#include <cstdint>
+
+#include "../../include/sage_fp4.h"
+#include "device.h"
+
+namespace sage {
+hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* codes, void* scales, hipStream_t st);
+hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
+hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                             void* out, bool out_f32, hipStream_t st);
+hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                             void* out, bool out_f32, hipStream_t st);
+}  // namespace sage
+
+namespace {
+
+constexpr int kMaxN = 1 << 20;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int D) {
+  if (D != 64 && D != 128) return SAGE_ERR_HEAD_DIM;
+  if (B <= 0 || H <= 0 || N <= 0 || N > kMaxN) return SAGE_ERR_SHAPE;
+  if ((int64_t)B * H > (int64_t)65535 || (int64_t)B * H * N * D >= kMaxElems) return SAGE_ERR_SHAPE;
+  return SAGE_OK;
+}
+
+int64_t padded(int N) { return ((int64_t)N + sage::KV_TILE - 1) / sage::KV_TILE * sage::KV_TILE; }
+
+}  // namespace
+
+extern "C" {
+
+int sage_fp4_version(void) { return 100; }
+
+int sage_fp4_kv_tile(void) { return sage::KV_TILE; }
+
+int sage_fp4_slot_token(int slot) { return (slot < 0 || slot >= sage::KV_TILE) ? -1 : sage::slot_token(slot); }
+
+size_t sage_fp4_codes_bytes(int role, int fmt, int B, int H, int N, int D) {
+  if (check_shape(B, H, N, D) != SAGE_OK || (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4)) return 0;
+  if (role == SAGE_ROLE_Q || role == SAGE_ROLE_K) return (size_t)B * H * N * (D / 2);
+  if (role == SAGE_ROLE_V) return (size_t)B * H * D * (padded(N) / 2);
+  return 0;
+}
+
+size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D) {
+  if (check_shape(B, H, N, D) != SAGE_OK || (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4)) return 0;
+  const int blk = fmt == SAGE_FMT_NVFP4 ? 16 : 32;
+  if (role == SAGE_ROLE_Q || role == SAGE_ROLE_K) return (size_t)B * H * N * (D / blk);
+  if (role == SAGE_ROLE_V) return (size_t)B * H * D * (padded(N) / blk);
+  return 0;
+}
+
+int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D, void* codes, void* scales,
+                   void* stream) {
+  if (role != SAGE_ROLE_Q && role != SAGE_ROLE_K && role != SAGE_ROLE_V) return SAGE_ERR_ENUM;
+  if (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4) return SAGE_ERR_ENUM;
+  if (!x || !codes || !scales) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SAGE_ERR_ALIGN;
+  const bool mx = fmt == SAGE_FMT_MXFP4;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (role == SAGE_ROLE_V) e = sage::launch_quant_v(mx, x, B * H, N, D, codes, scales, st);
+  else e = sage::launch_quant_rows(mx, x, (int64_t)B * H * N, D, codes, scales, st);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
+                      const void* k_scales, const void* v_codes, const void* v_scales, int B, int H, int N,
+                      int D, int causal, float sm_scale, void* out, int out_dtype, void* stream) {
+  if (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4) return SAGE_ERR_ENUM;
+  if (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32) return SAGE_ERR_ENUM;
+  const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
+  for (const void* p : ptrs)
+    if (!p) return SAGE_ERR_NULL;
+  if (!out) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SAGE_ERR_ALIGN;
+  if (!aligned16(out)) return SAGE_ERR_ALIGN;
+  const float c = sm_scale > 0.0f ? sm_scale : (float)(1.0 / __builtin_sqrt((double)D));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fmt == SAGE_FMT_NVFP4
+                           ? sage::launch_attn_nvfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st)
+                           : sage::launch_attn_mxfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+const char* sage_fp4_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_NULL: return "a required pointer is NULL";
+    case SAGE_ERR_SHAPE: return "B, H or N out of range";
+    case SAGE_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case SAGE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SAGE_ERR_ENUM: return "bad format, role or output type";
+    case SAGE_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// attn_mxfp4.hip — fused MXFP4 attention forward for gfx950 on the block-scaled FP4 MFMA.
+//
+// SageAttention3 (arXiv 2505.11594), DeepTech article, section on FP4 data types: MXFP4 is E2M1
+// with one E8M0 scale per 32 values; the pages compare it with NVFP4 for attention. The CDNA4
+// instruction v_mfma_scale_f32_16x16x128_f8f6f4 consumes exactly this format: each lane supplies
+// 32 consecutive E2M1 values of one row plus their E8M0 scale, so S = Q K^T and P V run natively
+// at the FP4 rate with FP32 accumulation.
+//
+// Same schedule as the NVFP4 kernel (8 waves x 16 queries per workgroup, 128-key tiles staged in
+// LDS, S^T = K Q^T so that a lane's 32 scores of one query are one MXFP4 block of P in slot order,
+// accumulator kept relative to the current tile maximum). Differences: K and V stay FP4 in LDS
+// (no dequantisation), and P has no first level (E8M0 scales cover its range): its codes are
+// E = exp(x - t) quantised with the lane-local block's power-of-two scale. x - t is formed
+// exactly, so the tile maximum has E = 1 exactly, which is an E8M0 scale boundary.
+#include "device.h"
+
+namespace sage {
+
+constexpr int MX_WAVES = 8;
+constexpr int MX_BQ = 16 * MX_WAVES;
+
+__device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
+  unsigned w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(512) void attn_mxfp4_kernel(
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
+    int N, int64_t Np, int nqt, float k2, void* __restrict__ out) {
+  constexpr int KROW = D / 2 + 16;   // K code row pitch (bytes)
+  constexpr int VROW = 64 + 16;      // V code row pitch (bytes): 128 slots
+  constexpr int NBD = D / 32;        // MXFP4 blocks along D
+  __shared__ __attribute__((aligned(16))) uint8_t sKc[KV_TILE * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t sKs[KV_TILE * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sVc[D * VROW];
+  __shared__ __attribute__((aligned(16))) uint8_t sVs[D * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int q0 = qt * MX_BQ;
+  const int qi = q0 + 16 * w + c;
+
+  // Q operand: lane holds the 32 codes of block g of query qi (zeros past D) and its scale.
+  v8i qf = {0, 0, 0, 0, 0, 0, 0, 0};
+  int qsc = 127;
+  if (qi < N && g < NBD) {
+    const int64_t row = bh * N + qi;
+    const uint4 u = *reinterpret_cast<const uint4*>(qc + row * (D / 2) + 16 * g);
+    qf[0] = (int)u.x; qf[1] = (int)u.y; qf[2] = (int)u.z; qf[3] = (int)u.w;
+    qsc = qs[row * NBD + g];
+  }
+
+  float m_u = -INFINITY, R = -INFINITY, l = 0.0f;
+  v4f O[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) O[dt] = v4f{0, 0, 0, 0};
+
+  const int ntiles = (int)(Np / KV_TILE);
+  const int kt_end = CAUSAL ? min(ntiles, (q0 + MX_BQ - 1) / KV_TILE + 1) : ntiles;
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();
+    {
+      // K codes: 128 rows of D/2 bytes; 16 bytes per thread
+      constexpr int TPK = D / 32;  // threads per key row
+      for (int e = tid; e < KV_TILE * TPK; e += 512) {
+        const int key = e / TPK, part = e % TPK;
+        const int j = kt * KV_TILE + key;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (j < N) u = *reinterpret_cast<const uint4*>(kc + (bh * N + j) * (D / 2) + 16 * part);
+        *reinterpret_cast<uint4*>(sKc + key * KROW + 16 * part) = u;
+      }
+      if (tid < KV_TILE * NBD) {
+        const int key = tid / NBD, b = tid % NBD;
+        const int j = kt * KV_TILE + key;
+        sKs[key * 4 + b] = j < N ? ks[(bh * N + j) * NBD + b] : (uint8_t)127;
+      }
+      // V codes: D rows of 64 bytes (the tile's 128 slots); 16 bytes per thread
+      for (int e = tid; e < D * 4; e += 512) {
+        const int d = e / 4, part = e % 4;
+        *reinterpret_cast<uint4*>(sVc + d * VROW + 16 * part) =
+            *reinterpret_cast<const uint4*>(vc + (bh * D + d) * (Np / 2) + (int64_t)kt * 64 + 16 * part);
+      }
+      if (tid < D) {
+        *reinterpret_cast<unsigned*>(sVs + tid * 4) =
+            *reinterpret_cast<const unsigned*>(vs + (bh * D + tid) * (Np / 32) + (int64_t)kt * 4);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T: one scaled FP4 MFMA per 16-key subtile (K dimension 128 >= D)
+    v4f S[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+      int asc = 127;
+      if (g < NBD) {
+        const uint4 u = *reinterpret_cast<const uint4*>(sKc + (16 * t + c) * KROW + 16 * g);
+        a[0] = (int)u.x; a[1] = (int)u.y; a[2] = (int)u.z; a[3] = (int)u.w;
+        asc = sKs[(16 * t + c) * 4 + g];
+      }
+      S[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qf, v4f{0, 0, 0, 0}, 4, 4, 0, asc, 0, qsc);
+    }
+    const int kbase = kt * KV_TILE;
+    if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = kbase + 16 * t + 4 * g + i;
+          if (j >= N || (CAUSAL && j > qi)) S[t][i] = -INFINITY;
+        }
+    }
+    // ---- online softmax; x = S*k2 (log2 units) formed once so that x - t is exact
+    float x[32];
+    float bmx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[4 * t + i] = S[t][i] * k2;
+        bmx = fmaxf(bmx, x[4 * t + i]);
+      }
+    const float t_u = xg_max(bmx);
+    const bool vis = t_u > -INFINITY;
+    const float m_new = fmaxf(m_u, t_u);
+    const bool accept = vis && (t_u >= m_new - 64.0f);
+    const float tt = vis ? t_u : 0.0f;
+
+    float E[32], esum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      E[e] = __builtin_amdgcn_exp2f(x[e] - tt);
+      esum += E[e];
+    }
+    // the lane's block: E8M0 scale 2^(floor(log2 amax) - 2); amax = exp2(block max - t)
+    const float amax = __builtin_amdgcn_exp2f(bmx - tt);
+    int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - 2;  // amax is 0 or normal for X >= -126
+    v8i pf = {0, 0, 0, 0, 0, 0, 0, 0};
+    int psc = 127;
+    if (accept && amax >= 0x1p-124f) {
+      const float sc = as_f((unsigned)(X + 127) << 23);
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) pf[wd] = (int)pack_e4(E + 8 * wd, sc);
+      psc = X + 127;
+    }
+    if (!accept) esum = 0.0f;
+    const float factor = accept ? __builtin_amdgcn_exp2f(R - t_u) : 1.0f;
+    R = accept ? t_u : R;
+    m_u = m_new;
+    l = l * factor + esum;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) O[dt] *= factor;
+
+    // ---- O^T += V^T P^T: one scaled FP4 MFMA per 16 channels; lane group g supplies slots
+    // 32g .. 32g+31 of V's row 16dt + c and of P's column qi
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint4 u = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
+      const v8i a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+      const int asc = sVs[(16 * dt + c) * 4 + g];
+      O[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf, O[dt], 4, 4, 0, asc, 0, psc);
+    }
+  }
+
+  const float L = xg_sum(l);
+  if (qi < N) {
+    const float inv = 1.0f / L;
+    const int64_t row = bh * N + qi;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const v4f o = O[dt] * inv;
+      if (OUT_F32) {
+        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + row * D + 16 * dt + 4 * g) = o;
+      } else {
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(out) + row * D + 16 * dt + 4 * g) =
+            v4h{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool F32>
+static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
+  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
+  const int nqt = (N + MX_BQ - 1) / MX_BQ;
+  attn_mxfp4_kernel<D, CAUSAL, F32><<<dim3(nqt, BH), dim3(512), 0, st>>>(
+      (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, k2, out);
+}
+
+hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                             void* out, bool out_f32, hipStream_t st) {
+  const float k2 = sm_scale * 1.4426950408889634f;
+#define SAGE_MX_CASE(DD, CC, FF) \
+  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF>(ptrs, BH, N, k2, out, st);
+  SAGE_MX_CASE(64, false, false) SAGE_MX_CASE(64, false, true) SAGE_MX_CASE(64, true, false)
+  SAGE_MX_CASE(64, true, true) SAGE_MX_CASE(128, false, false) SAGE_MX_CASE(128, false, true)
+  SAGE_MX_CASE(128, true, false) SAGE_MX_CASE(128, true, true)
+#undef SAGE_MX_CASE
+  return hipGetLastError();
+}
+
+}  // namespace sage

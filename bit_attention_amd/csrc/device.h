@@ -1,0 +1,69 @@
+// device.h — gfx950 device helpers for the FP4 attention kernels (GPU side only).
+//
+// Instruction semantics relied on (each checked on gfx950 against exhaustive or tie-point
+// tables before use):
+//   v_cvt_pk_fp8_f32          FP32 -> OCP E4M3, round to nearest even (overflow gives NaN, so
+//                             callers clamp to 448 first)
+//   v_cvt_f32_fp8             E4M3 -> FP32, exact
+//   v_cvt_scalef32_pk_fp4_f32 two FP32 -> two E2M1 codes of x / 2^floor(log2 scale), round to
+//                             nearest even, saturating at 6, sign kept (including -0)
+//   v_cvt_scalef32_pk_f16_fp4 two E2M1 codes -> two fp16 values code * 2^floor(log2 scale)
+//   v_exp_f32                 2^x within 1 ulp
+//   MFMA layouts: 16x16xK: A/B lane l holds row/column l%16, K-chunk l/16 (8 halves for f16,
+//   32 FP4 codes for the scaled FP4 form); C lane l holds rows 4(l/16)+i of column l%16.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+constexpr int KV_TILE = 128;
+
+// Token held by slot s of a 128-token tile: slot 32g + 4t + i holds token 16t + 4g + i. This is
+// the key order in which a wave holds S^T after eight 16x16 MFMA subtiles (lane group g, subtile
+// t, accumulator element i), so a lane's P values form whole blocks.
+__host__ __device__ inline int slot_token(int s) { return 16 * ((s & 31) >> 2) + 4 * (s >> 5) + (s & 3); }
+
+__device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
+__device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
+
+// E4M3 byte of y (0 <= y, finite), round to nearest even, clamped to 448.
+__device__ __forceinline__ unsigned e4m3_encode(float y) {
+  y = fminf(y, 448.0f);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float e4m3_decode(unsigned b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+// 2^floor(log2 s) for s > 0 (s normal FP32), 1 for s == 0.
+__device__ __forceinline__ float pow2_floor(float s) { return s > 0.0f ? as_f(as_u(s) & 0xFF800000u) : 1.0f; }
+
+// Max over the four lanes {l, l^16, l^32, l^48} that share a column of a 16x16 MFMA tile.
+__device__ __forceinline__ float xg_max(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
+  v = fmaxf(as_f(p[0]), as_f(p[1]));
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
+  return fmaxf(as_f(r[0]), as_f(r[1]));
+}
+__device__ __forceinline__ float xg_sum(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
+  v = as_f(p[0]) + as_f(p[1]);
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
+  return as_f(r[0]) + as_f(r[1]);
+}
+
+// Two E2M1 codes (low byte of `byte2`) -> fp16 pair code * s, exact for E4M3 s: the hardware
+// applies the power of two, the 1+m/8 mantissa is one exact fp16 multiply.
+__device__ __forceinline__ v2h dequant2(unsigned byte2, float p2, v2h mu) {
+  v2h h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(byte2, p2, 0);
+  return h * mu;
+}
+
+}  // namespace sage

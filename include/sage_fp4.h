@@ -1,0 +1,102 @@
+/*
+ * sage_fp4.h — C ABI of libsage_fp4.so: microscaling-FP4 attention forward on AMD MI355X (gfx950).
+ *
+ * The operation (SageAttention3, "Microscaling FP4 Attention for Inference and An Exploration
+ * of 8-Bit Training", arXiv 2505.11594; abstract, and the DeepTech article's sections on the two
+ * FP4 obstacles and on FP4 inference acceleration): Q, K and V are quantised to FP4 with
+ * microscaling, S = Q K^T is computed from the FP4 operands, an online softmax quantises the
+ * probabilities P in two levels (each token's values scaled into [0, 448*6], then 1x16 FP4
+ * microscaling), and P V is computed from FP4 operands with FP32 accumulation. Two formats:
+ *   NVFP4: E2M1 codes, blocks of 16, one E4M3 scale per block (the pages' choice);
+ *   MXFP4: E2M1 codes, blocks of 32, one E8M0 scale per block (the pages' comparison format).
+ *
+ * Numerics (the contract the CPU oracle in oracle/ implements independently):
+ *   - NVFP4 block scale: E4M3 of fl32(amax/6), round to nearest even, clamped to 448.
+ *     MXFP4 block scale: 2^(floor(log2 amax) - 2), clamped to the E8M0 range; 0x00 if amax == 0.
+ *   - codes: the E2M1 value nearest to the exact quotient x/scale, ties to the even code,
+ *     clamped to +-6; the sign bit is the input's; a zero scale gives codes of +-0.
+ *   - blocks lie along each matmul's contraction dimension: Q and K along D, V along tokens,
+ *     P along keys. Inside each 128-token tile, V and P use the slot order: slot 32g + 4t + i
+ *     holds token 16t + 4g + i (g < 4, t < 8, i < 4); blocks are runs of consecutive slots.
+ *   - scores x = sm_scale * S; key tiles of 128 (sage_fp4_kv_tile()); per (row, tile)
+ *     E = exp(x - tile max), NVFP4 P2 = 2688 E quantised per 16 slots with E4M3 scales
+ *     (MXFP4: P2 = E, 32 slots, E8M0); the normaliser sums the unquantised E.
+ *   - causal: key j is visible to query i iff j <= i. Exact key ties and decisions within a
+ *     few ulp of a rounding boundary may round either way (exp and FP32 summation order differ
+ *     from the oracle by a few ulp); codes and scales of Q, K, V are bit-exact.
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers owned by the caller; the library allocates
+ *     nothing, keeps no state and is thread-safe. Inputs are read-only.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
+ *     nothing synchronises.
+ *   - arguments are validated on the host before anything is enqueued; a negative sage_status
+ *     is returned on error and nothing is launched. SAGE_ERR_HIP reports a launch failure
+ *     (hipGetLastError after the launch).
+ *   - every pointer must be 16-byte aligned; tensors are dense and row-major.
+ *   - supported: D in {64, 128}; 1 <= N <= 1048576; B*H*N*D < 2^40. N_q == N_k, no GQA.
+ */
+#ifndef SAGE_FP4_H
+#define SAGE_FP4_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SAGE_FMT_NVFP4 = 0, SAGE_FMT_MXFP4 = 1 } sage_fmt_t;
+typedef enum { SAGE_ROLE_Q = 0, SAGE_ROLE_K = 1, SAGE_ROLE_V = 2 } sage_role_t;
+typedef enum { SAGE_OUT_F16 = 0, SAGE_OUT_F32 = 1 } sage_out_t;
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_NULL = -1,     /* a required pointer is NULL */
+  SAGE_ERR_SHAPE = -2,    /* B, H or N out of range */
+  SAGE_ERR_HEAD_DIM = -3, /* D not in {64, 128} */
+  SAGE_ERR_ALIGN = -4,    /* a pointer is not 16-byte aligned */
+  SAGE_ERR_ENUM = -5,     /* bad format, role or output type */
+  SAGE_ERR_HIP = -6       /* the HIP runtime reported an error for the launch */
+} sage_status_t;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int sage_fp4_version(void);
+
+/* Key-tile size of the online softmax (128). The per-(row, tile) first level of P makes the
+ * result depend on it. */
+int sage_fp4_kv_tile(void);
+
+/* Token held by `slot` (0..127) of a 128-token tile in the slot order above; -1 if out of range. */
+int sage_fp4_slot_token(int slot);
+
+/* Bytes needed for the codes / scales of one quantised tensor (0 for invalid arguments).
+ *   Q, K: codes [B,H,N,D/2], scales [B,H,N,D/16] (NVFP4) or [B,H,N,D/32] (MXFP4);
+ *   V:    codes [B,H,D,Np/2], scales [B,H,D,Np/16] or [B,H,D,Np/32], Np = ceil(N/128)*128. */
+size_t sage_fp4_codes_bytes(int role, int fmt, int B, int H, int N, int D);
+size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D);
+
+/* Quantise one fp16 tensor x [B,H,N,D] (dense, row-major) for its role in the attention.
+ * Q and K: blocks of 16 (32) consecutive channels of each token; codes [B,H,N,D/2] with
+ * element 2i in the low nibble of byte i; scales one byte per block.
+ * V: blocks along tokens. codes [B,H,D,Np/2] hold, for each channel d, the tokens of each
+ * 128-token tile in slot order (two per byte, low nibble first); token positions >= N hold 0.
+ * scales [B,H,D,Np/blk]. One kernel launch. Inputs must be finite. */
+int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D,
+                   void* codes, void* scales, void* stream);
+
+/* Attention forward from quantised operands (as produced by sage_fp4_quant with the same fmt).
+ * out [B,H,N,D], fp16 (SAGE_OUT_F16) or fp32 (SAGE_OUT_F32), dense row-major.
+ * sm_scale <= 0 selects fl32(1/sqrt(D)). causal != 0 applies the top-left causal mask.
+ * One kernel launch. */
+int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales,
+                      const void* k_codes, const void* k_scales,
+                      const void* v_codes, const void* v_scales,
+                      int B, int H, int N, int D, int causal, float sm_scale,
+                      void* out, int out_dtype, void* stream);
+
+/* Static description of a status code. */
+const char* sage_fp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_FP4_H */

@@ -1,0 +1,96 @@
+"""Shared helpers for the GPU tests: run the HIP path through the C ABI and the oracle on the same
+seeded inputs (each side quantises for itself; nothing flows from one to the other)."""
+import sys
+
+import numpy as np
+
+import oracle as orc
+from bit_attention_amd import synth
+
+_CACHE = {}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def workload(wl, **kw):
+    key = (wl, tuple(sorted((k, tuple(v) if isinstance(v, list) else v) for k, v in kw.items())))
+    if key not in _CACHE:
+        if len(_CACHE) > 2:
+            _CACHE.clear()
+        _CACHE[key] = synth.make_qkv(wl, **kw)
+    return _CACHE[key]
+
+
+def to_gpu(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_quant(x, role, fmt):
+    """numpy fp16 [B,H,N,D] -> numpy (codes, scales) in the oracle's array shapes."""
+    from bit_attention_amd import binding as bnd
+    B, H, N, D = x.shape
+    c, s = bnd.quant(to_gpu(x), role, fmt)
+    import torch
+    torch.cuda.synchronize()
+    blk = 16 if fmt == 0 else 32
+    if role == 2:
+        Np = orc.padded_n(N)
+        return c.cpu().numpy().reshape(B, H, D, Np // 2), s.cpu().numpy().reshape(B, H, D, Np // blk)
+    return c.cpu().numpy().reshape(B, H, N, D // 2), s.cpu().numpy().reshape(B, H, N, D // blk)
+
+
+def gpu_attn(fmt, q, k, v, causal, out_f32=True, prefill_nan=True):
+    """Full HIP path on numpy fp16 inputs: three quant launches + one attention launch."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    B, H, N, D = q.shape
+    Q = bnd.quant(to_gpu(q), 0, fmt)
+    K = bnd.quant(to_gpu(k), 1, fmt)
+    V = bnd.quant(to_gpu(v), 2, fmt)
+    out = torch.empty((B, H, N, D), dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
+    if prefill_nan:
+        out.fill_(float("nan"))
+    bnd.attn_fwd_into(fmt, Q, K, V, (B, H, N, D), out, causal=causal)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def oracle_attn(fmt, q, k, v, causal, rows=None):
+    """Oracle on its own quantisation of the same inputs; returns (out, slack)."""
+    B, H, N, D = q.shape
+    Q = orc.quant(orc.ROLE_Q, fmt, q)
+    K = orc.quant(orc.ROLE_K, fmt, k)
+    V = orc.quant(orc.ROLE_V, fmt, v)
+    return orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, rows=rows, want_slack=True)
+
+
+def sample_rows(N, n_each=8, seed=0):
+    """Query rows: the first and last tiles' edges, tile boundaries and a few random ones."""
+    rng = np.random.default_rng(seed)
+    r = set(range(min(n_each, N)))
+    r |= set(range(max(0, N - n_each), N))
+    for b in (127, 128, 129, 255, 256):
+        if b < N:
+            r.add(b)
+    r |= set(int(x) for x in rng.integers(0, N, n_each))
+    return np.array(sorted(r), np.int64)
+
+
+TOL = 2e-3  # max-abs output tolerance against the oracle
+
+
+def compare(gpu_rows, orc_rows, slack, what):
+    """|gpu - oracle| <= TOL + slack (per row). Returns stats."""
+    err = np.abs(gpu_rows.astype(np.float64) - orc_rows.astype(np.float64)).max(axis=-1)
+    bound = TOL + slack
+    bad = np.nonzero(~(err <= bound))[0]
+    clean = slack == 0
+    stats = dict(max_err=float(err.max()), max_err_clean=float(err[clean].max()) if clean.any() else 0.0,
+                 rows=int(err.size), rows_with_slack=int((~clean).sum()))
+    say(f"  [{what}] {stats}")
+    assert bad.size == 0, f"{what}: {bad.size} rows beyond tolerance, worst row {bad[np.argmax(err[bad])]} err {err[bad].max()} slack {slack[bad].max()}"
+    return stats

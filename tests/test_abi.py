@@ -1,0 +1,93 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/*.h declares,
+the size/layout helpers agree with the documented layouts, and argument validation returns the
+documented status before anything is launched (no compute call is made)."""
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+from bit_attention_amd import binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        txt = open(h).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\s*\*?\s+(sage_\w+)\s*\(", txt, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"sage_fp4_quant", "sage_fp4_attn_fwd"} <= names
+    L = bnd.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(bnd.EXPORTS) == names
+
+
+def test_constants_and_slot_order():
+    assert bnd.sage_fp4_kv_tile() == 128
+    assert bnd.sage_fp4_version() >= 100
+    order = [bnd.sage_fp4_slot_token(s) for s in range(128)]
+    assert sorted(order) == list(range(128))
+    assert order[:8] == [0, 1, 2, 3, 16, 17, 18, 19]
+    assert order[32] == 4 and bnd.sage_fp4_slot_token(128) == -1 and bnd.sage_fp4_slot_token(-1) == -1
+
+
+@pytest.mark.parametrize("fmt,blk", [(0, 16), (1, 32)])
+def test_size_helpers(fmt, blk):
+    B, H, N, D = 2, 3, 300, 128
+    assert bnd.sage_fp4_codes_bytes(0, fmt, B, H, N, D) == B * H * N * D // 2
+    assert bnd.sage_fp4_scales_bytes(1, fmt, B, H, N, D) == B * H * N * D // blk
+    assert bnd.sage_fp4_codes_bytes(2, fmt, B, H, N, D) == B * H * D * 384 // 2
+    assert bnd.sage_fp4_scales_bytes(2, fmt, B, H, N, D) == B * H * D * 384 // blk
+    assert bnd.sage_fp4_codes_bytes(0, fmt, B, H, N, 96) == 0
+    assert bnd.sage_fp4_codes_bytes(5, fmt, B, H, N, D) == 0
+
+
+FAKE = C.c_void_p(0x10000)  # never dereferenced: validation fails before any launch
+MIS = C.c_void_p(0x10008)
+
+
+def test_quant_validation():
+    q = bnd.sage_fp4_quant
+    assert q(3, 0, FAKE, 1, 1, 16, 64, FAKE, FAKE, None) == -5
+    assert q(0, 2, FAKE, 1, 1, 16, 64, FAKE, FAKE, None) == -5
+    assert q(0, 0, None, 1, 1, 16, 64, FAKE, FAKE, None) == -1
+    assert q(0, 0, FAKE, 1, 1, 16, 64, None, FAKE, None) == -1
+    assert q(0, 0, FAKE, 1, 1, 16, 96, FAKE, FAKE, None) == -3
+    assert q(0, 0, FAKE, 0, 1, 16, 64, FAKE, FAKE, None) == -2
+    assert q(0, 0, FAKE, 1, 1, 0, 64, FAKE, FAKE, None) == -2
+    assert q(0, 0, FAKE, 1, 1, (1 << 20) + 1, 64, FAKE, FAKE, None) == -2
+    assert q(0, 0, MIS, 1, 1, 16, 64, FAKE, FAKE, None) == -4
+
+
+def test_attn_validation():
+    a = bnd.sage_fp4_attn_fwd
+    ok = [FAKE] * 6
+    assert a(2, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -5
+    assert a(0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, 7, None) == -5
+    assert a(0, *ok[:5], None, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -1
+    assert a(0, *ok, 1, 1, 16, 64, 0, 0.0, None, 1, None) == -1
+    assert a(0, *ok, 1, 1, 16, 32, 0, 0.0, FAKE, 1, None) == -3
+    assert a(0, *ok, 1, -1, 16, 64, 0, 0.0, FAKE, 1, None) == -2
+    assert a(0, *ok[:2], MIS, *ok[3:], 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -4
+    assert a(0, *ok, 1, 1, 16, 64, 0, 0.0, MIS, 1, None) == -4
+    for s in (0, -1, -2, -3, -4, -5, -6, 99):
+        assert isinstance(bnd.status_string(s), str) and bnd.status_string(s)
+
+
+def test_library_does_not_link_the_oracle():
+    """The product library and the oracle share no code: no oracle symbol is exported or needed."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", bnd.LIB_PATH], capture_output=True, text=True).stdout
+    assert "orc_" not in out
+    deps = subprocess.run(["readelf", "-d", bnd.LIB_PATH], capture_output=True, text=True).stdout
+    assert "sage_oracle" not in deps
