@@ -1,0 +1,255 @@
+"""Benchmark of the FP4 microscaling attention forward on one MI355X.
+
+One step = the whole hot path over one batch: sage_fp4_quant of Q, K and V, then
+sage_fp4_attn_fwd, with the fp16 inputs already resident in HBM. Workload: B=4, H=32, N=4096,
+D=128, NVFP4, non-causal (the kernel-sweep point), synthetic seeded inputs.
+
+Prints one JSON line. `value` = 4*B*H*N^2*D / (step time) in TOPS (whole step, quantisation
+included); the attention kernel alone is reported in `attn_*` fields and `roofline`, timed with
+HIP events on the stream the kernels are launched on. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 attention fwd TOPS (4·B·H·N²·D/t) + %FP4-MFMA peak; cos-sim vs FP32"
+FP4_PEAK_TOPS = 10066.0      # MI355X dense FP4 MFMA (256 CU x 4 SIMD x 4096 flop/clk x 2.4 GHz)
+FP16_PEAK_TFLOPS = 2516.6    # dense fp16 MFMA
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = dict(B=4, H=32, N=4096, D=128)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for f in (name, "device.h"):
+        with open(os.path.join(ROOT, "bit_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, key: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(key)
+    if not e or e.get("source_hash") != kernel_source_hash(kernel_file):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def torch_reference_rows(q, k, v, heads, rows, sm_scale):
+    """Plain PyTorch fp32 attention on the GPU for a few (head, row) samples."""
+    import torch
+    outs = []
+    for h in heads:
+        qh = q.view(-1, q.shape[2], q.shape[3])[h].float()
+        kh = k.view(-1, k.shape[2], k.shape[3])[h].float().contiguous()
+        vh = v.view(-1, v.shape[2], v.shape[3])[h].float().contiguous()
+        s = torch.matmul(qh[rows], kh.t().contiguous()) * sm_scale
+        p = torch.softmax(s, dim=-1)
+        outs.append(torch.matmul(p, vh))
+    return torch.cat(outs).double().cpu().numpy()
+
+
+def cpu_baseline(q_np, k_np, v_np, shape, seconds_target=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: head after head, the
+    quantisation of the head's Q, K and V and the attention of every 4th query row of it, until
+    about `seconds_target` seconds of CPU time; the quantisation is charged pro rata to the rows
+    computed. Throughput by the same 4*N*D-per-row count as the GPU figure."""
+    import oracle as orc
+    B, H, N, D = shape
+    nthreads = orc.max_threads()
+    rows = np.arange(0, N, 4, dtype=np.int64)
+    total_t, total_rows, heads = 0.0, 0, 0
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        t0 = time.perf_counter()
+        Q = orc.quant(orc.ROLE_Q, orc.NVFP4, q_np[b:b + 1, h:h + 1])
+        K = orc.quant(orc.ROLE_K, orc.NVFP4, k_np[b:b + 1, h:h + 1])
+        V = orc.quant(orc.ROLE_V, orc.NVFP4, v_np[b:b + 1, h:h + 1])
+        t_quant = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        out = orc.attn_fwd(orc.NVFP4, Q, K, V, (1, 1, N, D), rows=rows, nthreads=nthreads)
+        t_attn = time.perf_counter() - t0
+        assert np.all(np.isfinite(out))
+        total_t += t_attn + t_quant * len(rows) / N
+        total_rows += len(rows)
+        heads += 1
+        if total_t >= seconds_target:
+            break
+    tops = 4.0 * N * D * total_rows / total_t / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": nthreads, "kind": "oracle",
+            "sample": f"{heads} heads x {len(rows)} query rows (every 4th row; non-causal, N={N}, "
+                      f"D={D}), NVFP4: per head the quantisation of Q, K, V (charged "
+                      f"{len(rows)}/{N}) and the attention rows; {total_t:.1f} s of CPU time",
+            "seconds": total_t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--causal", action="store_true", help="time the causal variant instead")
+    ap.add_argument("--fmt", choices=["nvfp4", "mxfp4"], default="nvfp4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the post-run extra measurements")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+              "(every (batch, head) is independent, so heads would shard with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_attention_amd import binding as bnd
+    from bit_attention_amd import synth
+
+    fmt = bnd.NVFP4 if args.fmt == "nvfp4" else bnd.MXFP4
+    B, H, N, D = (WORKLOAD[k] for k in "BHND")
+    shape = (B, H, N, D)
+    log(f"bench: generating inputs {shape} ...")
+    t0 = time.perf_counter()
+    q_np, k_np, v_np = synth.make_qkv(2)
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(q_np).to(dev)
+    k = torch.from_numpy(k_np).to(dev)
+    v = torch.from_numpy(v_np).to(dev)
+    Q = bnd.alloc_quant(bnd.ROLE_Q, fmt, *shape)
+    K = bnd.alloc_quant(bnd.ROLE_K, fmt, *shape)
+    V = bnd.alloc_quant(bnd.ROLE_V, fmt, *shape)
+    out = torch.empty(shape, dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    causal = args.causal
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
+        bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
+        bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
+        if i is not None:
+            ev[i][1].record(stream)
+        bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal)
+        if i is not None:
+            ev[i][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    flops_formula = 4.0 * B * H * N * N * D
+    flops = flops_formula / 2 if causal else flops_formula  # causal: masked work is skipped
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tops = flops / (attn_ms * 1e-3) / 1e12
+    kfile = "attn_nvfp4.hip" if fmt == bnd.NVFP4 else "attn_mxfp4.hip"
+    tkey = f"{'attn_nvfp4' if fmt == bnd.NVFP4 else 'attn_mxfp4'}_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
+    traffic = load_traffic(kfile, tkey)
+    if fmt == bnd.NVFP4:
+        roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tops / FP16_PEAK_TFLOPS, "traffic": traffic,
+                "kernel": "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"}
+    else:
+        roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": attn_tops / FP4_PEAK_TOPS, "traffic": traffic,
+                "kernel": "attn_mxfp4_kernel (block-scaled FP4 MFMA)"}
+    blk = 16 if fmt == bnd.NVFP4 else 32
+    quant_bytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / blk)
+    res = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": args.fmt, "data": "synthetic (seeded SplitMix64/Box-Muller N(0,1) fp16)",
+        "config": {"workload": f"kernel sweep point B={B} H={H} N={N} D={D} {args.fmt} "
+                               f"{'causal' if causal else 'non-causal'}",
+                   "B": B, "H": H, "N": N, "D": D, "causal": causal, "format": args.fmt,
+                   "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
+        "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
+        "quant_ms_3_tensors": quant_ms, "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+        "flops_counted": flops, "flops_formula_4BHN2D": flops_formula,
+        "roofline": roof,
+    }
+
+    # accuracy against a plain PyTorch fp32 reference on sampled rows of three heads
+    torch.cuda.synchronize()
+    heads = [0, B * H // 2 + 1, B * H - 1]
+    rows = torch.arange(0, N, N // 256, device=dev)
+    if not causal:
+        ref = torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D))
+        got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
+        a, b = got.reshape(-1), ref.reshape(-1)
+        res["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+        res["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 256 << 20
+
+    if not args.no_extras:
+        extras = {}
+        for name, f2, c2 in (("nvfp4_causal", bnd.NVFP4, True), ("mxfp4_noncausal", bnd.MXFP4, False),
+                             ("mxfp4_causal", bnd.MXFP4, True)):
+            if f2 == fmt and c2 == causal:
+                continue
+            Q2 = bnd.quant(q, bnd.ROLE_Q, f2); K2 = bnd.quant(k, bnd.ROLE_K, f2); V2 = bnd.quant(v, bnd.ROLE_V, f2)
+            for _ in range(3):
+                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            fl = flops_formula / 2 if c2 else flops_formula
+            t = fl / (ms * 1e-3) / 1e12
+            extras[name] = {"attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS}
+        res["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
