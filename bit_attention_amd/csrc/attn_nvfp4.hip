@@ -8,11 +8,16 @@
 //
 // CDNA4 design. The scaled FP4 MFMA takes only power-of-two (E8M0) block scales, and an E2M1
 // code times an E4M3 scale needs up to 6 significant bits, which no FP8/FP6 operand holds. So
-// NVFP4 operands are dequantised exactly to fp16 (code * 2^e by the hardware conversion, times
-// the 1+m/8 mantissa by one fp16 multiply) and both products run on v_mfma_f32_16x16x32_f16.
-//   - workgroup = 8 waves = 128 queries of one (batch, head); key tiles of 128.
-//   - K and V of a tile are staged in LDS once per workgroup, dequantised to fp16.
-//   - each wave computes S^T = K Q^T for its 16 queries: after 8 subtiles a lane holds the 32
+// NVFP4 operands are dequantised exactly to fp16 (the code value by the hardware conversion,
+// times the E4M3 scale by one fp16 multiply: at most 6 significant bits, 2^-10 .. 2688) and both
+// products run on v_mfma_f32_16x16x32_f16.
+//   - workgroup = 4 waves = 128 queries of one (batch, head); each wave owns 32 queries as two
+//     16-query groups, so every K/V operand read from LDS feeds two MFMAs. Two workgroups fit on
+//     a CU (LDS 2 x 68 KB at D = 128, at most 256 VGPRs per wave), so one stages while the other
+//     computes.
+//   - key tiles of 128: K and V codes of the next tile are loaded into registers while the
+//     current tile is computed, then dequantised into LDS between two barriers.
+//   - each group computes S^T = K Q^T for its 16 queries: after 8 subtiles a lane holds the 32
 //     scores of one query at keys 16t + 4g + i, exactly the slot order the quantisation kernel
 //     stores V in, so P's 1x16 blocks are lane-local (two per lane per tile), their maxima come
 //     out of the row-max pass, and the quantised P is already the B operand of O^T = V^T P^T.
@@ -21,28 +26,29 @@
 //     MFMA accumulates P2-hat * V-hat directly; one multiply rescales them per tile. A tile whose
 //     maximum lies more than 2^64 below the running maximum is dropped for that row (relative
 //     weight below 2^-64).
+//   - workgroups are ordered so that each XCD walks through whole heads (K/V stay in its L2).
 #include "device.h"
 
 namespace sage {
 
-constexpr int NV_WAVES = 8;
-constexpr int NV_BQ = 16 * NV_WAVES;
+constexpr int NV_WAVES = 4;
+constexpr int NV_BQ = 32 * NV_WAVES;  // queries per workgroup
 constexpr float LOG2_2688 = 11.392317422778762f;  // log2(448 * 6)
 
-__device__ __forceinline__ v8h dequant8(unsigned w, float p2, v2h mu) {
-  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * mu;
-  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * mu;
-  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * mu;
-  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * mu;
+// Eight E2M1 codes (one dword) times an fp16 scale pair, exact.
+__device__ __forceinline__ v8h dequant8(unsigned w, v2h s) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
   return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// E4M3 scale byte -> (2^floor(log2 s), 1+m/8 as an fp16 pair); s == 0 gives (1, 0).
-__device__ __forceinline__ void split_scale(unsigned sb, float* p2, v2h* mu) {
-  const float s = e4m3_decode(sb);
-  *p2 = pow2_floor(s);
-  const _Float16 m = (_Float16)(s / *p2);
-  *mu = v2h{m, m};
+// Four E4M3 scale bytes (one dword) -> fp16 values, exact (E4M3 fits fp16).
+__device__ __forceinline__ void scales4(unsigned sw, _Float16* h) {
+  const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+  const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw >> 16, 1.0f, false);
+  h[0] = lo[0]; h[1] = lo[1]; h[2] = hi[0]; h[3] = hi[1];
 }
 
 __device__ __forceinline__ unsigned pack_fp4_8(const float* q) {
@@ -54,158 +60,198 @@ __device__ __forceinline__ unsigned pack_fp4_8(const float* q) {
   return w;
 }
 
+// Online-softmax state of one 16-query group (per lane: one query, a quarter of its channels).
+template <int D>
+struct RowState {
+  float m_u, R, l2;
+  v4f O[D / 16];
+};
+
+// One tile of the online softmax with the two-level P quantisation for one group. S holds the
+// lane's 32 scores (masked ones -infinity); on return Pf holds P2-hat (fp16, code * s_P2) as the
+// four B operands of the PV product, and O, l2 have been rescaled to this tile's reference.
+template <int D>
+__device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, v8h* Pf) {
+  float bm[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 4 * h; t < 4 * h + 4; ++t)
+      mx = fmaxf(fmaxf(mx, fmaxf(S[t][0], S[t][1])), fmaxf(S[t][2], S[t][3]));
+    bm[h] = mx;
+  }
+  const float tS = xg_max(fmaxf(bm[0], bm[1]));
+  const bool vis = tS > -INFINITY;
+  const float t_u = tS * k2;  // tile maximum in log2 units
+  const float m_new = fmaxf(st.m_u, t_u);
+  const bool accept = vis && (t_u >= m_new - 64.0f);
+  const float bias = vis ? LOG2_2688 - t_u : -INFINITY;  // log2(P2) = S*k2 + bias
+
+  float sP[2], bq[2];
+  v2h sh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, bias));  // block max of P2
+    const unsigned sb = e4m3_encode(pmax * (1.0f / 6.0f));
+    sP[h] = e4m3_decode(sb);
+    bq[h] = sP[h] > 0.0f ? bias - __builtin_amdgcn_logf(sP[h]) : -INFINITY;  // log2(P2/s)
+    const _Float16 s16 = (_Float16)sP[h];
+    sh[h] = v2h{s16, s16};
+  }
+  float qsum[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int h = u >> 1;
+    float q[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      q[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * u + (jj >> 2)][jj & 3], k2, bq[h]));  // P2/s
+      qsum[h] += q[jj];
+    }
+    Pf[u] = accept ? dequant8(pack_fp4_8(q), sh[h]) : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const float l2t = accept ? sP[0] * qsum[0] + sP[1] * qsum[1] : 0.0f;
+  const float factor = accept ? __builtin_amdgcn_exp2f(st.R - t_u) : 1.0f;
+  st.R = accept ? t_u : st.R;
+  st.m_u = m_new;
+  st.l2 = st.l2 * factor + l2t;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.O[dt] *= factor;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(512) void attn_nvfp4_kernel(
+__global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
   constexpr int KP = D + 8;        // K-hat row pitch (halves)
   constexpr int VP = KV_TILE + 8;  // V-hat row pitch (halves)
-  constexpr int CH = D / 8;        // code bytes per thread per tile, for K and for V
+  constexpr int CB = D / 4;        // code bytes each thread stages per tile, for K and for V
+  constexpr int CW = CB / 4;       // ... in dwords (8 codes each; two dwords per 16-block)
+  constexpr int VT = 64 / CB;      // threads per V channel row (64 code bytes per tile)
   __shared__ __attribute__((aligned(16))) _Float16 sK[KV_TILE * KP];
   __shared__ __attribute__((aligned(16))) _Float16 sV[D * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy tiles first
-  const int64_t bh = blockIdx.y;
+  const int work = xcd_work((int)blockIdx.x, nwork);
+  const int64_t bh = work / nqt;
+  const int qt = CAUSAL ? (nqt - 1 - work % nqt) : work % nqt;  // heavy causal tiles first
   const int q0 = qt * NV_BQ;
-  const int qi = q0 + 16 * w + c;  // this lane's query
+  const int qi0 = q0 + 32 * w + c;  // group a holds query qi0 + 16a
 
-  // Q-hat fragments (B operand of S^T = K Q^T): lane holds Q-hat[qi][32kk + 8g .. +8).
-  v8h qf[D / 32];
+  // Q-hat fragments (B operand of S^T = K Q^T): lane holds Q-hat[q][32kk + 8g .. +8).
+  v8h qf[2][D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    qf[kk] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-    if (qi < N) {
-      const int64_t row = bh * N + qi;
-      const unsigned wq = *reinterpret_cast<const unsigned*>(qc + row * (D / 2) + 16 * kk + 4 * g);
-      float p2; v2h mu;
-      split_scale(qs[row * (D / 16) + 2 * kk + (g >> 1)], &p2, &mu);
-      qf[kk] = dequant8(wq, p2, mu);
+  for (int a = 0; a < 2; ++a) {
+    const int qi = qi0 + 16 * a;
+    const int64_t row = bh * N + qi;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      qf[a][kk] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      if (qi < N) {
+        const unsigned wq = *reinterpret_cast<const unsigned*>(qc + row * (D / 2) + 16 * kk + 4 * g);
+        const unsigned sb = qs[row * (D / 16) + 2 * kk + (g >> 1)];
+        const _Float16 s16 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false)[0];
+        qf[a][kk] = dequant8(wq, v2h{s16, s16});
+      }
     }
   }
 
-  float m_u = -INFINITY, R = -INFINITY, l2 = 0.0f;
-  v4f O[D / 16];
+  RowState<D> st[2];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) O[dt] = v4f{0, 0, 0, 0};
+  for (int a = 0; a < 2; ++a) {
+    st[a].m_u = -INFINITY; st[a].R = -INFINITY; st[a].l2 = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st[a].O[dt] = v4f{0, 0, 0, 0};
+  }
+
+  // staging assignment: K row `kkey`, code bytes [kpart*CB, +CB); V channel `vd`, bytes
+  // [vpart*CB, +CB) of the tile's 64
+  const int kkey = tid >> 1, kpart = tid & 1;
+  const int vd = tid / VT, vpart = tid % VT;
+  const uint8_t* vcrow = vc + (bh * D + vd) * (Np / 2) + vpart * CB;
+  const uint8_t* vsrow = vs + (bh * D + vd) * (Np / 16) + vpart * (CB / 8);
+  unsigned kr[CW], vr[CW], ksr = 0, vsr = 0;
+
+  auto prefetch = [&](int kt) {
+    const int j = kt * KV_TILE + kkey;
+    if (j < N) {
+      const int64_t row = bh * N + j;
+      const uint4* src = reinterpret_cast<const uint4*>(kc + row * (D / 2) + kpart * CB);
+#pragma unroll
+      for (int u = 0; u < CW / 4; ++u) {
+        const uint4 x = src[u];
+        kr[4 * u] = x.x; kr[4 * u + 1] = x.y; kr[4 * u + 2] = x.z; kr[4 * u + 3] = x.w;
+      }
+      if (CB / 8 == 4) ksr = *reinterpret_cast<const unsigned*>(ks + row * (D / 16) + kpart * 4);
+      else ksr = *reinterpret_cast<const unsigned short*>(ks + row * (D / 16) + kpart * 2);
+    } else {
+#pragma unroll
+      for (int u = 0; u < CW; ++u) kr[u] = 0;
+      ksr = 0;
+    }
+    const uint4* vsrc = reinterpret_cast<const uint4*>(vcrow + (int64_t)kt * 64);
+#pragma unroll
+    for (int u = 0; u < CW / 4; ++u) {
+      const uint4 x = vsrc[u];
+      vr[4 * u] = x.x; vr[4 * u + 1] = x.y; vr[4 * u + 2] = x.z; vr[4 * u + 3] = x.w;
+    }
+    if (CB / 8 == 4) vsr = *reinterpret_cast<const unsigned*>(vsrow + (int64_t)kt * 8);
+    else vsr = *reinterpret_cast<const unsigned short*>(vsrow + (int64_t)kt * 8);
+  };
 
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + NV_BQ - 1) / KV_TILE + 1) : ntiles;
+  prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();  // the previous tile's LDS reads are complete
     {
-      // K: thread -> (key, part): CH code bytes = 2*CH codes = CH/8 blocks of 16
-      const int key = tid / 4, part = tid % 4;
-      const int j = kt * KV_TILE + key;
-      _Float16* dst = sK + key * KP + part * 2 * CH;
-      if (j < N) {
-        const int64_t row = bh * N + j;
-        const unsigned* src = reinterpret_cast<const unsigned*>(kc + row * (D / 2) + part * CH);
+      _Float16 kh[4], vh[4];
+      scales4(ksr, kh);
+      scales4(vsr, vh);
+      _Float16* kdst = sK + kkey * KP + kpart * 2 * CB;
+      _Float16* vdst = sV + vd * VP + vpart * 2 * CB;
 #pragma unroll
-        for (int u = 0; u < CH / 4; ++u) {
-          float p2; v2h mu;
-          split_scale(ks[row * (D / 16) + (part * 2 * CH + 8 * u) / 16], &p2, &mu);
-          *reinterpret_cast<v8h*>(dst + 8 * u) = dequant8(src[u], p2, mu);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < CH / 4; ++u) *reinterpret_cast<v8h*>(dst + 8 * u) = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-    {
-      // V: codes [D][Np/2]; thread -> (channel, part): CH bytes = 2*CH slots
-      constexpr int TPR = 64 / CH;  // threads per channel row
-      const int d = tid / TPR, part = tid % TPR;
-      const int64_t vrow = bh * D + d;
-      const unsigned* src = reinterpret_cast<const unsigned*>(vc + vrow * (Np / 2) + (int64_t)kt * 64 + part * CH);
-      _Float16* dst = sV + d * VP + part * 2 * CH;
-#pragma unroll
-      for (int u = 0; u < CH / 4; ++u) {
-        float p2; v2h mu;
-        split_scale(vs[vrow * (Np / 16) + (int64_t)kt * 8 + (part * 2 * CH + 8 * u) / 16], &p2, &mu);
-        *reinterpret_cast<v8h*>(dst + 8 * u) = dequant8(src[u], p2, mu);
+      for (int u = 0; u < CW; ++u) {
+        *reinterpret_cast<v8h*>(kdst + 8 * u) = dequant8(kr[u], v2h{kh[u >> 1], kh[u >> 1]});
+        *reinterpret_cast<v8h*>(vdst + 8 * u) = dequant8(vr[u], v2h{vh[u >> 1], vh[u >> 1]});
       }
     }
     __syncthreads();
+    if (kt + 1 < kt_end) prefetch(kt + 1);
 
-    // ---- S^T = K-hat Q-hat^T for 16 queries: subtile t covers keys 16t..16t+15
-    v4f S[8];
+    // ---- S^T = K-hat Q-hat^T for both groups: subtile t covers keys 16t..16t+15
+    v4f S[2][8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      S[t] = v4f{0, 0, 0, 0};
+      S[0][t] = v4f{0, 0, 0, 0};
+      S[1][t] = v4f{0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         const v8h a = *reinterpret_cast<const v8h*>(sK + (16 * t + c) * KP + 32 * kk + 8 * g);
-        S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[kk], S[t], 0, 0, 0);
+        S[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[0][kk], S[0][t], 0, 0, 0);
+        S[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[1][kk], S[1][t], 0, 0, 0);
       }
     }
     // ---- mask: keys past N, and keys after the query when causal
     const int kbase = kt * KV_TILE;
     if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kbase + 16 * t + 4 * g + i;
-          if (j >= N || (CAUSAL && j > qi)) S[t][i] = -INFINITY;
-        }
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = kbase + 16 * t + 4 * g + i;
+            if (j >= N || (CAUSAL && j > qi0 + 16 * a)) S[a][t][i] = -INFINITY;
+          }
     }
-    // ---- online softmax with the two-level quantisation of P
-    float bm[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 4 * h; t < 4 * h + 4; ++t)
-        mx = fmaxf(fmaxf(mx, fmaxf(S[t][0], S[t][1])), fmaxf(S[t][2], S[t][3]));
-      bm[h] = mx;
-    }
-    const float tS = xg_max(fmaxf(bm[0], bm[1]));
-    const bool vis = tS > -INFINITY;
-    const float t_u = tS * k2;  // tile maximum in log2 units
-    const float m_new = fmaxf(m_u, t_u);
-    const bool accept = vis && (t_u >= m_new - 64.0f);
-    const float bias = vis ? LOG2_2688 - t_u : -INFINITY;  // log2(P2) = S*k2 + bias
-
-    float sP[2], bq[2], p2s[2];
-    v2h mus[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, bias));  // block max of P2
-      const unsigned sb = e4m3_encode(pmax * (1.0f / 6.0f));
-      sP[h] = e4m3_decode(sb);
-      bq[h] = sP[h] > 0.0f ? bias - __builtin_amdgcn_logf(sP[h]) : -INFINITY;  // log2(P2/s)
-      p2s[h] = pow2_floor(sP[h]);
-      const _Float16 m = (_Float16)(sP[h] / p2s[h]);
-      mus[h] = v2h{m, m};
-    }
-    float qsum[2] = {0.0f, 0.0f};
-    v8h Pf[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int h = u >> 1;
-      float q[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        q[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * u + (jj >> 2)][jj & 3], k2, bq[h]));  // P2/s
-        qsum[h] += q[jj];
-      }
-      Pf[u] = dequant8(pack_fp4_8(q), p2s[h], mus[h]);
-    }
-    float l2t = sP[0] * qsum[0] + sP[1] * qsum[1];
-    if (!accept) {
-      l2t = 0.0f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) Pf[u] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    const float factor = accept ? __builtin_amdgcn_exp2f(R - t_u) : 1.0f;
-    R = accept ? t_u : R;
-    m_u = m_new;
-    l2 = l2 * factor + l2t;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) O[dt] *= factor;
+    // ---- online softmax with the two-level quantisation of P, per group
+    v8h Pf[2][4];
+    softmax_tile<D>(S[0], k2, st[0], Pf[0]);
+    softmax_tile<D>(S[1], k2, st[1], Pf[1]);
 
     // ---- O^T += V-hat^T P-hat^T: MFMA step u covers slots 32g + 8u .. +8 of every lane group
 #pragma unroll
@@ -213,24 +259,29 @@ __global__ __launch_bounds__(512) void attn_nvfp4_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const v8h a = *reinterpret_cast<const v8h*>(sV + (16 * dt + c) * VP + 32 * g + 8 * u);
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Pf[u], O[dt], 0, 0, 0);
+        st[0].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Pf[0][u], st[0].O[dt], 0, 0, 0);
+        st[1].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Pf[1][u], st[1].O[dt], 0, 0, 0);
       }
   }
 
-  // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of query qi
-  const float L = xg_sum(l2);
-  if (qi < N) {
-    const float inv = 1.0f / L;
-    const int64_t row = bh * N + qi;
+  // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of its query in each group
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const v4f o = O[dt] * inv;
-      if (OUT_F32) {
-        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + row * D + 16 * dt + 4 * g) = o;
-      } else {
-        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(out) + row * D + 16 * dt + 4 * g) =
-            v4h{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+  for (int a = 0; a < 2; ++a) {
+    const float L = xg_sum(st[a].l2);
+    const int qi = qi0 + 16 * a;
+    if (qi < N) {
+      const float inv = 1.0f / L;
+      const int64_t row = bh * N + qi;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const v4f o = st[a].O[dt] * inv;
+        if (OUT_F32) {
+          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + row * D + 16 * dt + 4 * g) = o;
+        } else {
+          typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(out) + row * D + 16 * dt + 4 * g) =
+              v4h{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+        }
       }
     }
   }
@@ -240,9 +291,10 @@ template <int D, bool CAUSAL, bool F32>
 static void launch_nv(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + NV_BQ - 1) / NV_BQ;
-  attn_nvfp4_kernel<D, CAUSAL, F32><<<dim3(nqt, BH), dim3(512), 0, st>>>(
+  const int nwork = nqt * BH;
+  attn_nvfp4_kernel<D, CAUSAL, F32><<<dim3(nwork), dim3(64 * NV_WAVES), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, k2, out);
 }
 
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,

@@ -32,6 +32,15 @@ constexpr int KV_TILE = 128;
 // t, accumulator element i), so a lane's P values form whole blocks.
 __host__ __device__ inline int slot_token(int s) { return 16 * ((s & 31) >> 2) + 4 * (s >> 5) + (s & 3); }
 
+// Work item of workgroup L out of T. Workgroups are dispatched round-robin over the 8 XCDs
+// (XCD x receives L = x, x + 8, ...); each XCD is given one contiguous range of work items, so
+// the workgroups one XCD runs side by side share (batch, head), and with it K and V in that
+// XCD's L2. A bijection of [0, T) for any T.
+__device__ __forceinline__ int xcd_work(int L, int T) {
+  const int x = L & 7, k = L >> 3, q = T >> 3, r = T & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
 __device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
 
