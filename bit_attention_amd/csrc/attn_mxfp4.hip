@@ -6,12 +6,19 @@
 // 32 consecutive E2M1 values of one row plus their E8M0 scale, so S = Q K^T and P V run natively
 // at the FP4 rate with FP32 accumulation.
 //
-// Same schedule as the NVFP4 kernel (8 waves x 16 queries per workgroup, 128-key tiles staged in
-// LDS, S^T = K Q^T so that a lane's 32 scores of one query are one MXFP4 block of P in slot order,
-// accumulator kept relative to the current tile maximum). Differences: K and V stay FP4 in LDS
-// (no dequantisation), and P has no first level (E8M0 scales cover its range): its codes are
-// E = exp(x - t) quantised with the lane-local block's power-of-two scale. x - t is formed
-// exactly, so the tile maximum has E = 1 exactly, which is an E8M0 scale boundary.
+// Schedule: 8 waves x 16 queries per workgroup, 128-key tiles of FP4 codes and scales staged in
+// LDS (no dequantisation), S^T = K Q^T so that a lane's 32 scores of one query are one MXFP4
+// block of P in slot order, accumulator kept relative to the current tile maximum. At most 128
+// VGPRs, so two workgroups (4 waves per SIMD) share a CU: the softmax is VALU-bound and needs the
+// occupancy to overlap one wave's exp/packing with another's MFMAs. Workgroups are ordered so
+// that each XCD walks through whole heads.
+// P has no first level (E8M0 scales cover its range): its codes are E = 2^(x - t) quantised with
+// the lane-local block's power-of-two scale.
+//
+// Exactness of the tile maximum: E = 1 exactly for the maximal score, and that value sits on an
+// E8M0 scale boundary. E is evaluated as clamp01(exp2(S*k2 - T)) with one fma, where T is the
+// tile maximum in log2 units rounded toward -infinity: for the maximal score the fma's exact
+// argument is in [0, ulp), so exp2 gives >= 1 and the clamp (folded into v_exp_f32) returns 1.
 #include "device.h"
 
 namespace sage {
@@ -28,11 +35,15 @@ __device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
   return w;
 }
 
+__device__ __forceinline__ float exp2_01(float x) {
+  return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.0f, 1.0f);
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
   constexpr int KROW = D / 2 + 16;   // K code row pitch (bytes)
   constexpr int VROW = 64 + 16;      // V code row pitch (bytes): 128 slots
   constexpr int NBD = D / 32;        // MXFP4 blocks along D
@@ -43,8 +54,9 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int work = xcd_work((int)blockIdx.x, nwork);
+  const int64_t bh = work / nqt;
+  const int qt = CAUSAL ? (nqt - 1 - work % nqt) : work % nqt;
   const int q0 = qt * MX_BQ;
   const int qi = q0 + 16 * w + c;
 
@@ -118,42 +130,43 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
           if (j >= N || (CAUSAL && j > qi)) S[t][i] = -INFINITY;
         }
     }
-    // ---- online softmax; x = S*k2 (log2 units) formed once so that x - t is exact
-    float x[32];
-    float bmx = -INFINITY;
+    // ---- online softmax in log2 units
+    float bmx = -INFINITY;  // the lane's block maximum of S
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[4 * t + i] = S[t][i] * k2;
-        bmx = fmaxf(bmx, x[4 * t + i]);
-      }
-    const float t_u = xg_max(bmx);
-    const bool vis = t_u > -INFINITY;
-    const float m_new = fmaxf(m_u, t_u);
-    const bool accept = vis && (t_u >= m_new - 64.0f);
-    const float tt = vis ? t_u : 0.0f;
+    for (int t = 0; t < 8; ++t) bmx = fmaxf(bmx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
+    const float tS = xg_max(bmx);
+    const bool vis = tS > -INFINITY;
+    float T = 0.0f;  // tile maximum in log2 units, rounded toward -infinity
+    if (vis) {
+      T = tS * k2;
+      if (__builtin_fmaf(tS, k2, -T) < 0.0f)  // the product was rounded up: step one ulp down
+        T = T > 0.0f ? as_f(as_u(T) - 1u) : (T < 0.0f ? as_f(as_u(T) + 1u) : -0x1p-149f);
+    }
+    const float m_new = fmaxf(m_u, T);
+    const bool accept = vis && (T >= m_new - 64.0f);
 
-    float E[32], esum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      E[e] = __builtin_amdgcn_exp2f(x[e] - tt);
-      esum += E[e];
-    }
-    // the lane's block: E8M0 scale 2^(floor(log2 amax) - 2); amax = exp2(block max - t)
-    const float amax = __builtin_amdgcn_exp2f(bmx - tt);
-    int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - 2;  // amax is 0 or normal for X >= -126
+    // the lane's block: E8M0 scale 2^(floor(log2 amax) - 2), amax = the block maximum of E;
+    // then E chunk by chunk, summed and packed at once
+    const float amax = exp2_01(__builtin_fmaf(bmx, k2, -T));
+    const int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - 2;  // amax is 0 or normal for X >= -126
+    const bool keep = accept && amax >= 0x1p-124f;
+    const float sc = as_f((unsigned)max(X + 127, 1) << 23);
+    float esum = 0.0f;
     v8i pf = {0, 0, 0, 0, 0, 0, 0, 0};
-    int psc = 127;
-    if (accept && amax >= 0x1p-124f) {
-      const float sc = as_f((unsigned)(X + 127) << 23);
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) pf[wd] = (int)pack_e4(E + 8 * wd, sc);
-      psc = X + 127;
+    for (int wd = 0; wd < 4; ++wd) {
+      float E[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        E[e] = exp2_01(__builtin_fmaf(S[2 * wd + (e >> 2)][e & 3], k2, -T));
+        esum += E[e];
+      }
+      pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
     }
+    const int psc = keep ? X + 127 : 127;
     if (!accept) esum = 0.0f;
-    const float factor = accept ? __builtin_amdgcn_exp2f(R - t_u) : 1.0f;
-    R = accept ? t_u : R;
+    const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
+    R = accept ? T : R;
     m_u = m_new;
     l = l * factor + esum;
 #pragma unroll
@@ -192,9 +205,9 @@ template <int D, bool CAUSAL, bool F32>
 static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + MX_BQ - 1) / MX_BQ;
-  attn_mxfp4_kernel<D, CAUSAL, F32><<<dim3(nqt, BH), dim3(512), 0, st>>>(
+  attn_mxfp4_kernel<D, CAUSAL, F32><<<dim3(nqt * BH), dim3(512), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, k2, out);
 }
 
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
