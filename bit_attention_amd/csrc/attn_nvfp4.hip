@@ -17,6 +17,9 @@
 //     computes.
 //   - key tiles of 128: K and V codes of the next tile are loaded into registers while the
 //     current tile is computed, then dequantised into LDS between two barriers.
+//   - MFMA operands are read from LDS two MFMA pairs ahead through a ring of three fragments
+//     (a scheduling barrier per step stops the compiler from hoisting further, which would
+//     cost registers: the kernel sits at the 256-VGPR limit of two waves per SIMD).
 //   - each group computes S^T = K Q^T for its 16 queries: after 8 subtiles a lane holds the 32
 //     scores of one query at keys 16t + 4g + i, exactly the slot order the quantisation kernel
 //     stores V in, so P's 1x16 blocks are lane-local (two per lane per tile), their maxima come
@@ -222,17 +225,24 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     __syncthreads();
     if (kt + 1 < kt_end) prefetch(kt + 1);
 
-    // ---- S^T = K-hat Q-hat^T for both groups: subtile t covers keys 16t..16t+15
+    // ---- S^T = K-hat Q-hat^T for both groups: subtile t covers keys 16t..16t+15. Operand
+    // reads run two MFMA pairs ahead through a ring of three fragments.
     v4f S[2][8];
+    {
+      constexpr int NS = 8 * (D / 32);
+      const _Float16* K = sK + c * KP + 8 * g;
+      auto kaddr = [&](int s) { return K + 16 * (s / (D / 32)) * KP + 32 * (s % (D / 32)); };
+      v8h f[3];
+      f[0] = *reinterpret_cast<const v8h*>(kaddr(0));
+      f[1] = *reinterpret_cast<const v8h*>(kaddr(1));
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      S[0][t] = v4f{0, 0, 0, 0};
-      S[1][t] = v4f{0, 0, 0, 0};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const v8h a = *reinterpret_cast<const v8h*>(sK + (16 * t + c) * KP + 32 * kk + 8 * g);
-        S[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[0][kk], S[0][t], 0, 0, 0);
-        S[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[1][kk], S[1][t], 0, 0, 0);
+      for (int s2 = 0; s2 < NS; ++s2) {
+        if (s2 + 2 < NS) f[(s2 + 2) % 3] = *reinterpret_cast<const v8h*>(kaddr(s2 + 2));
+        const int t = s2 / (D / 32), kk = s2 % (D / 32);
+        if (kk == 0) { S[0][t] = v4f{0, 0, 0, 0}; S[1][t] = v4f{0, 0, 0, 0}; }
+        S[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s2 % 3], qf[0][kk], S[0][t], 0, 0, 0);
+        S[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s2 % 3], qf[1][kk], S[1][t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- mask: keys past N, and keys after the query when causal
@@ -254,14 +264,22 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     softmax_tile<D>(S[1], k2, st[1], Pf[1]);
 
     // ---- O^T += V-hat^T P-hat^T: MFMA step u covers slots 32g + 8u .. +8 of every lane group
+    {
+      constexpr int NS = D / 16 * 4;
+      const _Float16* V = sV + c * VP + 32 * g;
+      auto vaddr = [&](int s) { return V + 16 * (s >> 2) * VP + 8 * (s & 3); };
+      v8h f[3];
+      f[0] = *reinterpret_cast<const v8h*>(vaddr(0));
+      f[1] = *reinterpret_cast<const v8h*>(vaddr(1));
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v8h a = *reinterpret_cast<const v8h*>(sV + (16 * dt + c) * VP + 32 * g + 8 * u);
-        st[0].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Pf[0][u], st[0].O[dt], 0, 0, 0);
-        st[1].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, Pf[1][u], st[1].O[dt], 0, 0, 0);
+      for (int s2 = 0; s2 < NS; ++s2) {
+        if (s2 + 2 < NS) f[(s2 + 2) % 3] = *reinterpret_cast<const v8h*>(vaddr(s2 + 2));
+        const int dt = s2 >> 2, u = s2 & 3;
+        st[0].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s2 % 3], Pf[0][u], st[0].O[dt], 0, 0, 0);
+        st[1].O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s2 % 3], Pf[1][u], st[1].O[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
   }
 
   // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of its query in each group
