@@ -109,7 +109,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--causal", action="store_true", help="time the causal variant instead")
     ap.add_argument("--fmt", choices=["nvfp4", "mxfp4"], default="nvfp4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
