@@ -63,6 +63,15 @@ __device__ __forceinline__ unsigned pack_fp4_8(const float* q) {
   return w;
 }
 
+// Half-precision offset of 16-byte chunk `ch` of row `row` in the K-hat tile (rows of D halves,
+// chunk index XOR row mod D/8) and in the V-hat tile (rows of 128 halves, chunk index XOR a
+// residue mixing the row's low and high bit pairs).
+template <int D>
+__device__ __forceinline__ int lds_k(int row, int ch) { return row * D + 8 * (ch ^ (row & (D / 8 - 1))); }
+__device__ __forceinline__ int lds_v(int row, int ch) {
+  return row * KV_TILE + 8 * (ch ^ (((row & 3) << 2) | ((row >> 2) & 3)));
+}
+
 // Online-softmax state of one 16-query group (per lane: one query, a quarter of its channels).
 template <int D>
 struct RowState {
@@ -75,14 +84,14 @@ struct RowState {
 // four B operands of the PV product, and O, l2 have been rescaled to this tile's reference.
 template <int D>
 __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, v8h* Pf) {
-  float bm[2];
+  float bm[2];  // block maxima: a chain of three-input maxima over the block's 16 scores
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 4 * h; t < 4 * h + 4; ++t)
-      mx = fmaxf(fmaxf(mx, fmaxf(S[t][0], S[t][1])), fmaxf(S[t][2], S[t][3]));
-    bm[h] = mx;
+    const v4f* B = S + 4 * h;
+    const float a = max3f(B[0][0], B[0][1], B[0][2]), b = max3f(B[0][3], B[1][0], B[1][1]);
+    const float c = max3f(B[1][2], B[1][3], B[2][0]), d = max3f(B[2][1], B[2][2], B[2][3]);
+    const float e = max3f(B[3][0], B[3][1], B[3][2]);
+    bm[h] = fmaxf(max3f(a, b, c), max3f(d, e, B[3][3]));
   }
   const float tS = xg_max(fmaxf(bm[0], bm[1]));
   const bool vis = tS > -INFINITY;
@@ -99,7 +108,8 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
     const unsigned sb = e4m3_encode(pmax * (1.0f / 6.0f));
     sP[h] = e4m3_decode(sb);
     bq[h] = sP[h] > 0.0f ? bias - __builtin_amdgcn_logf(sP[h]) : -INFINITY;  // log2(P2/s)
-    const _Float16 s16 = (_Float16)sP[h];
+    // a rejected tile contributes nothing: its P blocks get scale 0 (codes are finite)
+    const _Float16 s16 = accept ? (_Float16)sP[h] : (_Float16)0.0f;
     sh[h] = v2h{s16, s16};
   }
   float qsum[2] = {0.0f, 0.0f};
@@ -112,7 +122,7 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
       q[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * u + (jj >> 2)][jj & 3], k2, bq[h]));  // P2/s
       qsum[h] += q[jj];
     }
-    Pf[u] = accept ? dequant8(pack_fp4_8(q), sh[h]) : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+    Pf[u] = dequant8(pack_fp4_8(q), sh[h]);
   }
   const float l2t = accept ? sP[0] * qsum[0] + sP[1] * qsum[1] : 0.0f;
   const float factor = accept ? __builtin_amdgcn_exp2f(st.R - t_u) : 1.0f;
@@ -128,13 +138,15 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
-  constexpr int KP = D + 8;        // K-hat row pitch (halves)
-  constexpr int VP = KV_TILE + 8;  // V-hat row pitch (halves)
+  constexpr int KC = D / 8;        // 16-byte chunks per K-hat row (16 or 8)
   constexpr int CB = D / 4;        // code bytes each thread stages per tile, for K and for V
   constexpr int CW = CB / 4;       // ... in dwords (8 codes each; two dwords per 16-block)
-  constexpr int VT = 64 / CB;      // threads per V channel row (64 code bytes per tile)
-  __shared__ __attribute__((aligned(16))) _Float16 sK[KV_TILE * KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[D * VP];
+  // LDS tiles with unpadded rows whose 16-byte chunks are XOR-swizzled per row (lds_k, lds_v).
+  // The swizzles were chosen against gfx950's LDS banking as measured with the bank-conflict
+  // counter: K's makes both the QK operand reads and the staging writes conflict-free, V's the
+  // PV operand reads; V's staging lanes are grouped (below) so that its writes are too.
+  __shared__ __attribute__((aligned(16))) _Float16 sK[KV_TILE * D];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[D * KV_TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -171,38 +183,52 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   }
 
   // staging assignment: K row `kkey`, code bytes [kpart*CB, +CB); V channel `vd`, bytes
-  // [vpart*CB, +CB) of the tile's 64
-  const int kkey = tid >> 1, kpart = tid & 1;
-  const int vd = tid / VT, vpart = tid % VT;
-  const uint8_t* vcrow = vc + (bh * D + vd) * (Np / 2) + vpart * CB;
-  const uint8_t* vsrow = vs + (bh * D + vd) * (Np / 16) + vpart * (CB / 8);
+  // [vpart*CB, +CB) of the tile's 64. A write instruction is served eight consecutive lanes at a
+  // time, which must hit distinct 16-byte slots modulo 128 bytes: with D = 128 eight consecutive
+  // lanes take eight consecutive K rows; for V they take rows whose swizzle residues differ
+  // (offsets 0, 1, 4, 5, 8, 9, 12, 13 of a 16-row group, or those plus 2).
+  const int kkey = D == 128 ? 32 * w + (lane & 15) + 16 * (lane >> 5) : tid >> 1;
+  const int kpart = D == 128 ? (lane >> 4) & 1 : tid & 1;
+  const int vgrp = lane >> 3, vpos = lane & 7;
+  const int vrow16 = (vpos & 1) + 4 * (vpos >> 1);
+  const int vd = D == 128 ? 32 * w + 16 * (vgrp >> 2) + vrow16 + 2 * ((vgrp >> 1) & 1)
+                          : 16 * w + vrow16 + 2 * (vgrp & 1);
+  const int vpart = D == 128 ? vgrp & 1 : vgrp >> 1;
+  // wave-uniform bases of this (batch, head); per-thread offsets stay 32-bit
+  const uint8_t* kc_h = kc + bh * N * (D / 2);
+  const uint8_t* ks_h = ks + bh * N * (D / 16);
+  const uint8_t* vc_h = vc + bh * D * (Np / 2);
+  const uint8_t* vs_h = vs + bh * D * (Np / 16);
+  const unsigned vc_off = (unsigned)(vd * (Np / 2) + vpart * CB);
+  const unsigned vs_off = (unsigned)(vd * (Np / 16) + vpart * (CB / 8));
   unsigned kr[CW], vr[CW], ksr = 0, vsr = 0;
 
   auto prefetch = [&](int kt) {
     const int j = kt * KV_TILE + kkey;
     if (j < N) {
-      const int64_t row = bh * N + j;
-      const uint4* src = reinterpret_cast<const uint4*>(kc + row * (D / 2) + kpart * CB);
+      const uint4* src = reinterpret_cast<const uint4*>(kc_h + (unsigned)(j * (D / 2) + kpart * CB));
 #pragma unroll
       for (int u = 0; u < CW / 4; ++u) {
         const uint4 x = src[u];
         kr[4 * u] = x.x; kr[4 * u + 1] = x.y; kr[4 * u + 2] = x.z; kr[4 * u + 3] = x.w;
       }
-      if (CB / 8 == 4) ksr = *reinterpret_cast<const unsigned*>(ks + row * (D / 16) + kpart * 4);
-      else ksr = *reinterpret_cast<const unsigned short*>(ks + row * (D / 16) + kpart * 2);
+      const uint8_t* sp = ks_h + (unsigned)(j * (D / 16) + kpart * (CB / 8));
+      if (CB / 8 == 4) ksr = *reinterpret_cast<const unsigned*>(sp);
+      else ksr = *reinterpret_cast<const unsigned short*>(sp);
     } else {
 #pragma unroll
       for (int u = 0; u < CW; ++u) kr[u] = 0;
       ksr = 0;
     }
-    const uint4* vsrc = reinterpret_cast<const uint4*>(vcrow + (int64_t)kt * 64);
+    const uint4* vsrc = reinterpret_cast<const uint4*>(vc_h + (vc_off + (unsigned)kt * 64u));
 #pragma unroll
     for (int u = 0; u < CW / 4; ++u) {
       const uint4 x = vsrc[u];
       vr[4 * u] = x.x; vr[4 * u + 1] = x.y; vr[4 * u + 2] = x.z; vr[4 * u + 3] = x.w;
     }
-    if (CB / 8 == 4) vsr = *reinterpret_cast<const unsigned*>(vsrow + (int64_t)kt * 8);
-    else vsr = *reinterpret_cast<const unsigned short*>(vsrow + (int64_t)kt * 8);
+    const uint8_t* vsp = vs_h + (vs_off + (unsigned)kt * 8u);
+    if (CB / 8 == 4) vsr = *reinterpret_cast<const unsigned*>(vsp);
+    else vsr = *reinterpret_cast<const unsigned short*>(vsp);
   };
 
   const int ntiles = (int)(Np / KV_TILE);
@@ -214,12 +240,10 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
       _Float16 kh[4], vh[4];
       scales4(ksr, kh);
       scales4(vsr, vh);
-      _Float16* kdst = sK + kkey * KP + kpart * 2 * CB;
-      _Float16* vdst = sV + vd * VP + vpart * 2 * CB;
 #pragma unroll
       for (int u = 0; u < CW; ++u) {
-        *reinterpret_cast<v8h*>(kdst + 8 * u) = dequant8(kr[u], v2h{kh[u >> 1], kh[u >> 1]});
-        *reinterpret_cast<v8h*>(vdst + 8 * u) = dequant8(vr[u], v2h{vh[u >> 1], vh[u >> 1]});
+        *reinterpret_cast<v8h*>(sK + lds_k<D>(kkey, CW * kpart + u)) = dequant8(kr[u], v2h{kh[u >> 1], kh[u >> 1]});
+        *reinterpret_cast<v8h*>(sV + lds_v(vd, CW * vpart + u)) = dequant8(vr[u], v2h{vh[u >> 1], vh[u >> 1]});
       }
     }
     __syncthreads();
@@ -230,8 +254,8 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     v4f S[2][8];
     {
       constexpr int NS = 8 * (D / 32);
-      const _Float16* K = sK + c * KP + 8 * g;
-      auto kaddr = [&](int s) { return K + 16 * (s / (D / 32)) * KP + 32 * (s % (D / 32)); };
+      // row 16t + c, chunk 4kk + g; the swizzle depends on the row only through c
+      auto kaddr = [&](int s) { return sK + 16 * (s / (D / 32)) * D + lds_k<D>(c, 4 * (s % (D / 32)) + g); };
       v8h f[3];
       f[0] = *reinterpret_cast<const v8h*>(kaddr(0));
       f[1] = *reinterpret_cast<const v8h*>(kaddr(1));
@@ -266,8 +290,8 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     // ---- O^T += V-hat^T P-hat^T: MFMA step u covers slots 32g + 8u .. +8 of every lane group
     {
       constexpr int NS = D / 16 * 4;
-      const _Float16* V = sV + c * VP + 32 * g;
-      auto vaddr = [&](int s) { return V + 16 * (s >> 2) * VP + 8 * (s & 3); };
+      // row 16dt + c, chunk 4g + u; the swizzle depends on the row only through c
+      auto vaddr = [&](int s) { return sV + 16 * (s >> 2) * KV_TILE + lds_v(c, 4 * g + (s & 3)); };
       v8h f[3];
       f[0] = *reinterpret_cast<const v8h*>(vaddr(0));
       f[1] = *reinterpret_cast<const v8h*>(vaddr(1));

@@ -54,6 +54,13 @@ __device__ __forceinline__ float e4m3_decode(unsigned b) { return __builtin_amdg
 // 2^floor(log2 s) for s > 0 (s normal FP32), 1 for s == 0.
 __device__ __forceinline__ float pow2_floor(float s) { return s > 0.0f ? as_f(as_u(s) & 0xFF800000u) : 1.0f; }
 
+// max(a, b, c) in one v_max3_f32 (the compiler re-balances fmaxf trees into pairs otherwise).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Max over the four lanes {l, l^16, l^32, l^48} that share a column of a 16x16 MFMA tile.
 __device__ __forceinline__ float xg_max(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
