@@ -106,11 +106,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   scales[b] = (uint8_t)sb;
 }
 
-// V: one workgroup per (batch*head, 128-token tile). The tile is staged in LDS (row pitch D+2
-// halves to spread banks), then each thread quantises (channel, block) items whose BLK values
-// are gathered in slot order. Token positions >= N are zero.
+// V, MXFP4: one workgroup per (batch*head, 128-token tile). The tile is staged in LDS (row pitch
+// D+2 halves to spread banks), then each thread quantises (channel, block) items whose 32 values
+// are gathered in slot order; with 32-value blocks this beats the register gather below, whose
+// blocks would need more registers than four waves per SIMD allow. Token positions >= N are zero.
 template <int D, int BLK, bool MX>
-__global__ __launch_bounds__(256) void quant_v_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void quant_v_lds_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, int N, int64_t Np) {
   constexpr int PITCH = D + 2;
   __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
@@ -147,6 +148,76 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const __half* __restrict__
   }
 }
 
+// V, NVFP4: one wave per (batch*head, pair of 128-token tiles). Each lane owns a channel pair; with
+// D = 128 the 64 lanes cover all channels and walk the two tiles in turn, with D = 64 each half
+// of the wave takes one tile. A token's channels are read by the lanes of that tile together
+// (one contiguous row per load), so the gather into slot order needs no LDS: a lane reads its
+// two channels token by token in the order the blocks take them. Each lane then writes its
+// channels' 64 code bytes per tile (a tile pair's 128 bytes come from one wave) and their scale
+// bytes. Token positions >= N are zero.
+template <int D, int BLK, bool MX>
+__global__ __launch_bounds__(256) void quant_v_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, int N, int64_t Np,
+                                                      int npairs, int nwaves) {
+  constexpr int LPT = D / 2;            // lanes per tile (one channel pair each)
+  constexpr int PASSES = LPT / 32;      // tiles of the pair walked in turn: 2 (D = 128) or 1
+  constexpr int NB = KV_TILE / BLK;     // blocks per channel per tile
+  constexpr int WPB = BLK / 8;          // code dwords per block
+  const int lane = threadIdx.x & 63;
+  const int wv = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (wv >= nwaves) return;  // whole waves only; the kernel has no barrier
+  const int64_t bh = wv / npairs;
+  const int pr = wv % npairs;
+  const int ntiles = (int)(Np / KV_TILE);
+  const int d0 = 2 * (lane % LPT);
+  const __half* xs = x + bh * N * (int64_t)D + d0;
+#pragma unroll 1
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int kt = 2 * pr + (PASSES == 2 ? pass : lane / LPT);
+    if (kt >= ntiles) break;
+    const int tok0 = kt * KV_TILE;
+    unsigned cw[2][NB * WPB];
+    unsigned sbytes[2][NB];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      float v[2][BLK];
+#pragma unroll
+      for (int u = 0; u < BLK; ++u) {
+        const int tok = tok0 + slot_token(blk * BLK + u);
+        unsigned bits = 0;
+        if (tok < N) bits = *reinterpret_cast<const unsigned*>(xs + (int64_t)tok * D);
+        v[0][u] = (float)__ushort_as_half((unsigned short)(bits & 0xFFFF));
+        v[1][u] = (float)__ushort_as_half((unsigned short)(bits >> 16));
+      }
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[ch][u]));
+        float sc;
+        sbytes[ch][blk] = MX ? mx_scale(amax, &sc) : nv_scale(amax, &sc);
+        encode_block<BLK>(v[ch], sc, MX, &cw[ch][blk * WPB]);
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int64_t row = bh * D + d0 + ch;
+      uint4* crow = reinterpret_cast<uint4*>(codes + row * (Np / 2) + (int64_t)kt * (KV_TILE / 2));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) crow[q] = make_uint4(cw[ch][4 * q], cw[ch][4 * q + 1], cw[ch][4 * q + 2], cw[ch][4 * q + 3]);
+      uint8_t* srow = scales + row * (Np / BLK) + (int64_t)kt * NB;
+      if (NB == 8) {
+        *reinterpret_cast<uint2*>(srow) =
+            make_uint2(sbytes[ch][0] | sbytes[ch][1] << 8 | sbytes[ch][2] << 16 | sbytes[ch][3] << 24,
+                       sbytes[ch][NB > 4 ? 4 : 0] | sbytes[ch][NB > 5 ? 5 : 0] << 8 |
+                           sbytes[ch][NB > 6 ? 6 : 0] << 16 | sbytes[ch][NB > 7 ? 7 : 0] << 24);
+      } else {
+        *reinterpret_cast<unsigned*>(srow) = sbytes[ch][0] | sbytes[ch][1] << 8 | sbytes[ch][2] << 16 | sbytes[ch][3] << 24;
+      }
+    }
+  }
+}
+
 // ---- launchers (arguments already validated by the C ABI layer) ----
 hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* codes, void* scales, hipStream_t st) {
   const int blk = mx ? 32 : 16;
@@ -159,15 +230,18 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
 
 hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
-  const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
   const __half* xp = (const __half*)x;
   uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
-  if (D == 64) {
-    if (mx) quant_v_kernel<64, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
-    else quant_v_kernel<64, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+  if (mx) {
+    const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
+    if (D == 64) quant_v_lds_kernel<64, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    else quant_v_lds_kernel<128, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
   } else {
-    if (mx) quant_v_kernel<128, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
-    else quant_v_kernel<128, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    const int npairs = (int)((Np / KV_TILE + 1) / 2);
+    const int nwaves = BH * npairs;
+    const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
+    if (D == 64) quant_v_kernel<64, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np, npairs, nwaves);
+    else quant_v_kernel<128, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np, npairs, nwaves);
   }
   return hipGetLastError();
 }
