@@ -41,7 +41,7 @@ def test_workloads_1_and_5_all_rows(wl, fmt, causal):
 
 
 FULL = [(2, orc.NVFP4, False), (2, orc.NVFP4, True), (3, orc.NVFP4, False), (4, orc.NVFP4, True),
-        (2, orc.MXFP4, False)]
+        (2, orc.MXFP4, False), (2, orc.MXFP4, True), (3, orc.MXFP4, False), (4, orc.MXFP4, True)]
 
 
 @pytest.mark.parametrize("wl,fmt,causal", FULL)
@@ -58,6 +58,26 @@ def test_full_size_sampled_rows(wl, fmt, causal):
     o, sl = oracle_attn(fmt, *sub, causal, rows=rows)
     gr = np.concatenate([g.reshape(B * H, N, D)[h][rows_i] for h in heads])
     compare(gr, o, sl, f"workload {wl} fmt {fmt} causal {causal}")
+
+
+@pytest.mark.parametrize("N", [1024, 2048, 8192, 16384])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sweep_lengths_sampled_rows(N, causal):
+    """The sequence lengths of the kernel sweep (D = 128, N(0,1) data) with 9 heads, an odd head
+    count, so the workgroup count is not a multiple of the 8 XCDs."""
+    B, H, D = 1, 9, 128
+    q, k, v = workload(2, B=B, H=H, N=N, D=D)
+    say(f"attn sweep N={N} causal={causal}")
+    for fmt in (orc.NVFP4, orc.MXFP4):
+        g = gpu_attn(fmt, q, k, v, causal)
+        assert np.all(np.isfinite(g)), "unwritten or non-finite outputs"
+        heads = [0, 4, 8]
+        rows_i = sample_rows(N, n_each=4, seed=N)
+        rows = np.concatenate([u * N + rows_i for u in range(len(heads))])
+        sub = tuple(x[:, heads] for x in (q, k, v))
+        o, sl = oracle_attn(fmt, *sub, causal, rows=rows)
+        gr = np.concatenate([g.reshape(B * H, N, D)[h][rows_i] for h in heads])
+        compare(gr, o, sl, f"sweep N={N} fmt {fmt} causal {causal}")
 
 
 @pytest.mark.parametrize("fmt", [orc.NVFP4, orc.MXFP4])
