@@ -60,6 +60,8 @@ def lib():
         L.orc_p_tile.argtypes = [I, P, P, P, P, P, P]; L.orc_p_tile.restype = I
         L.orc_attn_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, F, P, I64, P, P, D, I]
         L.orc_attn_fwd.restype = I
+        L.orc_attn_fwd_direct_p.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I64, P, P, D, I]
+        L.orc_attn_fwd_direct_p.restype = I
         L.orc_attn_ref_f64.argtypes = [P, P, P, I, I, I, I, I, D, P, I64, P, I]
         L.orc_attn_ref_f64.restype = I
         L.orc_max_threads.argtypes = []; L.orc_max_threads.restype = I
@@ -98,10 +100,13 @@ def quant(role: int, fmt: int, x: np.ndarray):
 
 
 def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, rows=None, want_slack=False,
-             delta=2.0 ** -14, nthreads=0):
-    """q, k, v: (codes, scales) tuples from quant(); shape = (B,H,N,D).
+             delta=2.0 ** -14, nthreads=0, direct_p=False):
+    """q, k, v: (codes, scales) tuples from quant(); shape = (B,H,N,D). direct_p selects the
+    Direct-P normaliser (MXFP4 operands only).
 
     Returns out float32 ([B,H,N,D], or [len(rows), D]) and, if want_slack, per-row slack."""
+    if direct_p and fmt != MXFP4:
+        raise ValueError("Direct-P takes MXFP4 operands")
     B, H, N, D = shape
     arrs = [np.ascontiguousarray(a) for t in (q, k, v) for a in t]
     if rows is None:
@@ -114,9 +119,12 @@ def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, rows=None, want_sl
         rp, nr = _p(rows), len(rows)
         nslack = len(rows)
     slack = np.zeros(nslack, np.float64) if want_slack else None
-    rc = lib().orc_attn_fwd(fmt, *[_p(a) for a in arrs], B, H, N, D, int(causal), float(sm_scale),
-                            rp, nr, _p(out), _p(slack) if want_slack else None, float(delta),
-                            int(nthreads))
+    tail = (B, H, N, D, int(causal), float(sm_scale), rp, nr, _p(out), _p(slack) if want_slack else None,
+            float(delta), int(nthreads))
+    if direct_p:
+        rc = lib().orc_attn_fwd_direct_p(*[_p(a) for a in arrs], *tail)
+    else:
+        rc = lib().orc_attn_fwd(fmt, *[_p(a) for a in arrs], *tail)
     if rc != 0:
         raise ValueError(f"orc_attn_fwd failed ({rc})")
     return (out, slack) if want_slack else out

@@ -41,6 +41,11 @@
  *     skipped.
  *  R12 S sums block partials (each exact in FP32) in block order; l sums E in key order; the
  *     PV accumulation sums block partials in slot order.
+ *  R13 Direct-P (the rit.work page on FP4 FlashAttention-4, section on what was done: scores
+ *     go straight to the MXFP4 codes the second matmul consumes, and the normaliser is taken
+ *     from the same rounded values): MXFP4 codes and scales of P exactly as R9, and the
+ *     normaliser sums the dequantised P instead of E: per tile, the block partials
+ *     scale * sum(code) in block order.
  *
  * Slack (test aid, not part of the method): a P rounding decision whose input lies within
  * relative delta of its boundary may legitimately go either way in an implementation whose
@@ -285,12 +290,12 @@ static double block_ambiguity(int fmt, const float* P2, const uint8_t* codes, un
   return worst_scale + elem;
 }
 
-int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
-                 const uint8_t* k_codes, const uint8_t* k_scales,
-                 const uint8_t* v_codes, const uint8_t* v_scales,
-                 int B, int H, int N, int D, int causal, float sm_scale,
-                 const int64_t* rows, int64_t n_rows, float* out,
-                 double* slack, double delta, int nthreads) {
+static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const uint8_t* q_scales,
+                         const uint8_t* k_codes, const uint8_t* k_scales,
+                         const uint8_t* v_codes, const uint8_t* v_scales,
+                         int B, int H, int N, int D, int causal, float sm_scale,
+                         const int64_t* rows, int64_t n_rows, float* out,
+                         double* slack, double delta, int nthreads) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out) return ORC_ERR_ARG;
   if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return ORC_ERR_ARG;
   if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return ORC_ERR_ARG;
@@ -351,8 +356,16 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
       const float alpha = (float)exp((double)m - (double)mn);
       const float beta = (float)exp((double)t - (double)mn);
       float sumE = 0.0f;
-      for (int o = 0; o < ORC_KV_TILE; ++o) sumE += E[slot_of_token[o]]; /* key order */
-      l = alpha * l + beta * sumE;                                       /* R8 */
+      if (!direct_p) {
+        for (int o = 0; o < ORC_KV_TILE; ++o) sumE += E[slot_of_token[o]]; /* key order, R8 */
+      } else {
+        for (int b = 0; b < ORC_KV_TILE / blk; ++b) {                      /* R13 */
+          float inner = 0.0f;
+          for (int u = 0; u < blk; ++u) inner += orc_e2m1_decode(pc[b * blk + u]);
+          sumE += scale_val(fmt, ps[b]) * inner;
+        }
+      }
+      l = alpha * l + beta * sumE;
       const float w = beta / Kp;                                          /* R7/R9 */
       for (int d = 0; d < D; ++d) {
         const uint8_t* vc = v_codes + (bh * D + d) * (Np / 2);
@@ -371,6 +384,19 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
       }
       m = mn;
       if (slack) {
+        /* With Direct-P a changed P value also moves the normaliser: the output then moves by
+         * at most |dP| (|v| + max|O|) / l, and max|O| <= the head's largest |V-hat|. */
+        double vhead = 0.0;
+        if (direct_p) {
+          for (int d = 0; d < D; ++d) {
+            const uint8_t* vc = v_codes + (bh * D + d) * (Np / 2);
+            const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
+            for (int64_t p = 0; p < Np; ++p) {
+              double v = fabs((double)orc_e2m1_decode(get_code(vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+              if (v > vhead) vhead = v;
+            }
+          }
+        }
         double vmax[ORC_KV_TILE];
         float P2[ORC_KV_TILE];
         for (int s = 0; s < ORC_KV_TILE; ++s) {
@@ -382,7 +408,7 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
             double v = fabs((double)orc_e2m1_decode(get_code(vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
             if (v > mv) mv = v;
           }
-          vmax[s] = mv;
+          vmax[s] = mv + vhead;
           P2[s] = fmt == ORC_NVFP4 ? 2688.0f * E[s] : E[s];
         }
         /* The tile maximum has E = exp(0) = 1 exactly in any implementation, unless another
@@ -417,6 +443,26 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
     free(tile_amb);
   }
   return ORC_OK;
+}
+
+int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
+                 const uint8_t* k_codes, const uint8_t* k_scales,
+                 const uint8_t* v_codes, const uint8_t* v_scales,
+                 int B, int H, int N, int D, int causal, float sm_scale,
+                 const int64_t* rows, int64_t n_rows, float* out,
+                 double* slack, double delta, int nthreads) {
+  return attn_fwd_impl(fmt, 0, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, B, H, N, D, causal,
+                       sm_scale, rows, n_rows, out, slack, delta, nthreads);
+}
+
+int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
+                          const uint8_t* k_codes, const uint8_t* k_scales,
+                          const uint8_t* v_codes, const uint8_t* v_scales,
+                          int B, int H, int N, int D, int causal, float sm_scale,
+                          const int64_t* rows, int64_t n_rows, float* out,
+                          double* slack, double delta, int nthreads) {
+  return attn_fwd_impl(ORC_MXFP4, 1, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, B, H, N, D,
+                       causal, sm_scale, rows, n_rows, out, slack, delta, nthreads);
 }
 
 int orc_attn_ref_f64(const uint16_t* q, const uint16_t* k, const uint16_t* v,

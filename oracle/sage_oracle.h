@@ -90,6 +90,16 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
                  const int64_t* rows, int64_t n_rows, float* out,
                  double* slack, double delta, int nthreads);
 
+/* ---- Direct-P variant (MXFP4 operands): as orc_attn_fwd with fmt = MXFP4, except that the
+ * softmax normaliser sums the dequantised P (code * block scale) instead of the unquantised
+ * E (rit.work page on FP4 FlashAttention-4: the normaliser comes from the rounded values). */
+int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
+                          const uint8_t* k_codes, const uint8_t* k_scales,
+                          const uint8_t* v_codes, const uint8_t* v_scales,
+                          int B, int H, int N, int D, int causal, float sm_scale,
+                          const int64_t* rows, int64_t n_rows, float* out,
+                          double* slack, double delta, int nthreads);
+
 /* ---- unquantised reference: softmax(c Q K^T) V in double from fp16 inputs ---- */
 int orc_attn_ref_f64(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      int B, int H, int N, int D, int causal, double sm_scale,
