@@ -224,17 +224,20 @@ def main():
 
     if not args.no_extras:
         extras = {}
-        for name, f2, c2 in (("nvfp4_causal", bnd.NVFP4, True), ("mxfp4_noncausal", bnd.MXFP4, False),
-                             ("mxfp4_causal", bnd.MXFP4, True)):
-            if f2 == fmt and c2 == causal:
+        for name, f2, c2, dp in (("nvfp4_causal", bnd.NVFP4, True, False),
+                                 ("mxfp4_noncausal", bnd.MXFP4, False, False),
+                                 ("mxfp4_causal", bnd.MXFP4, True, False),
+                                 ("mxfp4_direct_p_noncausal", bnd.MXFP4, False, True),
+                                 ("mxfp4_direct_p_causal", bnd.MXFP4, True, True)):
+            if f2 == fmt and c2 == causal and not dp:
                 continue
             Q2 = bnd.quant(q, bnd.ROLE_Q, f2); K2 = bnd.quant(k, bnd.ROLE_K, f2); V2 = bnd.quant(v, bnd.ROLE_V, f2)
             for _ in range(3):
-                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2)
+                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2, direct_p=dp)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(10):
-                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2)
+                bnd.attn_fwd_into(f2, Q2, K2, V2, shape, out, causal=c2, direct_p=dp)
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 10

@@ -17,7 +17,8 @@ OUT_F16, OUT_F32 = 0, 1
 STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR_HEAD_DIM",
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
-           "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_status_string"]
+           "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
+           "sage_fp4_status_string"]
 
 _lib = None
 
@@ -45,6 +46,8 @@ def lib():
         L.sage_fp4_quant.argtypes = [I, I, P, I, I, I, I, P, P, P]; L.sage_fp4_quant.restype = I
         L.sage_fp4_attn_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P]
         L.sage_fp4_attn_fwd.restype = I
+        L.sage_fp4_attn_fwd_direct_p.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I, P]
+        L.sage_fp4_attn_fwd_direct_p.restype = I
         L.sage_fp4_status_string.argtypes = [I]; L.sage_fp4_status_string.restype = C.c_char_p
         _lib = L
     return _lib
@@ -79,6 +82,12 @@ def sage_fp4_attn_fwd(fmt, qc, qs, kc, ks, vc, vs, B, H, N, D, causal, sm_scale,
                       stream_ptr) -> int:
     return lib().sage_fp4_attn_fwd(fmt, qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal), float(sm_scale),
                                    out_ptr, out_dtype, stream_ptr)
+
+
+def sage_fp4_attn_fwd_direct_p(qc, qs, kc, ks, vc, vs, B, H, N, D, causal, sm_scale, out_ptr, out_dtype,
+                               stream_ptr) -> int:
+    return lib().sage_fp4_attn_fwd_direct_p(qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal), float(sm_scale),
+                                            out_ptr, out_dtype, stream_ptr)
 
 
 def status_string(status: int) -> str:
@@ -128,26 +137,38 @@ def quant(x, role, fmt, stream=None):
     return quant_into(x, role, fmt, codes, scales, stream)
 
 
-def attn_fwd_into(fmt, q, k, v, shape, out, causal=False, sm_scale=0.0, stream=None):
+def _out_code(out):
     import torch
-    B, H, N, D = shape
     if out.dtype == torch.float32:
-        od = OUT_F32
-    elif out.dtype == torch.float16:
-        od = OUT_F16
-    else:
-        raise TypeError("out must be float16 or float32")
+        return OUT_F32
+    if out.dtype == torch.float16:
+        return OUT_F16
+    raise TypeError("out must be float16 or float32")
+
+
+def attn_fwd_into(fmt, q, k, v, shape, out, causal=False, sm_scale=0.0, stream=None, direct_p=False):
+    """direct_p=True calls sage_fp4_attn_fwd_direct_p (MXFP4 operands only)."""
+    B, H, N, D = shape
+    od = _out_code(out)
     ptrs = [C.c_void_p(t.data_ptr()) for pair in (q, k, v) for t in pair]
-    rc = sage_fp4_attn_fwd(fmt, *ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()), od,
-                           _stream_ptr(stream))
+    if direct_p:
+        if fmt != MXFP4:
+            raise ValueError("Direct-P takes MXFP4 operands")
+        rc = sage_fp4_attn_fwd_direct_p(*ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()), od,
+                                        _stream_ptr(stream))
+        what = "sage_fp4_attn_fwd_direct_p"
+    else:
+        rc = sage_fp4_attn_fwd(fmt, *ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()), od,
+                               _stream_ptr(stream))
+        what = "sage_fp4_attn_fwd"
     if rc != 0:
-        raise SageError(rc, "sage_fp4_attn_fwd")
+        raise SageError(rc, what)
     return out
 
 
-def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, out_dtype=None, stream=None):
+def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, out_dtype=None, stream=None, direct_p=False):
     """q, k, v: (codes, scales) pairs from quant(); returns out [B,H,N,D]."""
     import torch
     dt = torch.float32 if out_dtype is None else out_dtype
     out = torch.empty(shape, dtype=dt, device=q[0].device)
-    return attn_fwd_into(fmt, q, k, v, shape, out, causal, sm_scale, stream)
+    return attn_fwd_into(fmt, q, k, v, shape, out, causal, sm_scale, stream, direct_p)

@@ -13,6 +13,8 @@ hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool
                              void* out, bool out_f32, hipStream_t st);
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                              void* out, bool out_f32, hipStream_t st);
+hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
+                                      float sm_scale, void* out, bool out_f32, hipStream_t st);
 }  // namespace sage
 
 namespace {
@@ -35,7 +37,7 @@ int64_t padded(int N) { return ((int64_t)N + sage::KV_TILE - 1) / sage::KV_TILE 
 
 extern "C" {
 
-int sage_fp4_version(void) { return 100; }
+int sage_fp4_version(void) { return 200; }
 
 int sage_fp4_kv_tile(void) { return sage::KV_TILE; }
 
@@ -72,25 +74,50 @@ int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D,
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
+// Validation shared by both attention entry points; SAGE_OK when the call may launch.
+static int check_attn(const void* const* ptrs, int B, int H, int N, int D, const void* out, int out_dtype) {
+  if (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32) return SAGE_ERR_ENUM;
+  for (int i = 0; i < 6; ++i)
+    if (!ptrs[i]) return SAGE_ERR_NULL;
+  if (!out) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(ptrs[i])) return SAGE_ERR_ALIGN;
+  if (!aligned16(out)) return SAGE_ERR_ALIGN;
+  return SAGE_OK;
+}
+
+static float scale_or_default(float sm_scale, int D) {
+  return sm_scale > 0.0f ? sm_scale : (float)(1.0 / __builtin_sqrt((double)D));
+}
+
 int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                       const void* k_scales, const void* v_codes, const void* v_scales, int B, int H, int N,
                       int D, int causal, float sm_scale, void* out, int out_dtype, void* stream) {
   if (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4) return SAGE_ERR_ENUM;
-  if (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32) return SAGE_ERR_ENUM;
   const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
-  for (const void* p : ptrs)
-    if (!p) return SAGE_ERR_NULL;
-  if (!out) return SAGE_ERR_NULL;
-  const int sh = check_shape(B, H, N, D);
-  if (sh != SAGE_OK) return sh;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SAGE_ERR_ALIGN;
-  if (!aligned16(out)) return SAGE_ERR_ALIGN;
-  const float c = sm_scale > 0.0f ? sm_scale : (float)(1.0 / __builtin_sqrt((double)D));
+  const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
+  if (chk != SAGE_OK) return chk;
+  const float c = scale_or_default(sm_scale, D);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = fmt == SAGE_FMT_NVFP4
                            ? sage::launch_attn_nvfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st)
                            : sage::launch_attn_mxfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_fp4_attn_fwd_direct_p(const void* q_codes, const void* q_scales, const void* k_codes,
+                               const void* k_scales, const void* v_codes, const void* v_scales, int B, int H,
+                               int N, int D, int causal, float sm_scale, void* out, int out_dtype,
+                               void* stream) {
+  const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
+  const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
+  if (chk != SAGE_OK) return chk;
+  const float c = scale_or_default(sm_scale, D);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e =
+      sage::launch_attn_mxfp4_direct_p(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

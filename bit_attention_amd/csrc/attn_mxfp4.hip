@@ -39,7 +39,7 @@ __device__ __forceinline__ float exp2_01(float x) {
   return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.0f, 1.0f);
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P>
 __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
@@ -71,6 +71,7 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
   }
 
   float m_u = -INFINITY, R = -INFINITY, l = 0.0f;
+  v4f Lacc = {0, 0, 0, 0};  // Direct-P: every element holds the running sum of P-hat of query qi
   v4f O[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) O[dt] = v4f{0, 0, 0, 0};
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         E[e] = exp2_01(__builtin_fmaf(S[2 * wd + (e >> 2)][e & 3], k2, -T));
-        esum += E[e];
+        if (!DIRECT_P) esum += E[e];
       }
       pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
     }
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
     const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
     R = accept ? T : R;
     m_u = m_new;
-    l = l * factor + esum;
+    if (DIRECT_P) Lacc *= factor;
+    else l = l * factor + esum;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[dt] *= factor;
 
@@ -181,9 +183,16 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
       const int asc = sVs[(16 * dt + c) * 4 + g];
       O[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf, O[dt], 4, 4, 0, asc, 0, psc);
     }
+    if (DIRECT_P) {
+      // Direct-P normaliser: the sum of the rounded P values, as one more MFMA of P against a
+      // 16 x 128 tile of ones (E2M1 code 2 = 1.0, unit scale); all 16 rows of the product equal
+      // the row sum, and C's layout hands each lane the sum of its own query qi.
+      const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+      Lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, Lacc, 4, 4, 0, 127, 0, psc);
+    }
   }
 
-  const float L = xg_sum(l);
+  const float L = DIRECT_P ? Lacc[0] : xg_sum(l);
   if (qi < N) {
     const float inv = 1.0f / L;
     const int64_t row = bh * N + qi;
@@ -201,25 +210,36 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool F32>
+template <int D, bool CAUSAL, bool F32, bool DP>
 static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + MX_BQ - 1) / MX_BQ;
-  attn_mxfp4_kernel<D, CAUSAL, F32><<<dim3(nqt * BH), dim3(512), 0, st>>>(
+  attn_mxfp4_kernel<D, CAUSAL, F32, DP><<<dim3(nqt * BH), dim3(512), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
       (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, k2, out);
 }
 
-hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, hipStream_t st) {
+template <bool DP>
+static hipError_t launch_mx_any(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                                void* out, bool out_f32, hipStream_t st) {
   const float k2 = sm_scale * 1.4426950408889634f;
 #define SAGE_MX_CASE(DD, CC, FF) \
-  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF>(ptrs, BH, N, k2, out, st);
+  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF, DP>(ptrs, BH, N, k2, out, st);
   SAGE_MX_CASE(64, false, false) SAGE_MX_CASE(64, false, true) SAGE_MX_CASE(64, true, false)
   SAGE_MX_CASE(64, true, true) SAGE_MX_CASE(128, false, false) SAGE_MX_CASE(128, false, true)
   SAGE_MX_CASE(128, true, false) SAGE_MX_CASE(128, true, true)
 #undef SAGE_MX_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                             void* out, bool out_f32, hipStream_t st) {
+  return launch_mx_any<false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+}
+
+hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
+                                      float sm_scale, void* out, bool out_f32, hipStream_t st) {
+  return launch_mx_any<true>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
 }
 
 }  // namespace sage

@@ -93,6 +93,19 @@ int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales,
                       int B, int H, int N, int D, int causal, float sm_scale,
                       void* out, int out_dtype, void* stream);
 
+/* Direct-P variant of the MXFP4 attention forward (the rit.work page on FP4 FlashAttention-4,
+ * section on what was done): the scores go straight to the MXFP4 codes of P consumed by the
+ * second matmul, and the softmax normaliser is the sum of those rounded values (the decoded
+ * E2M1 codes times their E8M0 block scales) instead of the unquantised E. Everything else -
+ * operands (MXFP4 codes and scales from sage_fp4_quant with SAGE_FMT_MXFP4), tiles, P
+ * quantisation, masking, output layout, validation and errors - is that of sage_fp4_attn_fwd
+ * with fmt = SAGE_FMT_MXFP4. One kernel launch. */
+int sage_fp4_attn_fwd_direct_p(const void* q_codes, const void* q_scales,
+                               const void* k_codes, const void* k_scales,
+                               const void* v_codes, const void* v_scales,
+                               int B, int H, int N, int D, int causal, float sm_scale,
+                               void* out, int out_dtype, void* stream);
+
 /* Static description of a status code. */
 const char* sage_fp4_status_string(int status);
 

@@ -43,8 +43,9 @@ def gpu_quant(x, role, fmt):
     return c.cpu().numpy().reshape(B, H, N, D // 2), s.cpu().numpy().reshape(B, H, N, D // blk)
 
 
-def gpu_attn(fmt, q, k, v, causal, out_f32=True, prefill_nan=True):
-    """Full HIP path on numpy fp16 inputs: three quant launches + one attention launch."""
+def gpu_attn(fmt, q, k, v, causal, out_f32=True, prefill_nan=True, direct_p=False):
+    """Full HIP path on numpy fp16 inputs: three quant launches + one attention launch
+    (sage_fp4_attn_fwd, or sage_fp4_attn_fwd_direct_p when direct_p)."""
     import torch
     from bit_attention_amd import binding as bnd
     B, H, N, D = q.shape
@@ -54,18 +55,19 @@ def gpu_attn(fmt, q, k, v, causal, out_f32=True, prefill_nan=True):
     out = torch.empty((B, H, N, D), dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
     if prefill_nan:
         out.fill_(float("nan"))
-    bnd.attn_fwd_into(fmt, Q, K, V, (B, H, N, D), out, causal=causal)
+    bnd.attn_fwd_into(fmt, Q, K, V, (B, H, N, D), out, causal=causal, direct_p=direct_p)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()
 
 
-def oracle_attn(fmt, q, k, v, causal, rows=None):
+def oracle_attn(fmt, q, k, v, causal, rows=None, direct_p=False):
     """Oracle on its own quantisation of the same inputs; returns (out, slack)."""
     B, H, N, D = q.shape
     Q = orc.quant(orc.ROLE_Q, fmt, q)
     K = orc.quant(orc.ROLE_K, fmt, k)
     V = orc.quant(orc.ROLE_V, fmt, v)
-    return orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, rows=rows, want_slack=True)
+    return orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, rows=rows, want_slack=True,
+                        direct_p=direct_p)
 
 
 def sample_rows(N, n_each=8, seed=0):

@@ -84,6 +84,20 @@ def test_attn_validation():
         assert isinstance(bnd.status_string(s), str) and bnd.status_string(s)
 
 
+def test_attn_direct_p_validation():
+    a = bnd.sage_fp4_attn_fwd_direct_p
+    ok = [FAKE] * 6
+    assert a(*ok, 1, 1, 16, 64, 0, 0.0, FAKE, 7, None) == -5
+    assert a(*ok[:5], None, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -1
+    assert a(None, *ok[1:], 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -1
+    assert a(*ok, 1, 1, 16, 64, 0, 0.0, None, 0, None) == -1
+    assert a(*ok, 1, 1, 16, 96, 1, 0.0, FAKE, 1, None) == -3
+    assert a(*ok, 1, 1, 0, 64, 0, 0.0, FAKE, 1, None) == -2
+    assert a(*ok, 70000, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -2
+    assert a(*ok[:4], MIS, ok[5], 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -4
+    assert a(*ok, 1, 1, 16, 128, 1, 0.0, MIS, 0, None) == -4
+
+
 def test_library_does_not_link_the_oracle():
     """The product library and the oracle share no code: no oracle symbol is exported or needed."""
     import subprocess
