@@ -11,7 +11,10 @@
 // block of P in slot order, accumulator kept relative to the current tile maximum. At most 128
 // VGPRs, so two workgroups (4 waves per SIMD) share a CU: the softmax is VALU-bound and needs the
 // occupancy to overlap one wave's exp/packing with another's MFMAs. Workgroups are ordered so
-// that each XCD walks through whole heads.
+// that each XCD walks through whole heads. The next tile's codes and scales are loaded into
+// registers as soon as the current tile's scores are consumed, so the global loads overlap the
+// PV products and the barrier. Scale bytes sit in LDS so that a lane reads its eight K (or V)
+// scales of a tile as one 8-byte word; the instruction's op_sel bits pick the byte per MFMA.
 // P has no first level (E8M0 scales cover its range): its codes are E = 2^(x - t) quantised with
 // the lane-local block's power-of-two scale.
 //
@@ -35,12 +38,23 @@ __device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
   return w;
 }
 
+// FP4 x FP4 block-scaled MFMA whose A scale is byte `sel` of `sa` (the instruction's op_sel bits
+// pick the byte; `sel` is a constant after unrolling, so the switch folds away).
+__device__ __forceinline__ v4f mfma_fp4_sel(const v8i& a, const v8i& b, const v4f& c, int sel, int sa, int sb) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 1, sa, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 2, sa, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 3, sa, 0, sb);
+  }
+}
+
 __device__ __forceinline__ float exp2_01(float x) {
   return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.0f, 1.0f);
 }
 
 template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P>
-__global__ __launch_bounds__(512) void attn_mxfp4_kernel(
+__global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
@@ -48,9 +62,12 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
   constexpr int VROW = 64 + 16;      // V code row pitch (bytes): 128 slots
   constexpr int NBD = D / 32;        // MXFP4 blocks along D
   __shared__ __attribute__((aligned(16))) uint8_t sKc[KV_TILE * KROW];
+  // scale bytes, laid out so that lane (g, c) finds its eight per tile in one 8-byte word:
+  // K: byte (4c + g) * 8 + t holds key 16t + c's block g; V: byte (4c + g) * 8 + dt holds
+  // channel 16dt + c's block g (dt < D/16)
   __shared__ __attribute__((aligned(16))) uint8_t sKs[KV_TILE * 4];
   __shared__ __attribute__((aligned(16))) uint8_t sVc[D * VROW];
-  __shared__ __attribute__((aligned(16))) uint8_t sVs[D * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sVs[16 * 4 * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -78,48 +95,63 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
 
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + MX_BQ - 1) / KV_TILE + 1) : ntiles;
+
+  // Staging: each thread owns at most one 16-byte piece of the K codes, one of the V codes, the
+  // scale bytes of one key and one V channel's four scale bytes. The next tile's pieces are
+  // loaded into registers once the current tile's scores are consumed, so the loads are in
+  // flight during the PV products and the barrier.
+  constexpr int TPK = D / 32;  // 16-byte pieces per key row
+  const bool has_k = tid < KV_TILE * TPK, has_v = tid < D * 4;
+  const int kkey = tid / TPK, kpart = tid % TPK, vd = tid >> 2, vpart = tid & 3;
+  const uint8_t* kc_h = kc + bh * N * (D / 2);
+  const uint8_t* ks_h = ks + bh * N * NBD;
+  const uint8_t* vc_h = vc + bh * D * (Np / 2);   // uniform base; per-thread offsets below are 32-bit
+  const uint8_t* vs_h = vs + bh * D * (Np / 32);
+  const unsigned v_off = (unsigned)(vd * (Np / 2) + 16 * vpart), vs_off = (unsigned)(tid * (Np / 32));
+  uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
+  unsigned rks = 0, rvs = 0;
+  auto prefetch = [&](int kt) {
+    const int j = kt * KV_TILE + kkey;
+    if (has_k) {
+      rk = make_uint4(0, 0, 0, 0);
+      if (j < N) rk = *reinterpret_cast<const uint4*>(kc_h + (int64_t)j * (D / 2) + 16 * kpart);
+    }
+    if (tid < KV_TILE) {
+      const int jj = kt * KV_TILE + tid;
+      if (NBD == 4) rks = jj < N ? *reinterpret_cast<const unsigned*>(ks_h + (int64_t)jj * 4) : 0x7F7F7F7Fu;
+      else rks = jj < N ? *reinterpret_cast<const unsigned short*>(ks_h + (int64_t)jj * 2) : 0x7F7Fu;
+    }
+    if (has_v) rv = *reinterpret_cast<const uint4*>(vc_h + v_off + (unsigned)kt * 64u);
+    if (tid < D) rvs = *reinterpret_cast<const unsigned*>(vs_h + vs_off + (unsigned)kt * 4u);
+  };
+  prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();
-    {
-      // K codes: 128 rows of D/2 bytes; 16 bytes per thread
-      constexpr int TPK = D / 32;  // threads per key row
-      for (int e = tid; e < KV_TILE * TPK; e += 512) {
-        const int key = e / TPK, part = e % TPK;
-        const int j = kt * KV_TILE + key;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (j < N) u = *reinterpret_cast<const uint4*>(kc + (bh * N + j) * (D / 2) + 16 * part);
-        *reinterpret_cast<uint4*>(sKc + key * KROW + 16 * part) = u;
-      }
-      if (tid < KV_TILE * NBD) {
-        const int key = tid / NBD, b = tid % NBD;
-        const int j = kt * KV_TILE + key;
-        sKs[key * 4 + b] = j < N ? ks[(bh * N + j) * NBD + b] : (uint8_t)127;
-      }
-      // V codes: D rows of 64 bytes (the tile's 128 slots); 16 bytes per thread
-      for (int e = tid; e < D * 4; e += 512) {
-        const int d = e / 4, part = e % 4;
-        *reinterpret_cast<uint4*>(sVc + d * VROW + 16 * part) =
-            *reinterpret_cast<const uint4*>(vc + (bh * D + d) * (Np / 2) + (int64_t)kt * 64 + 16 * part);
-      }
-      if (tid < D) {
-        *reinterpret_cast<unsigned*>(sVs + tid * 4) =
-            *reinterpret_cast<const unsigned*>(vs + (bh * D + tid) * (Np / 32) + (int64_t)kt * 4);
-      }
+    if (has_k) *reinterpret_cast<uint4*>(sKc + kkey * KROW + 16 * kpart) = rk;
+    if (tid < KV_TILE) {
+#pragma unroll
+      for (int b = 0; b < NBD; ++b) sKs[((tid & 15) * 4 + b) * 8 + (tid >> 4)] = (uint8_t)(rks >> (8 * b));
+    }
+    if (has_v) *reinterpret_cast<uint4*>(sVc + vd * VROW + 16 * vpart) = rv;
+    if (tid < D) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sVs[((tid & 15) * 4 + b) * 8 + (tid >> 4)] = (uint8_t)(rvs >> (8 * b));
     }
     __syncthreads();
 
     // ---- S^T = K Q^T: one scaled FP4 MFMA per 16-key subtile (K dimension 128 >= D)
     v4f S[8];
+    uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if (g < NBD) ksw = *reinterpret_cast<const uint2*>(sKs + (c * 4 + g) * 8);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-      int asc = 127;
       if (g < NBD) {
         const uint4 u = *reinterpret_cast<const uint4*>(sKc + (16 * t + c) * KROW + 16 * g);
         a[0] = (int)u.x; a[1] = (int)u.y; a[2] = (int)u.z; a[3] = (int)u.w;
-        asc = sKs[(16 * t + c) * 4 + g];
       }
-      S[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qf, v4f{0, 0, 0, 0}, 4, 4, 0, asc, 0, qsc);
+      // the scale operand's byte t & 3 is selected by the instruction's op_sel bits
+      S[t] = mfma_fp4_sel(a, qf, v4f{0, 0, 0, 0}, t & 3, (int)(t < 4 ? ksw.x : ksw.y), qsc);
     }
     const int kbase = kt * KV_TILE;
     if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
@@ -165,23 +197,26 @@ __global__ __launch_bounds__(512) void attn_mxfp4_kernel(
       pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
     }
     const int psc = keep ? X + 127 : 127;
+    if (kt + 1 < kt_end) prefetch(kt + 1);
     if (!accept) esum = 0.0f;
     const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
     R = accept ? T : R;
     m_u = m_new;
-    if (DIRECT_P) Lacc *= factor;
+    if (DIRECT_P) Lacc[0] *= factor;  // only element 0 is read
     else l = l * factor + esum;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[dt] *= factor;
 
     // ---- O^T += V^T P^T: one scaled FP4 MFMA per 16 channels; lane group g supplies slots
     // 32g .. 32g+31 of V's row 16dt + c and of P's column qi
+    uint2 vsw;
+    if (D == 128) vsw = *reinterpret_cast<const uint2*>(sVs + (c * 4 + g) * 8);
+    else vsw = make_uint2(*reinterpret_cast<const unsigned*>(sVs + (c * 4 + g) * 8), 0u);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const uint4 u = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
       const v8i a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-      const int asc = sVs[(16 * dt + c) * 4 + g];
-      O[dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf, O[dt], 4, 4, 0, asc, 0, psc);
+      O[dt] = mfma_fp4_sel(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
     }
     if (DIRECT_P) {
       // Direct-P normaliser: the sum of the rounded P values, as one more MFMA of P against a
