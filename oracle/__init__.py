@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsage_oracle.so")
 SRC = os.path.join(HERE, "sage_oracle.c")
 
-NVFP4, MXFP4 = 0, 1
+NVFP4, MXFP4, MX4_PV8 = 0, 1, 2  # MX4_PV8: MXFP4 Q/K, MXFP8 (E4M3, 1x32, E8M0) P and V
 ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
 KV_TILE = 128
 
@@ -51,11 +51,14 @@ def lib():
         L.orc_e4m3_encode.argtypes = [F]; L.orc_e4m3_encode.restype = C.c_uint
         L.orc_e2m1_quant.argtypes = [F, F]; L.orc_e2m1_quant.restype = C.c_uint
         L.orc_mx_scale.argtypes = [F]; L.orc_mx_scale.restype = C.c_uint
+        L.orc_mx8_scale.argtypes = [F]; L.orc_mx8_scale.restype = C.c_uint
+        L.orc_e4m3_quant.argtypes = [F, F]; L.orc_e4m3_quant.restype = C.c_uint
         L.orc_slot_token.argtypes = [I]; L.orc_slot_token.restype = I
         L.orc_e4m3_encode_many.argtypes = [P, I64, P]; L.orc_e4m3_encode_many.restype = None
         L.orc_e2m1_quant_many.argtypes = [P, P, I64, P]; L.orc_e2m1_quant_many.restype = None
         L.orc_quant_block_nv.argtypes = [P, I, P, P]; L.orc_quant_block_nv.restype = None
         L.orc_quant_block_mx.argtypes = [P, I, P, P]; L.orc_quant_block_mx.restype = None
+        L.orc_quant_block_mx8.argtypes = [P, I, P, P]; L.orc_quant_block_mx8.restype = None
         L.orc_quant.argtypes = [I, I, P, I, I, I, I, P, P]; L.orc_quant.restype = I
         L.orc_p_tile.argtypes = [I, P, P, P, P, P, P]; L.orc_p_tile.restype = I
         L.orc_attn_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, F, P, I64, P, P, D, I]
@@ -88,7 +91,7 @@ def quant(role: int, fmt: int, x: np.ndarray):
     b = blk(fmt)
     if role == ROLE_V:
         Np = padded_n(N)
-        codes = np.zeros((B, H, D, Np // 2), np.uint8)
+        codes = np.zeros((B, H, D, Np if fmt == MX4_PV8 else Np // 2), np.uint8)
         scales = np.zeros((B, H, D, Np // b), np.uint8)
     else:
         codes = np.zeros((B, H, N, D // 2), np.uint8)
@@ -179,7 +182,7 @@ def quant_block(fmt, x: np.ndarray):
     x = np.ascontiguousarray(x, dtype=np.float32)
     codes = np.zeros(len(x), np.uint8)
     s = np.zeros(1, np.uint8)
-    f = lib().orc_quant_block_nv if fmt == NVFP4 else lib().orc_quant_block_mx
+    f = {NVFP4: lib().orc_quant_block_nv, MXFP4: lib().orc_quant_block_mx, MX4_PV8: lib().orc_quant_block_mx8}[fmt]
     f(_p(x), len(x), _p(codes), _p(s))
     return codes, int(s[0])
 
@@ -200,9 +203,17 @@ def unpack(codes: np.ndarray) -> np.ndarray:
     return np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
 
 
+def e4m3_table() -> np.ndarray:
+    return np.array([lib().orc_e4m3_decode(b) for b in range(256)], np.float32)
+
+
 def dequant(fmt, codes, scales) -> np.ndarray:
-    """Values code*scale (float64) along the last axis."""
-    c = e2m1_table()[unpack(codes)].astype(np.float64)
+    """Values code*scale (float64) along the last axis. With MX4_PV8 the codes are the FP8 bytes
+    of V (or P); its Q and K codes are MXFP4 and dequantise with fmt = MXFP4."""
+    if fmt == MX4_PV8:
+        c = e4m3_table()[codes].astype(np.float64)
+    else:
+        c = e2m1_table()[unpack(codes)].astype(np.float64)
     s = scale_table(fmt)[scales].astype(np.float64)
     return c * np.repeat(s, blk(fmt), axis=-1)
 

@@ -46,6 +46,14 @@
  *     from the same rounded values): MXFP4 codes and scales of P exactly as R9, and the
  *     normaliser sums the dequantised P instead of E: per tile, the block partials
  *     scale * sum(code) in block order.
+ *  R14 FP4 QK with FP8 P and V (the rit.work page on FP4 FlashAttention-4, section on what was
+ *     done: in its distributed training P and V were kept in FP8, since every variant with
+ *     MXFP4 for them diverged). Q and K are MXFP4 as R4. P and V are MXFP8: E4M3 elements in
+ *     blocks of 32 consecutive slots (R5, R6) with one E8M0 scale 2^(floor(log2 amax) - 8)
+ *     per block (the OCP Microscaling rule; 8 is the largest E4M3 exponent), byte 0 for an
+ *     all-zero block; the element is the E4M3 value nearest the exact quotient x / scale,
+ *     ties to the even code, magnitudes above 448 clamp to 448, sign bit the input's. As in
+ *     R9, P2 = E with tile weight beta, and the normaliser sums E (R8).
  *
  * Slack (test aid, not part of the method): a P rounding decision whose input lies within
  * relative delta of its boundary may legitimately go either way in an implementation whose
@@ -144,6 +152,24 @@ unsigned orc_mx_scale(float amax) {
   return (unsigned)(X + 127);
 }
 
+/* R14: E8M0 byte of an MXFP8 block */
+unsigned orc_mx8_scale(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  frexpf(amax, &e);
+  int X = (e - 1) - 8;
+  if (X < -127) X = -127;
+  if (X > 127) X = 127;
+  return (unsigned)(X + 127);
+}
+
+/* R14: E4M3 element of x with power-of-two scale s (x/s is exact in FP32 here) */
+unsigned orc_e4m3_quant(float x, float s) {
+  unsigned sign = signbit(x) ? 0x80u : 0u;
+  if (!(s > 0.0f)) return sign;
+  return sign | orc_e4m3_encode(fabsf(x) / s);
+}
+
 /* R6 */
 int orc_slot_token(int slot) {
   int g = slot / 32, t = (slot % 32) / 4, i = slot % 4;
@@ -169,12 +195,29 @@ void orc_quant_block_mx(const float* x, int n, uint8_t* codes, uint8_t* scale) {
   *scale = (uint8_t)sb;
 }
 
-static int blk_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+void orc_quant_block_mx8(const float* x, int n, uint8_t* codes, uint8_t* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  unsigned sb = orc_mx8_scale(amax);
+  float s = orc_e8m0_decode(sb);
+  for (int i = 0; i < n; ++i) codes[i] = (uint8_t)orc_e4m3_quant(x[i], s);
+  *scale = (uint8_t)sb;
+}
 
+static int valid_fmt(int fmt) { return fmt == ORC_NVFP4 || fmt == ORC_MXFP4 || fmt == ORC_MX4_PV8; }
+static int blk_of(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+static int pv8(int fmt) { return fmt == ORC_MX4_PV8; }
+
+/* block quantiser of P and V (Q and K of the R14 variant are MXFP4) */
 static void quant_block(int fmt, const float* x, int n, uint8_t* codes, uint8_t* scale) {
   if (fmt == ORC_NVFP4) orc_quant_block_nv(x, n, codes, scale);
-  else orc_quant_block_mx(x, n, codes, scale);
+  else if (fmt == ORC_MXFP4) orc_quant_block_mx(x, n, codes, scale);
+  else orc_quant_block_mx8(x, n, codes, scale);
 }
+
+/* value of one P or V element code, and the element quantiser with block scale s */
+static float pv_val(int fmt, unsigned code) { return pv8(fmt) ? orc_e4m3_decode(code) : orc_e2m1_decode(code); }
+static unsigned pv_quant(int fmt, float x, float s) { return pv8(fmt) ? orc_e4m3_quant(x, s) : orc_e2m1_quant(x, s); }
 
 static void put_code(uint8_t* packed, int64_t pos, unsigned code) {
   uint8_t* b = packed + pos / 2;
@@ -187,20 +230,25 @@ static unsigned get_code(const uint8_t* packed, int64_t pos) {
   return (pos % 2 == 0) ? (b & 15u) : (b >> 4);
 }
 
+/* V code at slot position pos of one channel row: a nibble, or a byte in the R14 variant */
+static unsigned get_v_code(int fmt, const uint8_t* row, int64_t pos) { return pv8(fmt) ? row[pos] : get_code(row, pos); }
+static int64_t v_row_bytes(int fmt, int64_t Np) { return pv8(fmt) ? Np : Np / 2; }
+
 int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
               uint8_t* codes, uint8_t* scales) {
   if (!x || !codes || !scales || B <= 0 || H <= 0 || N <= 0) return ORC_ERR_ARG;
   if (D != 64 && D != 128) return ORC_ERR_ARG;
-  if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return ORC_ERR_ARG;
+  if (!valid_fmt(fmt)) return ORC_ERR_ARG;
   const int blk = blk_of(fmt);
   float xb[32];
   uint8_t cb[32], sb;
   if (role == ORC_ROLE_Q || role == ORC_ROLE_K) {
-    /* R5: blocks along D */
+    /* R5: blocks along D; R14: MXFP4 */
+    const int qk_fmt = pv8(fmt) ? ORC_MXFP4 : fmt;
     for (int64_t r = 0; r < (int64_t)B * H * N; ++r) {
       for (int b0 = 0; b0 < D; b0 += blk) {
         for (int u = 0; u < blk; ++u) xb[u] = orc_f16_to_f32(x[r * D + b0 + u]);
-        quant_block(fmt, xb, blk, cb, &sb);
+        quant_block(qk_fmt, xb, blk, cb, &sb);
         for (int u = 0; u < blk; ++u) put_code(codes + r * (D / 2), b0 + u, cb[u]);
         scales[r * (D / blk) + b0 / blk] = sb;
       }
@@ -213,7 +261,7 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
   for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
     const uint16_t* xh = x + bh * N * D;
     for (int d = 0; d < D; ++d) {
-      uint8_t* crow = codes + (bh * D + d) * (Np / 2);
+      uint8_t* crow = codes + (bh * D + d) * v_row_bytes(fmt, Np);
       uint8_t* srow = scales + (bh * D + d) * (Np / blk);
       for (int64_t p0 = 0; p0 < Np; p0 += blk) {
         for (int u = 0; u < blk; ++u) {
@@ -222,7 +270,10 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
           xb[u] = tok < N ? orc_f16_to_f32(xh[tok * D + d]) : 0.0f;
         }
         quant_block(fmt, xb, blk, cb, &sb);
-        for (int u = 0; u < blk; ++u) put_code(crow, p0 + u, cb[u]);
+        for (int u = 0; u < blk; ++u) {
+          if (pv8(fmt)) crow[p0 + u] = cb[u];
+          else put_code(crow, p0 + u, cb[u]);
+        }
         srow[p0 / blk] = sb;
       }
     }
@@ -265,13 +316,14 @@ static double block_ambiguity(int fmt, const float* P2, const uint8_t* codes, un
   for (int k = -1; k <= 1 && !has_exact; k += 2) {
     unsigned alt;
     if (fmt == ORC_NVFP4) alt = orc_e4m3_encode((float)((double)(amax / 6.0f) * (1.0 + k * delta)));
-    else alt = orc_mx_scale((float)((double)amax * (1.0 + k * delta)));
+    else if (fmt == ORC_MXFP4) alt = orc_mx_scale((float)((double)amax * (1.0 + k * delta)));
+    else alt = orc_mx8_scale((float)((double)amax * (1.0 + k * delta)));
     if (alt == sbyte) continue;
     const float s2 = scale_val(fmt, alt);
     double a = 0.0;
     for (int u = 0; u < blk; ++u) {
-      double v1 = (double)orc_e2m1_decode(codes[u]) * s;
-      double v2 = (double)orc_e2m1_decode(orc_e2m1_quant(P2[u], s2)) * s2;
+      double v1 = (double)pv_val(fmt, codes[u]) * s;
+      double v2 = (double)pv_val(fmt, pv_quant(fmt, P2[u], s2)) * s2;
       a += fabs(v2 - v1) * vmax[u];
     }
     if (a > worst_scale) worst_scale = a;
@@ -281,8 +333,8 @@ static double block_ambiguity(int fmt, const float* P2, const uint8_t* codes, un
     if (P2[u] == 0.0f || exact[u]) continue;
     double worst = 0.0;
     for (int k = -1; k <= 1; k += 2) {
-      unsigned c2 = orc_e2m1_quant((float)((double)P2[u] * (1.0 + k * delta)), s);
-      double dv = fabs((double)orc_e2m1_decode(c2) - (double)orc_e2m1_decode(codes[u])) * s;
+      unsigned c2 = pv_quant(fmt, (float)((double)P2[u] * (1.0 + k * delta)), s);
+      double dv = fabs((double)pv_val(fmt, c2) - (double)pv_val(fmt, codes[u])) * s;
       if (dv > worst) worst = dv;
     }
     elem += worst * vmax[u];
@@ -298,7 +350,7 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
                          double* slack, double delta, int nthreads) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out) return ORC_ERR_ARG;
   if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return ORC_ERR_ARG;
-  if (fmt != ORC_NVFP4 && fmt != ORC_MXFP4) return ORC_ERR_ARG;
+  if (!valid_fmt(fmt)) return ORC_ERR_ARG;
   const int64_t total = (int64_t)B * H * N;
   if (!rows) n_rows = total;
   for (int64_t r = 0; rows && r < n_rows; ++r)
@@ -345,7 +397,7 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
             const int k = b * blk + u;
             inner += orc_e2m1_decode(get_code(qc, k)) * orc_e2m1_decode(get_code(kc, k));
           }
-          const float sc = scale_val(fmt, qs[b]) * scale_val(fmt, ks[b]);
+          const float sc = scale_val(fmt, qs[b]) * scale_val(fmt, ks[b]); /* E8M0 for R14 too */
           S += sc * inner;
         }
         x[s] = c * S;
@@ -361,21 +413,21 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
       } else {
         for (int b = 0; b < ORC_KV_TILE / blk; ++b) {                      /* R13 */
           float inner = 0.0f;
-          for (int u = 0; u < blk; ++u) inner += orc_e2m1_decode(pc[b * blk + u]);
+          for (int u = 0; u < blk; ++u) inner += pv_val(fmt, pc[b * blk + u]);
           sumE += scale_val(fmt, ps[b]) * inner;
         }
       }
       l = alpha * l + beta * sumE;
       const float w = beta / Kp;                                          /* R7/R9 */
       for (int d = 0; d < D; ++d) {
-        const uint8_t* vc = v_codes + (bh * D + d) * (Np / 2);
+        const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
         const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
         float acc = 0.0f;
         for (int b = 0; b < ORC_KV_TILE / blk; ++b) {
           float inner = 0.0f;
           for (int u = 0; u < blk; ++u) {
             const int s = b * blk + u;
-            inner += orc_e2m1_decode(pc[s]) * orc_e2m1_decode(get_code(vc, (int64_t)kt * ORC_KV_TILE + s));
+            inner += pv_val(fmt, pc[s]) * pv_val(fmt, get_v_code(fmt, vc, (int64_t)kt * ORC_KV_TILE + s));
           }
           const float sc = scale_val(fmt, ps[b]) * scale_val(fmt, vsc[((int64_t)kt * ORC_KV_TILE) / blk + b]);
           acc += sc * inner;
@@ -389,10 +441,10 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
         double vhead = 0.0;
         if (direct_p) {
           for (int d = 0; d < D; ++d) {
-            const uint8_t* vc = v_codes + (bh * D + d) * (Np / 2);
+            const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
             const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
             for (int64_t p = 0; p < Np; ++p) {
-              double v = fabs((double)orc_e2m1_decode(get_code(vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+              double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
               if (v > vhead) vhead = v;
             }
           }
@@ -402,10 +454,10 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
         for (int s = 0; s < ORC_KV_TILE; ++s) {
           double mv = 0.0;
           for (int d = 0; d < D; ++d) {
-            const uint8_t* vc = v_codes + (bh * D + d) * (Np / 2);
+            const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
             const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
             const int64_t p = (int64_t)kt * ORC_KV_TILE + s;
-            double v = fabs((double)orc_e2m1_decode(get_code(vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+            double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
             if (v > mv) mv = v;
           }
           vmax[s] = mv + vhead;

@@ -31,6 +31,8 @@
  *   V codes              [B,H,D,Np/2]     tokens in slot order inside each 128-token tile
  *   V scales             [B,H,D,Np/16] or [B,H,D,Np/32]
  *   Np = ceil(N/128)*128; token positions >= N are zero.
+ * ORC_MX4_PV8 (FP4 QK, FP8 PV; reading R14 in sage_oracle.c): Q/K codes and scales as MXFP4;
+ *   V codes [B,H,D,Np] one E4M3 byte per element (slot order), V scales [B,H,D,Np/32] E8M0.
  * Slot order inside a 128-token tile: slot s = 32g + 4t + i holds token 16t + 4g + i
  * (g in 0..3, t in 0..7, i in 0..3). Blocks of P and of V are consecutive slots.
  */
@@ -45,7 +47,7 @@ extern "C" {
 
 #define ORC_KV_TILE 128
 
-enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1 };
+enum { ORC_NVFP4 = 0, ORC_MXFP4 = 1, ORC_MX4_PV8 = 2 };
 enum { ORC_ROLE_Q = 0, ORC_ROLE_K = 1, ORC_ROLE_V = 2 };
 enum { ORC_OK = 0, ORC_ERR_ARG = -1 };
 
@@ -57,6 +59,8 @@ float orc_e8m0_decode(unsigned byte);            /* 2^(byte-127); 0xFF = NaN */
 unsigned orc_e4m3_encode(float y);               /* y >= 0 finite: nearest E4M3, ties to even, clamp 448 */
 unsigned orc_e2m1_quant(float x, float s);       /* nearest E2M1 to the exact x/s, ties to even, clamp 6 */
 unsigned orc_mx_scale(float amax);               /* E8M0 byte: floor(log2 amax) - 2, clamped; 0 if amax == 0 */
+unsigned orc_mx8_scale(float amax);              /* E8M0 byte: floor(log2 amax) - 8, clamped; 0 if amax == 0 */
+unsigned orc_e4m3_quant(float x, float s);       /* sign | nearest E4M3 to |x|/s (s a power of two), ties even, clamp 448 */
 int orc_slot_token(int slot);                    /* token offset held by slot (0..127) */
 /* bulk forms of the two encoders (loops over the scalar functions above) */
 void orc_e4m3_encode_many(const float* y, int64_t n, uint8_t* out);
@@ -65,6 +69,7 @@ void orc_e2m1_quant_many(const float* x, const float* s, int64_t n, uint8_t* out
 /* ---- block quantisers: n values -> n codes (one per byte, low nibble) + one scale byte ---- */
 void orc_quant_block_nv(const float* x, int n, uint8_t* codes, uint8_t* scale);
 void orc_quant_block_mx(const float* x, int n, uint8_t* codes, uint8_t* scale);
+void orc_quant_block_mx8(const float* x, int n, uint8_t* codes, uint8_t* scale); /* E4M3 codes, one per byte */
 
 /* ---- tensor quantiser (fp16 input bits). Returns ORC_OK or ORC_ERR_ARG. ---- */
 int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
