@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP4 attention fwd TOPS (4·B·H·N²·D/t) + %FP4-MFMA peak; cos-sim vs FP32"
 FP4_PEAK_TOPS = 10066.0      # MI355X dense FP4 MFMA (256 CU x 4 SIMD x 4096 flop/clk x 2.4 GHz)
+FP8_PEAK_TOPS = 5033.0       # MI355X dense FP8 MFMA (half the FP4 rate)
 FP16_PEAK_TFLOPS = 2516.6    # dense fp16 MFMA
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(B=4, H=32, N=4096, D=128)
@@ -228,7 +229,9 @@ def main():
                                  ("mxfp4_noncausal", bnd.MXFP4, False, False),
                                  ("mxfp4_causal", bnd.MXFP4, True, False),
                                  ("mxfp4_direct_p_noncausal", bnd.MXFP4, False, True),
-                                 ("mxfp4_direct_p_causal", bnd.MXFP4, True, True)):
+                                 ("mxfp4_direct_p_causal", bnd.MXFP4, True, True),
+                                 ("mx4_pv8_noncausal", bnd.MX4_PV8, False, False),
+                                 ("mx4_pv8_causal", bnd.MX4_PV8, True, False)):
             if f2 == fmt and c2 == causal and not dp:
                 continue
             Q2 = bnd.quant(q, bnd.ROLE_Q, f2); K2 = bnd.quant(k, bnd.ROLE_K, f2); V2 = bnd.quant(v, bnd.ROLE_V, f2)
@@ -244,6 +247,9 @@ def main():
             fl = flops_formula / 2 if c2 else flops_formula
             t = fl / (ms * 1e-3) / 1e12
             extras[name] = {"attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS}
+            if f2 == bnd.MX4_PV8:  # half the flops at the FP4 rate (QK), half at the FP8 rate (PV)
+                mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)
+                extras[name]["frac_fp4_fp8_mixed_peak"] = t / mixed
         res["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsage_fp4.so")
 
-NVFP4, MXFP4 = 0, 1
+NVFP4, MXFP4, MX4_PV8 = 0, 1, 2
 ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
 STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR_HEAD_DIM",

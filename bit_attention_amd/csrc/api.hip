@@ -9,12 +9,15 @@
 namespace sage {
 hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* codes, void* scales, hipStream_t st);
 hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
+hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                              void* out, bool out_f32, hipStream_t st);
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                              void* out, bool out_f32, hipStream_t st);
 hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
                                       float sm_scale, void* out, bool out_f32, hipStream_t st);
+hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                               void* out, bool out_f32, hipStream_t st);
 }  // namespace sage
 
 namespace {
@@ -23,6 +26,8 @@ constexpr int kMaxN = 1 << 20;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_fmt(int fmt) { return fmt == SAGE_FMT_NVFP4 || fmt == SAGE_FMT_MXFP4 || fmt == SAGE_FMT_MX4_PV8; }
 
 int check_shape(int B, int H, int N, int D) {
   if (D != 64 && D != 128) return SAGE_ERR_HEAD_DIM;
@@ -37,21 +42,21 @@ int64_t padded(int N) { return ((int64_t)N + sage::KV_TILE - 1) / sage::KV_TILE 
 
 extern "C" {
 
-int sage_fp4_version(void) { return 200; }
+int sage_fp4_version(void) { return 300; }
 
 int sage_fp4_kv_tile(void) { return sage::KV_TILE; }
 
 int sage_fp4_slot_token(int slot) { return (slot < 0 || slot >= sage::KV_TILE) ? -1 : sage::slot_token(slot); }
 
 size_t sage_fp4_codes_bytes(int role, int fmt, int B, int H, int N, int D) {
-  if (check_shape(B, H, N, D) != SAGE_OK || (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4)) return 0;
+  if (check_shape(B, H, N, D) != SAGE_OK || !valid_fmt(fmt)) return 0;
   if (role == SAGE_ROLE_Q || role == SAGE_ROLE_K) return (size_t)B * H * N * (D / 2);
-  if (role == SAGE_ROLE_V) return (size_t)B * H * D * (padded(N) / 2);
+  if (role == SAGE_ROLE_V) return (size_t)B * H * D * (fmt == SAGE_FMT_MX4_PV8 ? padded(N) : padded(N) / 2);
   return 0;
 }
 
 size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D) {
-  if (check_shape(B, H, N, D) != SAGE_OK || (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4)) return 0;
+  if (check_shape(B, H, N, D) != SAGE_OK || !valid_fmt(fmt)) return 0;
   const int blk = fmt == SAGE_FMT_NVFP4 ? 16 : 32;
   if (role == SAGE_ROLE_Q || role == SAGE_ROLE_K) return (size_t)B * H * N * (D / blk);
   if (role == SAGE_ROLE_V) return (size_t)B * H * D * (padded(N) / blk);
@@ -61,15 +66,16 @@ size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D) {
 int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D, void* codes, void* scales,
                    void* stream) {
   if (role != SAGE_ROLE_Q && role != SAGE_ROLE_K && role != SAGE_ROLE_V) return SAGE_ERR_ENUM;
-  if (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4) return SAGE_ERR_ENUM;
+  if (!valid_fmt(fmt)) return SAGE_ERR_ENUM;
   if (!x || !codes || !scales) return SAGE_ERR_NULL;
   const int sh = check_shape(B, H, N, D);
   if (sh != SAGE_OK) return sh;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SAGE_ERR_ALIGN;
-  const bool mx = fmt == SAGE_FMT_MXFP4;
+  const bool mx = fmt != SAGE_FMT_NVFP4;  // Q and K of the FP8-PV format are MXFP4
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (role == SAGE_ROLE_V) e = sage::launch_quant_v(mx, x, B * H, N, D, codes, scales, st);
+  if (role == SAGE_ROLE_V && fmt == SAGE_FMT_MX4_PV8) e = sage::launch_quant_v8(x, B * H, N, D, codes, scales, st);
+  else if (role == SAGE_ROLE_V) e = sage::launch_quant_v(mx, x, B * H, N, D, codes, scales, st);
   else e = sage::launch_quant_rows(mx, x, (int64_t)B * H * N, D, codes, scales, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
@@ -95,15 +101,16 @@ static float scale_or_default(float sm_scale, int D) {
 int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                       const void* k_scales, const void* v_codes, const void* v_scales, int B, int H, int N,
                       int D, int causal, float sm_scale, void* out, int out_dtype, void* stream) {
-  if (fmt != SAGE_FMT_NVFP4 && fmt != SAGE_FMT_MXFP4) return SAGE_ERR_ENUM;
+  if (!valid_fmt(fmt)) return SAGE_ERR_ENUM;
   const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
   const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
   if (chk != SAGE_OK) return chk;
   const float c = scale_or_default(sm_scale, D);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = fmt == SAGE_FMT_NVFP4
-                           ? sage::launch_attn_nvfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st)
-                           : sage::launch_attn_mxfp4(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st);
+  const bool f32 = out_dtype == SAGE_OUT_F32, cz = causal != 0;
+  const hipError_t e = fmt == SAGE_FMT_NVFP4   ? sage::launch_attn_nvfp4(ptrs, B * H, N, D, cz, c, out, f32, st)
+                       : fmt == SAGE_FMT_MXFP4 ? sage::launch_attn_mxfp4(ptrs, B * H, N, D, cz, c, out, f32, st)
+                                               : sage::launch_attn_mx4_pv8(ptrs, B * H, N, D, cz, c, out, f32, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

@@ -38,29 +38,67 @@ __device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
   return w;
 }
 
-// FP4 x FP4 block-scaled MFMA whose A scale is byte `sel` of `sa` (the instruction's op_sel bits
-// pick the byte; `sel` is a constant after unrolling, so the switch folds away).
-__device__ __forceinline__ v4f mfma_fp4_sel(const v8i& a, const v8i& b, const v4f& c, int sel, int sa, int sb) {
+// Block-scaled MFMA (operand format F: 4 = FP4 E2M1, 0 = FP8 E4M3, the same for A and B) whose A
+// scale is byte `sel` of `sa` (the instruction's op_sel bits pick the byte; `sel` is a constant
+// after unrolling, so the switch folds away).
+template <int F>
+__device__ __forceinline__ v4f mfma_sel(const v8i& a, const v8i& b, const v4f& c, int sel, int sa, int sb) {
   switch (sel) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 1, sa, 0, sb);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 2, sa, 0, sb);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 3, sa, 0, sb);
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F, F, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F, F, 1, sa, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F, F, 2, sa, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F, F, 3, sa, 0, sb);
   }
+}
+
+// Four FP32 values -> four E4M3 bytes of v / 2^floor(log2 scale), round to nearest even (the
+// callers keep every quotient within +-448).
+__device__ __forceinline__ unsigned pack_e4m3(float v0, float v1, float v2, float v3, float scale) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v0, v1, scale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v2, v3, scale, true);
+  return (unsigned)(unsigned short)w[0] | ((unsigned)(unsigned short)w[1] << 16);
 }
 
 __device__ __forceinline__ float exp2_01(float x) {
   return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.0f, 1.0f);
 }
 
-template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P>
+// PV8: P and V in MXFP8 (E4M3 elements, E8M0 scale per 32 slots) instead of MXFP4; the PV
+// products then run at the FP8 rate. DIRECT_P (MXFP4 only): the normaliser sums the rounded P.
+//
+// FP8 operand layout (measured on gfx950): in v_mfma_scale_f32_16x16x128_f8f6f4 with FP8
+// operands, lane group g (lanes 16g .. 16g+15) holds K-indices 16g .. 16g+15 in its first four
+// VGPRs and 64+16g .. 64+16g+15 in the last four, while the scale of K-block b (indices 32b ..
+// 32b+31) still comes from lane group b. So a lane's 32 P values are not one block: its first
+// half shares block g/2 with the partner group g^1, its second half block 2 + g/2. To make the
+// S^T layout deliver exactly those slots, the PV8 instance stores the K tile in LDS under a
+// row permutation rho (a bit permutation of the key index) and reads subtile rows as before:
+// lane group g of subtile t then holds slots 16g + 4t + i (t < 4) and 64 + 16g + 4(t-4) + i
+// (t >= 4), i.e. P's B-operand bytes in place, and the block maxima need one exchange with
+// the partner group.
+__host__ __device__ constexpr int pv8_rho(int key) {
+  return (key & 0x33) | (((key >> 3) & 1) << 6) | (((key >> 2) & 1) << 3) | (((key >> 6) & 1) << 2);
+}
+
+// The lane's partner value after a permlane swap of `mine` (the pair holds both, in an order
+// that depends on the lane; equal values make either choice right).
+__device__ __forceinline__ unsigned partner_of(unsigned mine, unsigned p0, unsigned p1) {
+  return p0 == mine ? p1 : p0;
+}
+template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P, bool PV8>
 __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
-  constexpr int KROW = D / 2 + 16;   // K code row pitch (bytes)
-  constexpr int VROW = 64 + 16;      // V code row pitch (bytes): 128 slots
-  constexpr int NBD = D / 32;        // MXFP4 blocks along D
+  static_assert(!(PV8 && DIRECT_P), "Direct-P is defined for MXFP4 P");
+  constexpr int KROW = D / 2 + 16;        // K code row pitch (bytes)
+  constexpr int VB = PV8 ? 128 : 64;      // V code bytes per channel and tile (128 slots)
+  constexpr int VROW = VB + 16;           // V code row pitch (bytes)
+  constexpr int VPIECES = D * VB / 16;    // 16-byte pieces of a V tile
+  constexpr int VPT = (VPIECES + 511) / 512;  // pieces per thread
+  constexpr int NBD = D / 32;             // MXFP4 blocks along D
   __shared__ __attribute__((aligned(16))) uint8_t sKc[KV_TILE * KROW];
   // scale bytes, laid out so that lane (g, c) finds its eight per tile in one 8-byte word:
   // K: byte (4c + g) * 8 + t holds key 16t + c's block g; V: byte (4c + g) * 8 + dt holds
@@ -101,15 +139,19 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
   // loaded into registers once the current tile's scores are consumed, so the loads are in
   // flight during the PV products and the barrier.
   constexpr int TPK = D / 32;  // 16-byte pieces per key row
-  const bool has_k = tid < KV_TILE * TPK, has_v = tid < D * 4;
-  const int kkey = tid / TPK, kpart = tid % TPK, vd = tid >> 2, vpart = tid & 3;
+  constexpr int VPR = VB / 16;  // 16-byte pieces per V channel row
+  const bool has_k = tid < KV_TILE * TPK;
+  const int kkey = tid / TPK, kpart = tid % TPK;
   const uint8_t* kc_h = kc + bh * N * (D / 2);
   const uint8_t* ks_h = ks + bh * N * NBD;
-  const uint8_t* vc_h = vc + bh * D * (Np / 2);   // uniform base; per-thread offsets below are 32-bit
+  const int64_t vrow_bytes = PV8 ? Np : Np / 2;
+  const uint8_t* vc_h = vc + bh * D * vrow_bytes;   // uniform base; per-thread offsets are 32-bit
   const uint8_t* vs_h = vs + bh * D * (Np / 32);
-  const unsigned v_off = (unsigned)(vd * (Np / 2) + 16 * vpart), vs_off = (unsigned)(tid * (Np / 32));
-  uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
+  const unsigned vs_off = (unsigned)(tid * (Np / 32));
+  uint4 rk = make_uint4(0, 0, 0, 0), rv[VPT];
   unsigned rks = 0, rvs = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) rv[i] = make_uint4(0, 0, 0, 0);
   auto prefetch = [&](int kt) {
     const int j = kt * KV_TILE + kkey;
     if (has_k) {
@@ -121,18 +163,29 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
       if (NBD == 4) rks = jj < N ? *reinterpret_cast<const unsigned*>(ks_h + (int64_t)jj * 4) : 0x7F7F7F7Fu;
       else rks = jj < N ? *reinterpret_cast<const unsigned short*>(ks_h + (int64_t)jj * 2) : 0x7F7Fu;
     }
-    if (has_v) rv = *reinterpret_cast<const uint4*>(vc_h + v_off + (unsigned)kt * 64u);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = tid + 512 * i;
+      if (e < VPIECES)
+        rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)((e / VPR) * vrow_bytes + 16 * (e % VPR)) +
+                                                (unsigned)kt * (unsigned)VB);
+    }
     if (tid < D) rvs = *reinterpret_cast<const unsigned*>(vs_h + vs_off + (unsigned)kt * 4u);
   };
   prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();
-    if (has_k) *reinterpret_cast<uint4*>(sKc + kkey * KROW + 16 * kpart) = rk;
+    if (has_k) *reinterpret_cast<uint4*>(sKc + (PV8 ? pv8_rho(kkey) : kkey) * KROW + 16 * kpart) = rk;
     if (tid < KV_TILE) {
+      const int r = PV8 ? pv8_rho(tid) : tid;  // LDS row of this key
 #pragma unroll
-      for (int b = 0; b < NBD; ++b) sKs[((tid & 15) * 4 + b) * 8 + (tid >> 4)] = (uint8_t)(rks >> (8 * b));
+      for (int b = 0; b < NBD; ++b) sKs[((r & 15) * 4 + b) * 8 + (r >> 4)] = (uint8_t)(rks >> (8 * b));
     }
-    if (has_v) *reinterpret_cast<uint4*>(sVc + vd * VROW + 16 * vpart) = rv;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = tid + 512 * i;
+      if (e < VPIECES) *reinterpret_cast<uint4*>(sVc + (e / VPR) * VROW + 16 * (e % VPR)) = rv[i];
+    }
     if (tid < D) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) sVs[((tid & 15) * 4 + b) * 8 + (tid >> 4)] = (uint8_t)(rvs >> (8 * b));
@@ -151,7 +204,7 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
         a[0] = (int)u.x; a[1] = (int)u.y; a[2] = (int)u.z; a[3] = (int)u.w;
       }
       // the scale operand's byte t & 3 is selected by the instruction's op_sel bits
-      S[t] = mfma_fp4_sel(a, qf, v4f{0, 0, 0, 0}, t & 3, (int)(t < 4 ? ksw.x : ksw.y), qsc);
+      S[t] = mfma_sel<4>(a, qf, v4f{0, 0, 0, 0}, t & 3, (int)(t < 4 ? ksw.x : ksw.y), qsc);
     }
     const int kbase = kt * KV_TILE;
     if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
@@ -159,15 +212,29 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
       for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = kbase + 16 * t + 4 * g + i;
+          const int j = kbase + (PV8 ? 64 * (g & 1) + 16 * (t & 3) + 8 * (t >> 2) + 4 * (g >> 1) + i
+                                     : 16 * t + 4 * g + i);
           if (j >= N || (CAUSAL && j > qi)) S[t][i] = -INFINITY;
         }
     }
     // ---- online softmax in log2 units
-    float bmx = -INFINITY;  // the lane's block maximum of S
+    // bmx: the maximum of S over the lane's P block (PV8: over the block of its first half,
+    // which it shares with the partner group g^1; bmB: the same for the second half)
+    float bmx = -INFINITY, bmB = -INFINITY, tS;
+    if (PV8) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) bmx = fmaxf(bmx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
-    const float tS = xg_max(bmx);
+      for (int t = 0; t < 4; ++t) {
+        bmx = max3f(bmx, fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3]));
+        bmB = max3f(bmB, fmaxf(S[t + 4][0], S[t + 4][1]), fmaxf(S[t + 4][2], S[t + 4][3]));
+      }
+      bmx = pair16_max(bmx);
+      bmB = pair16_max(bmB);
+      tS = pair32_max(fmaxf(bmx, bmB));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bmx = fmaxf(bmx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
+      tS = xg_max(bmx);
+    }
     const bool vis = tS > -INFINITY;
     float T = 0.0f;  // tile maximum in log2 units, rounded toward -infinity
     if (vis) {
@@ -178,25 +245,56 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
     const float m_new = fmaxf(m_u, T);
     const bool accept = vis && (T >= m_new - 64.0f);
 
-    // the lane's block: E8M0 scale 2^(floor(log2 amax) - 2), amax = the block maximum of E;
-    // then E chunk by chunk, summed and packed at once
+    // the lane's block: E8M0 scale 2^(floor(log2 amax) - EMAX), amax = the block maximum of E
+    // (EMAX = 2 for E2M1, 8 for E4M3); then E chunk by chunk, summed and packed at once
+    constexpr int EMAX = PV8 ? 8 : 2;
+    constexpr float AMIN = PV8 ? 0x1p-118f : 0x1p-124f;  // below: X < -126, the block is dropped
     const float amax = exp2_01(__builtin_fmaf(bmx, k2, -T));
-    const int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - 2;  // amax is 0 or normal for X >= -126
-    const bool keep = accept && amax >= 0x1p-124f;
+    const int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - EMAX;  // amax is 0 or normal here
+    const bool keep = accept && amax >= AMIN;
     const float sc = as_f((unsigned)max(X + 127, 1) << 23);
     float esum = 0.0f;
     v8i pf = {0, 0, 0, 0, 0, 0, 0, 0};
+    int psc;
+    if (PV8) {
+      const float amaxB = exp2_01(__builtin_fmaf(bmB, k2, -T));
+      const int XB = (int)((as_u(amaxB) >> 23) & 0xFF) - 127 - EMAX;
+      const bool keepB = accept && amaxB >= AMIN;
+      const float scB = as_f((unsigned)max(XB + 127, 1) << 23);
+      // E4M3 saturates at 448: quotients E / 2^X in [448, 512) clamp to 448
+      const float cap = 448.0f * sc, capB = 448.0f * scB;
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      float E[8];
+      for (int wd = 0; wd < 8; ++wd) {
+        float E[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        E[e] = exp2_01(__builtin_fmaf(S[2 * wd + (e >> 2)][e & 3], k2, -T));
-        if (!DIRECT_P) esum += E[e];
+        for (int i = 0; i < 4; ++i) {
+          E[i] = exp2_01(__builtin_fmaf(S[wd][i], k2, -T));
+          esum += E[i];
+          E[i] = fminf(E[i], wd < 4 ? cap : capB);
+        }
+        const bool kp = wd < 4 ? keep : keepB;
+        pf[wd] = kp ? (int)pack_e4m3(E[0], E[1], E[2], E[3], wd < 4 ? sc : scB) : 0;
       }
-      pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
+      // the B operand's scale of K-block g: block 0 (1) is the first half of groups 0, 1 (2, 3),
+      // block 2 (3) the second half; groups 1 and 2 take it from their partner across 32 lanes
+      const int sA = keep ? X + 127 : 127, sB = keepB ? XB + 127 : 127;
+      const unsigned send = (unsigned)(g < 2 ? sB : sA);
+      const auto pr = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+      const int recv = (int)partner_of(send, pr[0], pr[1]);
+      psc = g == 0 ? sA : (g == 3 ? sB : recv);
+    } else {
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        float E[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          E[e] = exp2_01(__builtin_fmaf(S[2 * wd + (e >> 2)][e & 3], k2, -T));
+          if (!DIRECT_P) esum += E[e];
+        }
+        pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
+      }
+      psc = keep ? X + 127 : 127;
     }
-    const int psc = keep ? X + 127 : 127;
     if (kt + 1 < kt_end) prefetch(kt + 1);
     if (!accept) esum = 0.0f;
     const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
@@ -207,16 +305,24 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[dt] *= factor;
 
-    // ---- O^T += V^T P^T: one scaled FP4 MFMA per 16 channels; lane group g supplies slots
-    // 32g .. 32g+31 of V's row 16dt + c and of P's column qi
+    // ---- O^T += V^T P^T: one scaled FP4 (FP8) MFMA per 16 channels; lane group g supplies
+    // slots 32g .. 32g+31 (FP8: 16g .. 16g+15 and 64+16g .. 64+16g+15) of V's row 16dt + c and
+    // of P's column qi
     uint2 vsw;
     if (D == 128) vsw = *reinterpret_cast<const uint2*>(sVs + (c * 4 + g) * 8);
     else vsw = make_uint2(*reinterpret_cast<const unsigned*>(sVs + (c * 4 + g) * 8), 0u);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const uint4 u = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
-      const v8i a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-      O[dt] = mfma_fp4_sel(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
+      if (PV8) {
+        const uint4 u0 = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
+        const uint4 u1 = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 64 + 16 * g);
+        const v8i a = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        O[dt] = mfma_sel<0>(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
+        const v8i a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        O[dt] = mfma_sel<4>(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
+      }
     }
     if (DIRECT_P) {
       // Direct-P normaliser: the sum of the rounded P values, as one more MFMA of P against a
@@ -245,21 +351,21 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool F32, bool DP>
+template <int D, bool CAUSAL, bool F32, bool DP, bool PV8>
 static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + MX_BQ - 1) / MX_BQ;
-  attn_mxfp4_kernel<D, CAUSAL, F32, DP><<<dim3(nqt * BH), dim3(512), 0, st>>>(
+  attn_mxfp4_kernel<D, CAUSAL, F32, DP, PV8><<<dim3(nqt * BH), dim3(512), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
       (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, k2, out);
 }
 
-template <bool DP>
+template <bool DP, bool PV8>
 static hipError_t launch_mx_any(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                                 void* out, bool out_f32, hipStream_t st) {
   const float k2 = sm_scale * 1.4426950408889634f;
 #define SAGE_MX_CASE(DD, CC, FF) \
-  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF, DP>(ptrs, BH, N, k2, out, st);
+  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF, DP, PV8>(ptrs, BH, N, k2, out, st);
   SAGE_MX_CASE(64, false, false) SAGE_MX_CASE(64, false, true) SAGE_MX_CASE(64, true, false)
   SAGE_MX_CASE(64, true, true) SAGE_MX_CASE(128, false, false) SAGE_MX_CASE(128, false, true)
   SAGE_MX_CASE(128, true, false) SAGE_MX_CASE(128, true, true)
@@ -269,12 +375,17 @@ static hipError_t launch_mx_any(const void* const* ptrs, int BH, int N, int D, b
 
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                              void* out, bool out_f32, hipStream_t st) {
-  return launch_mx_any<false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+  return launch_mx_any<false, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
 }
 
 hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
                                       float sm_scale, void* out, bool out_f32, hipStream_t st) {
-  return launch_mx_any<true>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+  return launch_mx_any<true, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+}
+
+hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
+                               void* out, bool out_f32, hipStream_t st) {
+  return launch_mx_any<false, true>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
 }
 
 }  // namespace sage

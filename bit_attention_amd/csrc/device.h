@@ -61,13 +61,17 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// Max over the four lanes {l, l^16, l^32, l^48} that share a column of a 16x16 MFMA tile.
-__device__ __forceinline__ float xg_max(float v) {
+// Max over the lane pair {l, l^16}, over {l, l^32}, and over the four lanes {l, l^16, l^32,
+// l^48} that share a column of a 16x16 MFMA tile.
+__device__ __forceinline__ float pair16_max(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
-  v = fmaxf(as_f(p[0]), as_f(p[1]));
+  return fmaxf(as_f(p[0]), as_f(p[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
   return fmaxf(as_f(r[0]), as_f(r[1]));
 }
+__device__ __forceinline__ float xg_max(float v) { return pair32_max(pair16_max(v)); }
 __device__ __forceinline__ float xg_sum(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
   v = as_f(p[0]) + as_f(p[1]);

@@ -1,5 +1,6 @@
 // quant.hip — FP4 microscaling quantisation kernels (Q, K along D; V along tokens in slot
-// order), NVFP4 (1x16, E4M3 scale) and MXFP4 (1x32, E8M0 scale).
+// order), NVFP4 (1x16, E4M3 scale) and MXFP4 (1x32, E8M0 scale); and MXFP8 V (E4M3 elements,
+// 1x32, E8M0 scale) for the variant with FP8 P and V.
 //
 // SageAttention3 (arXiv 2505.11594), DeepTech article: both matmuls of attention take FP4
 // operands quantised in 1x16 groups (section on the two FP4 obstacles); NVFP4 is E2M1 with an
@@ -64,6 +65,15 @@ __device__ __forceinline__ unsigned mx_scale(float amax, float* s) {
   int X = fl - 2;
   X = X < -127 ? -127 : (X > 127 ? 127 : X);
   *s = X >= -126 ? as_f((unsigned)(X + 127) << 23) : as_f(1u << (X + 149));  // 2^X, exact
+  return (unsigned)(X + 127);
+}
+
+// MXFP8 scale byte: the OCP rule 2^(floor(log2 amax) - 8) (8 = the largest E4M3 exponent);
+// byte 0 and s = 0 for amax == 0. amax is an fp16 magnitude here, so 2^X is a normal float.
+__device__ __forceinline__ unsigned mx8_scale(float amax, float* s) {
+  if (!(amax > 0.0f)) { *s = 0.0f; return 0u; }
+  const int X = (int)((as_u(amax) >> 23) & 0xFF) - 127 - 8;
+  *s = as_f((unsigned)(X + 127) << 23);
   return (unsigned)(X + 127);
 }
 
@@ -148,6 +158,55 @@ __global__ __launch_bounds__(256) void quant_v_lds_kernel(const __half* __restri
   }
 }
 
+// V, MXFP8: the workgroup layout of quant_v_lds_kernel; each (channel, block) item writes its 32
+// E4M3 bytes. The quotient x / 2^X is exact (a power-of-two scale); quotients beyond +-448 clamp
+// to +-448 before the hardware's round-to-nearest-even conversion; the sign is the input's.
+template <int D>
+__global__ __launch_bounds__(256) void quant_v8_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int N, int64_t Np) {
+  constexpr int PITCH = D + 2;
+  constexpr int BLK = 32, NB = KV_TILE / BLK;
+  __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
+  const int kt = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tok0 = kt * KV_TILE;
+  const __half* xs = x + (bh * N + tok0) * (int64_t)D;
+  const int ntok = min(KV_TILE, N - tok0);
+  for (int e = threadIdx.x; e < KV_TILE * D / 2; e += blockDim.x) {
+    const int tok = e / (D / 2), c2 = e % (D / 2);
+    unsigned u = 0;
+    if (tok < ntok) u = reinterpret_cast<const unsigned*>(xs)[(int64_t)tok * (D / 2) + c2];
+    *reinterpret_cast<unsigned*>(&tile[tok * PITCH + 2 * c2]) = u;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
+    const int d = it / NB, blk = it % NB;
+    float v[BLK];
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) v[u] = (float)tile[slot_token(blk * BLK + u) * PITCH + d];
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
+    float s;
+    const unsigned sb = mx8_scale(amax, &s);
+    const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
+    unsigned words[BLK / 4];
+#pragma unroll
+    for (int w = 0; w < BLK / 4; ++w) {
+      float q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+      words[w] = (unsigned)word;
+    }
+    uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * Np + (int64_t)kt * KV_TILE + blk * BLK);
+    crow[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    crow[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    scales[(bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk] = (uint8_t)sb;
+  }
+}
+
 // V, NVFP4: one wave per (batch*head, pair of 128-token tiles). Each lane owns a channel pair; with
 // D = 128 the 64 lanes cover all channels and walk the two tiles in turn, with D = 64 each half
 // of the wave takes one tile. A token's channels are read by the lanes of that tile together
@@ -225,6 +284,14 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
   const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
   if (mx) quant_rows_kernel<32, true><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, nblocks);
   else quant_rows_kernel<16, false><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
+  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
+  const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
+  if (D == 64) quant_v8_kernel<64><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
+  else quant_v8_kernel<128><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
   return hipGetLastError();
 }
 

@@ -9,6 +9,13 @@
  * microscaling), and P V is computed from FP4 operands with FP32 accumulation. Two formats:
  *   NVFP4: E2M1 codes, blocks of 16, one E4M3 scale per block (the pages' choice);
  *   MXFP4: E2M1 codes, blocks of 32, one E8M0 scale per block (the pages' comparison format).
+ * A third format keeps P and V in FP8 (the rit.work page on FP4 FlashAttention-4, section on
+ * what was done: its training had to leave P and V in FP8 because MXFP4 variants for them
+ * diverged):
+ *   MX4_PV8: Q and K as MXFP4; P and V as MXFP8, i.e. E4M3 elements in blocks of 32 with one
+ *   E8M0 scale 2^(floor(log2 amax) - 8) per block; an element is the E4M3 value nearest the
+ *   exact quotient x/scale, ties to even, clamped to +-448, sign bit the input's. The
+ *   normaliser sums the unquantised E, as for the FP4 formats.
  *
  * Numerics (the contract the CPU oracle in oracle/ implements independently):
  *   - NVFP4 block scale: E4M3 of fl32(amax/6), round to nearest even, clamped to 448.
@@ -45,7 +52,7 @@
 extern "C" {
 #endif
 
-typedef enum { SAGE_FMT_NVFP4 = 0, SAGE_FMT_MXFP4 = 1 } sage_fmt_t;
+typedef enum { SAGE_FMT_NVFP4 = 0, SAGE_FMT_MXFP4 = 1, SAGE_FMT_MX4_PV8 = 2 } sage_fmt_t;
 typedef enum { SAGE_ROLE_Q = 0, SAGE_ROLE_K = 1, SAGE_ROLE_V = 2 } sage_role_t;
 typedef enum { SAGE_OUT_F16 = 0, SAGE_OUT_F32 = 1 } sage_out_t;
 typedef enum {
@@ -70,7 +77,8 @@ int sage_fp4_slot_token(int slot);
 
 /* Bytes needed for the codes / scales of one quantised tensor (0 for invalid arguments).
  *   Q, K: codes [B,H,N,D/2], scales [B,H,N,D/16] (NVFP4) or [B,H,N,D/32] (MXFP4);
- *   V:    codes [B,H,D,Np/2], scales [B,H,D,Np/16] or [B,H,D,Np/32], Np = ceil(N/128)*128. */
+ *   V:    codes [B,H,D,Np/2], scales [B,H,D,Np/16] or [B,H,D,Np/32], Np = ceil(N/128)*128;
+ *         MX4_PV8: codes [B,H,D,Np] (one E4M3 byte per element), scales [B,H,D,Np/32]. */
 size_t sage_fp4_codes_bytes(int role, int fmt, int B, int H, int N, int D);
 size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D);
 
@@ -78,7 +86,8 @@ size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D);
  * Q and K: blocks of 16 (32) consecutive channels of each token; codes [B,H,N,D/2] with
  * element 2i in the low nibble of byte i; scales one byte per block.
  * V: blocks along tokens. codes [B,H,D,Np/2] hold, for each channel d, the tokens of each
- * 128-token tile in slot order (two per byte, low nibble first); token positions >= N hold 0.
+ * 128-token tile in slot order (two per byte, low nibble first; MX4_PV8: one byte each);
+ * token positions >= N hold 0. With MX4_PV8, Q and K are quantised exactly as with MXFP4.
  * scales [B,H,D,Np/blk]. One kernel launch. Inputs must be finite. */
 int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D,
                    void* codes, void* scales, void* stream);

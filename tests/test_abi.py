@@ -34,19 +34,19 @@ def test_library_exports_every_declared_symbol():
 
 def test_constants_and_slot_order():
     assert bnd.sage_fp4_kv_tile() == 128
-    assert bnd.sage_fp4_version() >= 100
+    assert bnd.sage_fp4_version() >= 300
     order = [bnd.sage_fp4_slot_token(s) for s in range(128)]
     assert sorted(order) == list(range(128))
     assert order[:8] == [0, 1, 2, 3, 16, 17, 18, 19]
     assert order[32] == 4 and bnd.sage_fp4_slot_token(128) == -1 and bnd.sage_fp4_slot_token(-1) == -1
 
 
-@pytest.mark.parametrize("fmt,blk", [(0, 16), (1, 32)])
+@pytest.mark.parametrize("fmt,blk", [(0, 16), (1, 32), (2, 32)])
 def test_size_helpers(fmt, blk):
     B, H, N, D = 2, 3, 300, 128
     assert bnd.sage_fp4_codes_bytes(0, fmt, B, H, N, D) == B * H * N * D // 2
     assert bnd.sage_fp4_scales_bytes(1, fmt, B, H, N, D) == B * H * N * D // blk
-    assert bnd.sage_fp4_codes_bytes(2, fmt, B, H, N, D) == B * H * D * 384 // 2
+    assert bnd.sage_fp4_codes_bytes(2, fmt, B, H, N, D) == B * H * D * 384 // (1 if fmt == 2 else 2)
     assert bnd.sage_fp4_scales_bytes(2, fmt, B, H, N, D) == B * H * D * 384 // blk
     assert bnd.sage_fp4_codes_bytes(0, fmt, B, H, N, 96) == 0
     assert bnd.sage_fp4_codes_bytes(5, fmt, B, H, N, D) == 0
@@ -59,7 +59,8 @@ MIS = C.c_void_p(0x10008)
 def test_quant_validation():
     q = bnd.sage_fp4_quant
     assert q(3, 0, FAKE, 1, 1, 16, 64, FAKE, FAKE, None) == -5
-    assert q(0, 2, FAKE, 1, 1, 16, 64, FAKE, FAKE, None) == -5
+    assert q(0, 3, FAKE, 1, 1, 16, 64, FAKE, FAKE, None) == -5
+    assert q(2, 2, MIS, 1, 1, 16, 64, FAKE, FAKE, None) == -4
     assert q(0, 0, None, 1, 1, 16, 64, FAKE, FAKE, None) == -1
     assert q(0, 0, FAKE, 1, 1, 16, 64, None, FAKE, None) == -1
     assert q(0, 0, FAKE, 1, 1, 16, 96, FAKE, FAKE, None) == -3
@@ -72,7 +73,8 @@ def test_quant_validation():
 def test_attn_validation():
     a = bnd.sage_fp4_attn_fwd
     ok = [FAKE] * 6
-    assert a(2, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -5
+    assert a(3, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -5
+    assert a(2, *ok, 1, 1, 16, 96, 0, 0.0, FAKE, 1, None) == -3
     assert a(0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, 7, None) == -5
     assert a(0, *ok[:5], None, 1, 1, 16, 64, 0, 0.0, FAKE, 1, None) == -1
     assert a(0, *ok, 1, 1, 16, 64, 0, 0.0, None, 1, None) == -1

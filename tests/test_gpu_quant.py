@@ -1,9 +1,10 @@
 """GPU parity of sage_fp4_quant: codes and scales bit-exact against the oracle.
 
 Covers every positive and negative fp16 value against every E4M3 scale (NVFP4) and against every
-power-of-two scale fp16 inputs can produce (MXFP4), the saturation and underflow regions, zeros
-and signed zeros, every workload's tensors (whole small ones; sampled heads of the full-size
-ones, which the quantiser treats independently), ragged token counts and both head sizes."""
+power-of-two scale fp16 inputs can produce (MXFP4), MXFP8 V blocks over the whole fp16 range
+(clipping blocks included), the saturation and underflow regions, zeros and signed zeros, every
+workload's tensors (whole small ones; sampled heads of the full-size ones, which the quantiser
+treats independently), ragged token counts and both head sizes."""
 import numpy as np
 import pytest
 
@@ -13,6 +14,7 @@ from helpers import gpu_quant, say, workload
 pytestmark = pytest.mark.gpu
 
 ALL = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+PV8 = orc.MX4_PV8
 FIN = ALL[np.isfinite(ALL)]
 
 
@@ -83,7 +85,40 @@ def test_mxfp4_every_fp16_against_every_scale():
     assert np.array_equal(gc, oc)
 
 
-@pytest.mark.parametrize("fmt", [orc.NVFP4, orc.MXFP4])
+def test_mxfp8_v_blocks_over_the_fp16_range():
+    """V of the FP8-PV format: per (channel, 32-slot block) a random binade for the block maximum
+    (all of fp16's), its significand drawn from {1, 1.75, 1.8125, 1.999} and random ones (so some
+    blocks clip at 448), the other values spread over 24 binades below it, both signs, zeros
+    and signed zeros; written to token order through the slot order."""
+    rng = np.random.default_rng(13)
+    D, ntile = 64, 48
+    nb = ntile * 4
+    E = rng.integers(-24, 16, (D, nb))
+    sig = rng.choice([1.0, 1.75, 1.8125, 1.999, 1.5, 1.25], (D, nb))
+    vals = np.empty((D, nb, 32), np.float64)
+    for d in range(D):
+        for b in range(nb):
+            k = rng.integers(0, 24, 32)
+            m = rng.uniform(1, 2, 32)
+            v = m * 2.0 ** (E[d, b] - k) * rng.choice([-1.0, 1.0], 32)
+            v[rng.integers(0, 32)] = sig[d, b] * 2.0 ** E[d, b] * rng.choice([-1.0, 1.0])
+            v[rng.random(32) < 0.03] = 0.0
+            vals[d, b] = v
+    vals = np.clip(vals, -65504, 65504).astype(np.float16)
+    vals[vals == 0] = np.where(rng.random((vals == 0).sum()) < 0.5, np.float16(-0.0), np.float16(0.0))
+    st = orc.slot_tokens()
+    x = np.zeros((1, 1, ntile * 128, D), np.float16)
+    for t in range(ntile):
+        blk = vals[:, 4 * t:4 * t + 4, :].reshape(D, 128)  # [d, slot]
+        x[0, 0, t * 128 + st, :] = blk.T
+    say(f"mxfp8 V table: {x.shape}")
+    gc, gs = gpu_quant(x, orc.ROLE_V, PV8)
+    oc, os_ = orc.quant(orc.ROLE_V, PV8, x)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
+
+
+@pytest.mark.parametrize("fmt", [orc.NVFP4, orc.MXFP4, PV8])
 @pytest.mark.parametrize("shape", [(1, 2, 256, 64), (2, 3, 300, 128), (1, 1, 1, 64), (1, 2, 129, 128)])
 def test_small_shapes_all_roles(fmt, shape):
     B, H, N, D = shape
@@ -96,7 +131,7 @@ def test_small_shapes_all_roles(fmt, shape):
         assert np.array_equal(gc, oc), (role, shape)
 
 
-@pytest.mark.parametrize("wl,fmt", [(2, orc.NVFP4), (3, orc.NVFP4), (4, orc.NVFP4), (3, orc.MXFP4)])
+@pytest.mark.parametrize("wl,fmt", [(2, orc.NVFP4), (3, orc.NVFP4), (4, orc.NVFP4), (3, orc.MXFP4), (4, PV8)])
 def test_full_size_workloads_sampled_heads(wl, fmt):
     """Full-size tensors through the GPU quantiser; the oracle checks a few whole heads."""
     q, k, v = workload(wl)
