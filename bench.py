@@ -112,7 +112,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--causal", action="store_true", help="time the causal variant instead")
-    ap.add_argument("--fmt", choices=["nvfp4", "mxfp4"], default="nvfp4")
+    ap.add_argument("--fmt", choices=["nvfp4", "mxfp4", "mx4_pv8"], default="nvfp4",
+                    help="mx4_pv8: MXFP4 Q and K, MXFP8 P and V")
+    ap.add_argument("--direct-p", action="store_true", help="time sage_fp4_attn_fwd_direct_p (mxfp4 only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the post-run extra measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -129,7 +131,10 @@ def main():
     from bit_attention_amd import binding as bnd
     from bit_attention_amd import synth
 
-    fmt = bnd.NVFP4 if args.fmt == "nvfp4" else bnd.MXFP4
+    fmt = {"nvfp4": bnd.NVFP4, "mxfp4": bnd.MXFP4, "mx4_pv8": bnd.MX4_PV8}[args.fmt]
+    if args.direct_p and fmt != bnd.MXFP4:
+        print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
+        sys.exit(2)
     B, H, N, D = (WORKLOAD[k] for k in "BHND")
     shape = (B, H, N, D)
     log(f"bench: generating inputs {shape} ...")
@@ -158,7 +163,7 @@ def main():
         bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
         if i is not None:
             ev[i][1].record(stream)
-        bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal)
+        bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
         if i is not None:
             ev[i][2].record(stream)
 
@@ -179,24 +184,33 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tops = flops / (attn_ms * 1e-3) / 1e12
     kfile = "attn_nvfp4.hip" if fmt == bnd.NVFP4 else "attn_mxfp4.hip"
-    tkey = f"{'attn_nvfp4' if fmt == bnd.NVFP4 else 'attn_mxfp4'}_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
+    kname = {bnd.NVFP4: "attn_nvfp4", bnd.MXFP4: "attn_mxfp4", bnd.MX4_PV8: "attn_mx4pv8"}[fmt]
+    kname += "_direct_p" if args.direct_p else ""
+    tkey = f"{kname}_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
     traffic = load_traffic(kfile, tkey)
     if fmt == bnd.NVFP4:
         roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tops / FP16_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"}
-    else:
+    elif fmt == bnd.MXFP4:
         roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": attn_tops / FP4_PEAK_TOPS, "traffic": traffic,
-                "kernel": "attn_mxfp4_kernel (block-scaled FP4 MFMA)"}
+                "kernel": "attn_mxfp4_kernel (block-scaled FP4 MFMA"
+                          + (", Direct-P normaliser)" if args.direct_p else ")")}
+    else:
+        mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)  # QK at the FP4 rate, PV at FP8
+        roof = {"bound": "mfma", "achieved": attn_tops, "peak": mixed, "unit": "TFLOP/s",
+                "frac": attn_tops / mixed, "traffic": traffic,
+                "kernel": "attn_mxfp4_kernel, FP8-PV instance (FP4 QK, FP8 PV MFMA)"}
     blk = 16 if fmt == bnd.NVFP4 else 32
-    quant_bytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / blk)
+    v_code_bytes = 1.0 if fmt == bnd.MX4_PV8 else 0.5  # MXFP8 V: one byte per element
+    quant_bytes = B * H * N * D * (2 * (2 + 0.5 + 1.0 / blk) + (2 + v_code_bytes + 1.0 / blk))
     res = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.fmt, "data": "synthetic (seeded SplitMix64/Box-Muller N(0,1) fp16)",
-        "config": {"workload": f"kernel sweep point B={B} H={H} N={N} D={D} {args.fmt} "
-                               f"{'causal' if causal else 'non-causal'}",
+        "config": {"workload": f"kernel sweep point B={B} H={H} N={N} D={D} {args.fmt}"
+                               f"{' direct-p' if args.direct_p else ''} {'causal' if causal else 'non-causal'}",
                    "B": B, "H": H, "N": N, "D": D, "causal": causal, "format": args.fmt,
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
         "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
@@ -232,7 +246,7 @@ def main():
                                  ("mxfp4_direct_p_causal", bnd.MXFP4, True, True),
                                  ("mx4_pv8_noncausal", bnd.MX4_PV8, False, False),
                                  ("mx4_pv8_causal", bnd.MX4_PV8, True, False)):
-            if f2 == fmt and c2 == causal and not dp:
+            if f2 == fmt and c2 == causal and dp == args.direct_p:
                 continue
             Q2 = bnd.quant(q, bnd.ROLE_Q, f2); K2 = bnd.quant(k, bnd.ROLE_K, f2); V2 = bnd.quant(v, bnd.ROLE_V, f2)
             for _ in range(3):

@@ -6,7 +6,7 @@
 // 32 consecutive E2M1 values of one row plus their E8M0 scale, so S = Q K^T and P V run natively
 // at the FP4 rate with FP32 accumulation.
 //
-// Schedule: 8 waves x 16 queries per workgroup, 128-key tiles of FP4 codes and scales staged in
+// Schedule: 8 (D = 64: 4) waves x 16 queries per workgroup, 128-key tiles of FP4 codes and scales staged in
 // LDS (no dequantisation), S^T = K Q^T so that a lane's 32 scores of one query are one MXFP4
 // block of P in slot order, accumulator kept relative to the current tile maximum. At most 128
 // VGPRs, so two workgroups (4 waves per SIMD) share a CU: the softmax is VALU-bound and needs the
@@ -26,8 +26,9 @@
 
 namespace sage {
 
-constexpr int MX_WAVES = 8;
-constexpr int MX_BQ = 16 * MX_WAVES;
+// waves per workgroup (16 queries each): 8 at D = 128; at D = 64, where a tile's staging is half
+// as large, 4 waves (four workgroups per CU) measured faster
+template <int D> constexpr int mx_waves() { return D == 64 ? 4 : 8; }
 
 __device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
   unsigned w = 0;
@@ -88,16 +89,17 @@ __device__ __forceinline__ unsigned partner_of(unsigned mine, unsigned p0, unsig
   return p0 == mine ? p1 : p0;
 }
 template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P, bool PV8>
-__global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
+__global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
     int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
   static_assert(!(PV8 && DIRECT_P), "Direct-P is defined for MXFP4 P");
+  constexpr int MX_NT = 64 * mx_waves<D>(), MX_BQ = 16 * mx_waves<D>();
   constexpr int KROW = D / 2 + 16;        // K code row pitch (bytes)
   constexpr int VB = PV8 ? 128 : 64;      // V code bytes per channel and tile (128 slots)
   constexpr int VROW = VB + 16;           // V code row pitch (bytes)
   constexpr int VPIECES = D * VB / 16;    // 16-byte pieces of a V tile
-  constexpr int VPT = (VPIECES + 511) / 512;  // pieces per thread
+  constexpr int VPT = (VPIECES + MX_NT - 1) / MX_NT;  // pieces per thread
   constexpr int NBD = D / 32;             // MXFP4 blocks along D
   __shared__ __attribute__((aligned(16))) uint8_t sKc[KV_TILE * KROW];
   // scale bytes, laid out so that lane (g, c) finds its eight per tile in one 8-byte word:
@@ -134,29 +136,35 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + MX_BQ - 1) / KV_TILE + 1) : ntiles;
 
-  // Staging: each thread owns at most one 16-byte piece of the K codes, one of the V codes, the
-  // scale bytes of one key and one V channel's four scale bytes. The next tile's pieces are
-  // loaded into registers once the current tile's scores are consumed, so the loads are in
-  // flight during the PV products and the barrier.
+  // Staging: each thread owns a few 16-byte pieces of the K and V codes, the scale bytes of one
+  // key and one V channel's four scale bytes. The next tile's pieces are loaded into registers
+  // once the current tile's scores are consumed, so the loads are in flight during the PV
+  // products and the barrier.
   constexpr int TPK = D / 32;  // 16-byte pieces per key row
+  constexpr int KPIECES = KV_TILE * TPK;
+  constexpr int KPT = (KPIECES + MX_NT - 1) / MX_NT;
   constexpr int VPR = VB / 16;  // 16-byte pieces per V channel row
-  const bool has_k = tid < KV_TILE * TPK;
-  const int kkey = tid / TPK, kpart = tid % TPK;
+  static_assert(MX_NT >= KV_TILE && MX_NT >= D, "one thread per key and per V channel for the scales");
   const uint8_t* kc_h = kc + bh * N * (D / 2);
   const uint8_t* ks_h = ks + bh * N * NBD;
   const int64_t vrow_bytes = PV8 ? Np : Np / 2;
   const uint8_t* vc_h = vc + bh * D * vrow_bytes;   // uniform base; per-thread offsets are 32-bit
   const uint8_t* vs_h = vs + bh * D * (Np / 32);
   const unsigned vs_off = (unsigned)(tid * (Np / 32));
-  uint4 rk = make_uint4(0, 0, 0, 0), rv[VPT];
+  uint4 rk[KPT], rv[VPT];
   unsigned rks = 0, rvs = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) rk[i] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < VPT; ++i) rv[i] = make_uint4(0, 0, 0, 0);
   auto prefetch = [&](int kt) {
-    const int j = kt * KV_TILE + kkey;
-    if (has_k) {
-      rk = make_uint4(0, 0, 0, 0);
-      if (j < N) rk = *reinterpret_cast<const uint4*>(kc_h + (int64_t)j * (D / 2) + 16 * kpart);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + MX_NT * i, j = kt * KV_TILE + e / TPK;
+      if (e < KPIECES) {
+        rk[i] = make_uint4(0, 0, 0, 0);
+        if (j < N) rk[i] = *reinterpret_cast<const uint4*>(kc_h + (int64_t)j * (D / 2) + 16 * (e % TPK));
+      }
     }
     if (tid < KV_TILE) {
       const int jj = kt * KV_TILE + tid;
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int e = tid + 512 * i;
+      const int e = tid + MX_NT * i;
       if (e < VPIECES)
         rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)((e / VPR) * vrow_bytes + 16 * (e % VPR)) +
                                                 (unsigned)kt * (unsigned)VB);
@@ -175,7 +183,11 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
   prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
     __syncthreads();
-    if (has_k) *reinterpret_cast<uint4*>(sKc + (PV8 ? pv8_rho(kkey) : kkey) * KROW + 16 * kpart) = rk;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + MX_NT * i, key = e / TPK;
+      if (e < KPIECES) *reinterpret_cast<uint4*>(sKc + (PV8 ? pv8_rho(key) : key) * KROW + 16 * (e % TPK)) = rk[i];
+    }
     if (tid < KV_TILE) {
       const int r = PV8 ? pv8_rho(tid) : tid;  // LDS row of this key
 #pragma unroll
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int e = tid + 512 * i;
+      const int e = tid + MX_NT * i;
       if (e < VPIECES) *reinterpret_cast<uint4*>(sVc + (e / VPR) * VROW + 16 * (e % VPR)) = rv[i];
     }
     if (tid < D) {
@@ -354,8 +366,9 @@ __global__ __launch_bounds__(512, 4) void attn_mxfp4_kernel(
 template <int D, bool CAUSAL, bool F32, bool DP, bool PV8>
 static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
-  const int nqt = (N + MX_BQ - 1) / MX_BQ;
-  attn_mxfp4_kernel<D, CAUSAL, F32, DP, PV8><<<dim3(nqt * BH), dim3(512), 0, st>>>(
+  constexpr int BQ = 16 * mx_waves<D>();
+  const int nqt = (N + BQ - 1) / BQ;
+  attn_mxfp4_kernel<D, CAUSAL, F32, DP, PV8><<<dim3(nqt * BH), dim3(64 * mx_waves<D>()), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
       (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, k2, out);
 }
