@@ -116,29 +116,35 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   scales[b] = (uint8_t)sb;
 }
 
-// V, MXFP4: one workgroup per (batch*head, 128-token tile). The tile is staged in LDS (row pitch
-// D+2 halves to spread banks), then each thread quantises (channel, block) items whose 32 values
-// are gathered in slot order; with 32-value blocks this beats the register gather below, whose
-// blocks would need more registers than four waves per SIMD allow. Token positions >= N are zero.
-template <int D, int BLK, bool MX>
-__global__ __launch_bounds__(256) void quant_v_lds_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, int N, int64_t Np) {
-  constexpr int PITCH = D + 2;
+// V: one workgroup per (batch*head, 128-token tile). The tile, a contiguous D*256-byte run of
+// fp16, is staged in LDS with 16-byte loads and stores (row pitch D+8 halves keeps 16-byte
+// alignment). Item (channel d, block) gathers its values in slot order from LDS; the blocks of a
+// channel sit in consecutive lanes, so their code bytes form one contiguous run per channel, and
+// every fourth lane writes four blocks' scale bytes as one dword. Token positions >= N are zero.
+// FMT 0: NVFP4 (16-slot blocks, E4M3 scale of amax/6); 1: MXFP4 (32-slot blocks, E8M0 scale;
+// codes are the E2M1 value nearest the exact quotient, ties to even); 2: MXFP8 (32-slot blocks;
+// codes the E4M3 value nearest x / 2^X, ties to even, clamped to +-448; sign the input's).
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales, int N, int64_t Np) {
+  constexpr bool F8 = FMT == 2;
+  constexpr int PITCH = D + 8;  // halves
+  constexpr int BLK = FMT == 0 ? 16 : 32, NB = KV_TILE / BLK;
+  constexpr int CPB = F8 ? BLK : BLK / 2;  // code bytes per block
   __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
   const int kt = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int tok0 = kt * KV_TILE;
   const __half* xs = x + (bh * N + tok0) * (int64_t)D;
   const int ntok = min(KV_TILE, N - tok0);
-  // stage: 4-byte granules (pairs of halves), coalesced over the contiguous tile
-  for (int e = threadIdx.x; e < KV_TILE * D / 2; e += blockDim.x) {
-    const int tok = e / (D / 2), c2 = e % (D / 2);
-    unsigned u = 0;
-    if (tok < ntok) u = reinterpret_cast<const unsigned*>(xs)[(int64_t)tok * (D / 2) + c2];
-    *reinterpret_cast<unsigned*>(&tile[tok * PITCH + 2 * c2]) = u;
+  for (int e = threadIdx.x; e < KV_TILE * D / 8; e += blockDim.x) {
+    const int tok = e / (D / 8), c8 = e % (D / 8);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (tok < ntok) u = reinterpret_cast<const uint4*>(xs)[(int64_t)tok * (D / 8) + c8];
+    *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c8]) = u;
   }
   __syncthreads();
-  constexpr int NB = KV_TILE / BLK;  // blocks per channel per tile
+  static_assert((D * NB) % 256 == 0, "every lane of a quad takes part in each pass");
   for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
     const int d = it / NB, blk = it % NB;
     float v[BLK];
@@ -148,132 +154,36 @@ __global__ __launch_bounds__(256) void quant_v_lds_kernel(const __half* __restri
 #pragma unroll
     for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
     float s;
-    const unsigned sb = MX ? mx_scale(amax, &s) : nv_scale(amax, &s);
-    unsigned words[BLK / 8];
-    encode_block<BLK>(v, s, MX, words);
-    uint8_t* crow = codes + (bh * D + d) * (Np / 2) + (int64_t)kt * (KV_TILE / 2) + blk * (BLK / 2);
-    if (BLK == 16) *reinterpret_cast<uint2*>(crow) = make_uint2(words[0], words[1]);
-    else *reinterpret_cast<uint4*>(crow) = make_uint4(words[0], words[1], words[BLK / 8 > 2 ? 2 : 0], words[BLK / 8 > 3 ? 3 : 0]);
-    scales[(bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk] = (uint8_t)sb;
-  }
-}
-
-// V, MXFP8: the workgroup layout of quant_v_lds_kernel; each (channel, block) item writes its 32
-// E4M3 bytes. The quotient x / 2^X is exact (a power-of-two scale); quotients beyond +-448 clamp
-// to +-448 before the hardware's round-to-nearest-even conversion; the sign is the input's.
-template <int D>
-__global__ __launch_bounds__(256) void quant_v8_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales, int N, int64_t Np) {
-  constexpr int PITCH = D + 2;
-  constexpr int BLK = 32, NB = KV_TILE / BLK;
-  __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
-  const int kt = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int tok0 = kt * KV_TILE;
-  const __half* xs = x + (bh * N + tok0) * (int64_t)D;
-  const int ntok = min(KV_TILE, N - tok0);
-  for (int e = threadIdx.x; e < KV_TILE * D / 2; e += blockDim.x) {
-    const int tok = e / (D / 2), c2 = e % (D / 2);
-    unsigned u = 0;
-    if (tok < ntok) u = reinterpret_cast<const unsigned*>(xs)[(int64_t)tok * (D / 2) + c2];
-    *reinterpret_cast<unsigned*>(&tile[tok * PITCH + 2 * c2]) = u;
-  }
-  __syncthreads();
-  for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
-    const int d = it / NB, blk = it % NB;
-    float v[BLK];
+    const unsigned sb = FMT == 2 ? mx8_scale(amax, &s) : FMT == 1 ? mx_scale(amax, &s) : nv_scale(amax, &s);
+    unsigned words[CPB / 4];
+    if (F8) {
+      const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) v[u] = (float)tile[slot_token(blk * BLK + u) * PITCH + d];
-    float amax = 0.0f;
+      for (int w = 0; w < CPB / 4; ++w) {
+        float q[4];
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
-    float s;
-    const unsigned sb = mx8_scale(amax, &s);
-    const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
-    unsigned words[BLK / 4];
-#pragma unroll
-    for (int w = 0; w < BLK / 4; ++w) {
-      float q[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
-      words[w] = (unsigned)word;
-    }
-    uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * Np + (int64_t)kt * KV_TILE + blk * BLK);
-    crow[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    crow[1] = make_uint4(words[4], words[5], words[6], words[7]);
-    scales[(bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk] = (uint8_t)sb;
-  }
-}
-
-// V, NVFP4: one wave per (batch*head, pair of 128-token tiles). Each lane owns a channel pair; with
-// D = 128 the 64 lanes cover all channels and walk the two tiles in turn, with D = 64 each half
-// of the wave takes one tile. A token's channels are read by the lanes of that tile together
-// (one contiguous row per load), so the gather into slot order needs no LDS: a lane reads its
-// two channels token by token in the order the blocks take them. Each lane then writes its
-// channels' 64 code bytes per tile (a tile pair's 128 bytes come from one wave) and their scale
-// bytes. Token positions >= N are zero.
-template <int D, int BLK, bool MX>
-__global__ __launch_bounds__(256) void quant_v_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, int N, int64_t Np,
-                                                      int npairs, int nwaves) {
-  constexpr int LPT = D / 2;            // lanes per tile (one channel pair each)
-  constexpr int PASSES = LPT / 32;      // tiles of the pair walked in turn: 2 (D = 128) or 1
-  constexpr int NB = KV_TILE / BLK;     // blocks per channel per tile
-  constexpr int WPB = BLK / 8;          // code dwords per block
-  const int lane = threadIdx.x & 63;
-  const int wv = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (wv >= nwaves) return;  // whole waves only; the kernel has no barrier
-  const int64_t bh = wv / npairs;
-  const int pr = wv % npairs;
-  const int ntiles = (int)(Np / KV_TILE);
-  const int d0 = 2 * (lane % LPT);
-  const __half* xs = x + bh * N * (int64_t)D + d0;
-#pragma unroll 1
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int kt = 2 * pr + (PASSES == 2 ? pass : lane / LPT);
-    if (kt >= ntiles) break;
-    const int tok0 = kt * KV_TILE;
-    unsigned cw[2][NB * WPB];
-    unsigned sbytes[2][NB];
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      float v[2][BLK];
-#pragma unroll
-      for (int u = 0; u < BLK; ++u) {
-        const int tok = tok0 + slot_token(blk * BLK + u);
-        unsigned bits = 0;
-        if (tok < N) bits = *reinterpret_cast<const unsigned*>(xs + (int64_t)tok * D);
-        v[0][u] = (float)__ushort_as_half((unsigned short)(bits & 0xFFFF));
-        v[1][u] = (float)__ushort_as_half((unsigned short)(bits >> 16));
+        for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+        words[w] = (unsigned)word;
       }
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        float amax = 0.0f;
-#pragma unroll
-        for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[ch][u]));
-        float sc;
-        sbytes[ch][blk] = MX ? mx_scale(amax, &sc) : nv_scale(amax, &sc);
-        encode_block<BLK>(v[ch], sc, MX, &cw[ch][blk * WPB]);
-      }
+    } else {
+      encode_block<BLK>(v, s, FMT == 1, words);
     }
+    uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * (F8 ? Np : Np / 2) +
+                                           (int64_t)kt * (F8 ? KV_TILE : KV_TILE / 2) + blk * CPB);
+    if (CPB == 8) {
+      *reinterpret_cast<uint2*>(crow) = make_uint2(words[0], words[CPB / 4 > 1 ? 1 : 0]);
+    } else {
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      const int64_t row = bh * D + d0 + ch;
-      uint4* crow = reinterpret_cast<uint4*>(codes + row * (Np / 2) + (int64_t)kt * (KV_TILE / 2));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) crow[q] = make_uint4(cw[ch][4 * q], cw[ch][4 * q + 1], cw[ch][4 * q + 2], cw[ch][4 * q + 3]);
-      uint8_t* srow = scales + row * (Np / BLK) + (int64_t)kt * NB;
-      if (NB == 8) {
-        *reinterpret_cast<uint2*>(srow) =
-            make_uint2(sbytes[ch][0] | sbytes[ch][1] << 8 | sbytes[ch][2] << 16 | sbytes[ch][3] << 24,
-                       sbytes[ch][NB > 4 ? 4 : 0] | sbytes[ch][NB > 5 ? 5 : 0] << 8 |
-                           sbytes[ch][NB > 6 ? 6 : 0] << 16 | sbytes[ch][NB > 7 ? 7 : 0] << 24);
-      } else {
-        *reinterpret_cast<unsigned*>(srow) = sbytes[ch][0] | sbytes[ch][1] << 8 | sbytes[ch][2] << 16 | sbytes[ch][3] << 24;
-      }
+      for (int q = 0; q < CPB / 16; ++q)
+        crow[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
     }
+    // four consecutive blocks' scale bytes, gathered into the lane of the first
+    const unsigned s1 = __shfl_down(sb, 1, 4), s2 = __shfl_down(sb, 2, 4), s3 = __shfl_down(sb, 3, 4);
+    if ((blk & 3) == 0)
+      *reinterpret_cast<unsigned*>(scales + (bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk) =
+          sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
   }
 }
 
@@ -290,8 +200,8 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
-  if (D == 64) quant_v8_kernel<64><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
-  else quant_v8_kernel<128><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
+  if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
+  else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
   return hipGetLastError();
 }
 
@@ -299,16 +209,13 @@ hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* co
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const __half* xp = (const __half*)x;
   uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
+  const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
   if (mx) {
-    const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
-    if (D == 64) quant_v_lds_kernel<64, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
-    else quant_v_lds_kernel<128, 32, true><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np);
   } else {
-    const int npairs = (int)((Np / KV_TILE + 1) / 2);
-    const int nwaves = BH * npairs;
-    const dim3 grid((unsigned)((nwaves + 3) / 4)), block(256);
-    if (D == 64) quant_v_kernel<64, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np, npairs, nwaves);
-    else quant_v_kernel<128, 16, false><<<grid, block, 0, st>>>(xp, c, s, N, Np, npairs, nwaves);
+    if (D == 64) quant_v_tile_kernel<64, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    else quant_v_tile_kernel<128, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np);
   }
   return hipGetLastError();
 }
