@@ -1,0 +1,71 @@
+/* Plain-C client of include/sage_fp4.h: compiles the header as C99 and exercises every entry point
+ * that needs no GPU (version, tile, slot order, size helpers, status strings) plus the host-side
+ * validation of the launching entry points, which returns before anything is enqueued. Built and
+ * run by tests/test_c_header.py; prints "C ABI OK" and exits 0 when every check holds. */
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sage_fp4.h"
+
+static int failures = 0;
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond); \
+      ++failures;                                                     \
+    }                                                                 \
+  } while (0)
+
+int main(void) {
+  /* never dereferenced: every call below fails validation first */
+  void* fake = (void*)(uintptr_t)0x10000;
+  void* mis = (void*)(uintptr_t)0x10008;
+  int s;
+
+  CHECK(sage_fp4_version() >= 300);
+  CHECK(sage_fp4_kv_tile() == 128);
+  {
+    int seen[128];
+    memset(seen, 0, sizeof seen);
+    for (s = 0; s < 128; ++s) {
+      int t = sage_fp4_slot_token(s);
+      CHECK(t >= 0 && t < 128);
+      if (t >= 0 && t < 128) seen[t]++;
+      CHECK(t == 16 * ((s % 32) / 4) + 4 * (s / 32) + s % 4);
+    }
+    for (s = 0; s < 128; ++s) CHECK(seen[s] == 1);
+    CHECK(sage_fp4_slot_token(128) == -1 && sage_fp4_slot_token(-1) == -1);
+  }
+
+  /* layouts: B=2 H=3 N=300 D=128, Np = 384 */
+  CHECK(sage_fp4_codes_bytes(SAGE_ROLE_Q, SAGE_FMT_NVFP4, 2, 3, 300, 128) == (size_t)2 * 3 * 300 * 64);
+  CHECK(sage_fp4_scales_bytes(SAGE_ROLE_K, SAGE_FMT_NVFP4, 2, 3, 300, 128) == (size_t)2 * 3 * 300 * 8);
+  CHECK(sage_fp4_scales_bytes(SAGE_ROLE_K, SAGE_FMT_MXFP4, 2, 3, 300, 128) == (size_t)2 * 3 * 300 * 4);
+  CHECK(sage_fp4_codes_bytes(SAGE_ROLE_V, SAGE_FMT_MXFP4, 2, 3, 300, 128) == (size_t)2 * 3 * 128 * 192);
+  CHECK(sage_fp4_codes_bytes(SAGE_ROLE_V, SAGE_FMT_MX4_PV8, 2, 3, 300, 128) == (size_t)2 * 3 * 128 * 384);
+  CHECK(sage_fp4_scales_bytes(SAGE_ROLE_V, SAGE_FMT_MX4_PV8, 2, 3, 300, 128) == (size_t)2 * 3 * 128 * 12);
+  CHECK(sage_fp4_codes_bytes(SAGE_ROLE_Q, SAGE_FMT_NVFP4, 2, 3, 300, 96) == 0);
+  CHECK(sage_fp4_codes_bytes(SAGE_ROLE_Q, 7, 2, 3, 300, 128) == 0);
+
+  /* validation before any launch */
+  CHECK(sage_fp4_quant(SAGE_ROLE_V, SAGE_FMT_NVFP4, NULL, 1, 1, 16, 64, fake, fake, NULL) == SAGE_ERR_NULL);
+  CHECK(sage_fp4_quant(SAGE_ROLE_V, SAGE_FMT_NVFP4, fake, 1, 1, 16, 80, fake, fake, NULL) == SAGE_ERR_HEAD_DIM);
+  CHECK(sage_fp4_quant(SAGE_ROLE_V, SAGE_FMT_NVFP4, fake, 1, 1, 0, 64, fake, fake, NULL) == SAGE_ERR_SHAPE);
+  CHECK(sage_fp4_quant(SAGE_ROLE_V, SAGE_FMT_NVFP4, mis, 1, 1, 16, 64, fake, fake, NULL) == SAGE_ERR_ALIGN);
+  CHECK(sage_fp4_quant(9, SAGE_FMT_NVFP4, fake, 1, 1, 16, 64, fake, fake, NULL) == SAGE_ERR_ENUM);
+  CHECK(sage_fp4_attn_fwd(SAGE_FMT_MX4_PV8, fake, fake, fake, fake, fake, NULL, 1, 1, 16, 64, 0, 0.0f, fake,
+                          SAGE_OUT_F32, NULL) == SAGE_ERR_NULL);
+  CHECK(sage_fp4_attn_fwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 1, 0.0f, fake, 5,
+                          NULL) == SAGE_ERR_ENUM);
+  CHECK(sage_fp4_attn_fwd(SAGE_FMT_MXFP4, fake, fake, fake, fake, fake, fake, 70000, 1, 16, 64, 0, 0.0f, fake,
+                          SAGE_OUT_F16, NULL) == SAGE_ERR_SHAPE);
+  CHECK(sage_fp4_attn_fwd_direct_p(fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, mis, SAGE_OUT_F16,
+                                   NULL) == SAGE_ERR_ALIGN);
+  for (s = -6; s <= 0; ++s) CHECK(sage_fp4_status_string(s) != NULL && strlen(sage_fp4_status_string(s)) > 0);
+  CHECK(strcmp(sage_fp4_status_string(SAGE_OK), "ok") == 0);
+
+  if (failures) return 1;
+  printf("C ABI OK\n");
+  return 0;
+}
