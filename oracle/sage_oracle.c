@@ -240,12 +240,16 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
   if (D != 64 && D != 128) return ORC_ERR_ARG;
   if (!valid_fmt(fmt)) return ORC_ERR_ARG;
   const int blk = blk_of(fmt);
-  float xb[32];
-  uint8_t cb[32], sb;
+  /* rows (Q, K) and channel rows (V) are independent: OpenMP splits them, nothing else changes */
   if (role == ORC_ROLE_Q || role == ORC_ROLE_K) {
     /* R5: blocks along D; R14: MXFP4 */
     const int qk_fmt = pv8(fmt) ? ORC_MXFP4 : fmt;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
     for (int64_t r = 0; r < (int64_t)B * H * N; ++r) {
+      float xb[32];
+      uint8_t cb[32], sb;
       for (int b0 = 0; b0 < D; b0 += blk) {
         for (int u = 0; u < blk; ++u) xb[u] = orc_f16_to_f32(x[r * D + b0 + u]);
         quant_block(qk_fmt, xb, blk, cb, &sb);
@@ -258,24 +262,29 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
   if (role != ORC_ROLE_V) return ORC_ERR_ARG;
   /* R5/R6: V blocks along tokens, in slot order inside each 128-token tile; zero padding */
   const int64_t Np = ((int64_t)N + ORC_KV_TILE - 1) / ORC_KV_TILE * ORC_KV_TILE;
-  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t row = 0; row < (int64_t)B * H * D; ++row) {
+    const int64_t bh = row / D;
+    const int d = (int)(row % D);
     const uint16_t* xh = x + bh * N * D;
-    for (int d = 0; d < D; ++d) {
-      uint8_t* crow = codes + (bh * D + d) * v_row_bytes(fmt, Np);
-      uint8_t* srow = scales + (bh * D + d) * (Np / blk);
-      for (int64_t p0 = 0; p0 < Np; p0 += blk) {
-        for (int u = 0; u < blk; ++u) {
-          int64_t p = p0 + u;
-          int64_t tok = (p / ORC_KV_TILE) * ORC_KV_TILE + orc_slot_token((int)(p % ORC_KV_TILE));
-          xb[u] = tok < N ? orc_f16_to_f32(xh[tok * D + d]) : 0.0f;
-        }
-        quant_block(fmt, xb, blk, cb, &sb);
-        for (int u = 0; u < blk; ++u) {
-          if (pv8(fmt)) crow[p0 + u] = cb[u];
-          else put_code(crow, p0 + u, cb[u]);
-        }
-        srow[p0 / blk] = sb;
+    uint8_t* crow = codes + (bh * D + d) * v_row_bytes(fmt, Np);
+    uint8_t* srow = scales + (bh * D + d) * (Np / blk);
+    float xb[32];
+    uint8_t cb[32], sb;
+    for (int64_t p0 = 0; p0 < Np; p0 += blk) {
+      for (int u = 0; u < blk; ++u) {
+        int64_t p = p0 + u;
+        int64_t tok = (p / ORC_KV_TILE) * ORC_KV_TILE + orc_slot_token((int)(p % ORC_KV_TILE));
+        xb[u] = tok < N ? orc_f16_to_f32(xh[tok * D + d]) : 0.0f;
       }
+      quant_block(fmt, xb, blk, cb, &sb);
+      for (int u = 0; u < blk; ++u) {
+        if (pv8(fmt)) crow[p0 + u] = cb[u];
+        else put_code(crow, p0 + u, cb[u]);
+      }
+      srow[p0 / blk] = sb;
     }
   }
   return ORC_OK;
