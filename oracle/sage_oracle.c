@@ -389,6 +389,19 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
     int ntile_used = 0;
     float m = -INFINITY, l = 0.0f;
     float x[ORC_KV_TILE], E[ORC_KV_TILE];
+    /* Slack with Direct-P: a changed P value also moves the normaliser, so the output moves by
+     * at most |dP| (|v| + max|O|) / l, and max|O| <= the head's largest |V-hat|. */
+    double vhead = 0.0;
+    if (slack && direct_p) {
+      for (int d = 0; d < D; ++d) {
+        const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
+        const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
+        for (int64_t p = 0; p < Np; ++p) {
+          double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+          if (v > vhead) vhead = v;
+        }
+      }
+    }
     uint8_t vis[ORC_KV_TILE], pc[ORC_KV_TILE], ps[ORC_KV_TILE / 16];
     for (int kt = 0; kt < ntiles; ++kt) {
       if (causal && (int64_t)kt * ORC_KV_TILE > i) break; /* R11 */
@@ -445,19 +458,6 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
       }
       m = mn;
       if (slack) {
-        /* With Direct-P a changed P value also moves the normaliser: the output then moves by
-         * at most |dP| (|v| + max|O|) / l, and max|O| <= the head's largest |V-hat|. */
-        double vhead = 0.0;
-        if (direct_p) {
-          for (int d = 0; d < D; ++d) {
-            const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
-            const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
-            for (int64_t p = 0; p < Np; ++p) {
-              double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
-              if (v > vhead) vhead = v;
-            }
-          }
-        }
         double vmax[ORC_KV_TILE];
         float P2[ORC_KV_TILE];
         for (int s = 0; s < ORC_KV_TILE; ++s) {
