@@ -6,15 +6,17 @@
 // 32 consecutive E2M1 values of one row plus their E8M0 scale, so S = Q K^T and P V run natively
 // at the FP4 rate with FP32 accumulation.
 //
-// Schedule: 8 (D = 64: 4) waves x 16 queries per workgroup, 128-key tiles of FP4 codes and scales staged in
-// LDS (no dequantisation), S^T = K Q^T so that a lane's 32 scores of one query are one MXFP4
-// block of P in slot order, accumulator kept relative to the current tile maximum. At most 128
-// VGPRs, so two workgroups (4 waves per SIMD) share a CU: the softmax is VALU-bound and needs the
-// occupancy to overlap one wave's exp/packing with another's MFMAs. Workgroups are ordered so
-// that each XCD walks through whole heads. The next tile's codes and scales are loaded into
-// registers as soon as the current tile's scores are consumed, so the global loads overlap the
-// PV products and the barrier. Scale bytes sit in LDS so that a lane reads its eight K (or V)
-// scales of a tile as one 8-byte word; the instruction's op_sel bits pick the byte per MFMA.
+// Schedule: 8 (D = 64: 4) waves x 16 queries per workgroup, 128-key tiles of FP4 codes and
+// scales staged in LDS (no dequantisation), S^T = K Q^T so that a lane's 32 scores of one query
+// are one MXFP4 block of P in slot order, accumulator kept relative to the current tile maximum.
+// At most 128 VGPRs, so four waves share a SIMD. The softmax's VALU work dominates the time:
+// on gfx950 MFMA and plain VALU instructions do not overlap (measured), so what counts is the
+// number of VALU instructions per score, which the layout keeps at about six. Workgroups are
+// ordered so that each XCD walks through whole heads. The next tile's codes and scales are
+// loaded into registers as soon as the current tile's scores are consumed, so the global loads
+// overlap the PV products and the barrier. Scale bytes sit in LDS so that a lane reads its eight
+// K (or V) scales of a tile as one 8-byte word; the instruction's op_sel bits pick the byte.
+// Instances: plain MXFP4, Direct-P (normaliser from the rounded P) and FP8-PV (P, V in MXFP8).
 // P has no first level (E8M0 scales cover its range): its codes are E = 2^(x - t) quantised with
 // the lane-local block's power-of-two scale.
 //

@@ -13,7 +13,7 @@
 // products run on v_mfma_f32_16x16x32_f16.
 //   - workgroup = 4 waves = 128 queries of one (batch, head); each wave owns 32 queries as two
 //     16-query groups, so every K/V operand read from LDS feeds two MFMAs. Two workgroups fit on
-//     a CU (LDS 2 x 68 KB at D = 128, at most 256 VGPRs per wave), so one stages while the other
+//     a CU (LDS 2 x 64 KB at D = 128, at most 256 VGPRs per wave), so one stages while the other
 //     computes.
 //   - key tiles of 128: K and V codes of the next tile are loaded into registers while the
 //     current tile is computed, then dequantised into LDS between two barriers.
