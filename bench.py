@@ -72,7 +72,7 @@ def torch_reference_rows(q, k, v, heads, rows, sm_scale):
     return torch.cat(outs).double().cpu().numpy()
 
 
-def cpu_baseline(q_np, k_np, v_np, shape, seconds_target=15.0):
+def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15.0):
     """The oracle, as it stands, on a bounded sample of the same workload: head after head, the
     quantisation of the head's Q, K and V and the attention of every 4th query row of it, until
     about `seconds_target` seconds of CPU time; the quantisation is charged pro rata to the rows
@@ -85,12 +85,12 @@ def cpu_baseline(q_np, k_np, v_np, shape, seconds_target=15.0):
     for bh in range(B * H):
         b, h = divmod(bh, H)
         t0 = time.perf_counter()
-        Q = orc.quant(orc.ROLE_Q, orc.NVFP4, q_np[b:b + 1, h:h + 1])
-        K = orc.quant(orc.ROLE_K, orc.NVFP4, k_np[b:b + 1, h:h + 1])
-        V = orc.quant(orc.ROLE_V, orc.NVFP4, v_np[b:b + 1, h:h + 1])
+        Q = orc.quant(orc.ROLE_Q, fmt, q_np[b:b + 1, h:h + 1])
+        K = orc.quant(orc.ROLE_K, fmt, k_np[b:b + 1, h:h + 1])
+        V = orc.quant(orc.ROLE_V, fmt, v_np[b:b + 1, h:h + 1])
         t_quant = time.perf_counter() - t0
         t0 = time.perf_counter()
-        out = orc.attn_fwd(orc.NVFP4, Q, K, V, (1, 1, N, D), rows=rows, nthreads=nthreads)
+        out = orc.attn_fwd(fmt, Q, K, V, (1, 1, N, D), rows=rows, nthreads=nthreads, direct_p=direct_p)
         t_attn = time.perf_counter() - t0
         assert np.all(np.isfinite(out))
         total_t += t_attn + t_quant * len(rows) / N
@@ -101,9 +101,44 @@ def cpu_baseline(q_np, k_np, v_np, shape, seconds_target=15.0):
     tops = 4.0 * N * D * total_rows / total_t / 1e12
     return {"value": tops, "unit": "TOPS", "cores": nthreads, "kind": "oracle",
             "sample": f"{heads} heads x {len(rows)} query rows (every 4th row; non-causal, N={N}, "
-                      f"D={D}), NVFP4: per head the quantisation of Q, K, V (charged "
+                      f"D={D}), format {fmt}{' Direct-P' if direct_p else ''}: per head the quantisation of Q, K, V (charged "
                       f"{len(rows)}/{N}) and the attention rows; {total_t:.1f} s of CPU time",
             "seconds": total_t}
+
+
+def cpu_one_thread_small(fmt, direct_p=False):
+    """The oracle on one thread over the whole small parity workload (B1 H2 N256 D64): quantisation
+    of Q, K, V and every attention row."""
+    import oracle as orc
+    from bit_attention_amd import synth
+    q, k, v = synth.make_qkv(1)
+    B, H, N, D = q.shape
+    t0 = time.perf_counter()
+    Q = orc.quant(orc.ROLE_Q, fmt, q)
+    K = orc.quant(orc.ROLE_K, fmt, k)
+    V = orc.quant(orc.ROLE_V, fmt, v)
+    orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), nthreads=1, direct_p=direct_p)
+    t = time.perf_counter() - t0
+    return {"value": 4.0 * B * H * N * N * D / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"whole B{B} H{H} N{N} D{D} workload, non-causal (quantisation on the oracle's "
+                      f"default threads), attention on 1 thread", "seconds": t}
+
+
+def copy_ceiling_gbs(torch):
+    """Device-to-device copy of 1 GiB, timed with HIP events: bytes read + written per second."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del src, dst
+    return 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -215,6 +250,7 @@ def main():
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
         "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
         "quant_ms_3_tensors": quant_ms, "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+        "copy_ceiling_gbs": copy_ceiling_gbs(torch),
         "flops_counted": flops, "flops_formula_4BHN2D": flops_formula,
         "roofline": roof,
     }
@@ -223,8 +259,8 @@ def main():
     torch.cuda.synchronize()
     heads = [0, B * H // 2 + 1, B * H - 1]
     rows = torch.arange(0, N, N // 256, device=dev)
+    ref = torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D))  # non-causal
     if not causal:
-        ref = torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D))
         got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
         a, b = got.reshape(-1), ref.reshape(-1)
         res["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
@@ -261,6 +297,11 @@ def main():
             fl = flops_formula / 2 if c2 else flops_formula
             t = fl / (ms * 1e-3) / 1e12
             extras[name] = {"attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS}
+            if not c2:  # accuracy against the same fp32 reference rows
+                got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
+                a, b = got.reshape(-1), ref.reshape(-1)
+                extras[name]["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+                extras[name]["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
             if f2 == bnd.MX4_PV8:  # half the flops at the FP4 rate (QK), half at the FP8 rate (PV)
                 mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)
                 extras[name]["frac_fp4_fp8_mixed_peak"] = t / mixed
@@ -268,7 +309,9 @@ def main():
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape)
+        ofmt = {bnd.NVFP4: 0, bnd.MXFP4: 1, bnd.MX4_PV8: 2}[fmt]
+        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p)
+        res["cpu_one_thread_small_workload"] = cpu_one_thread_small(ofmt, args.direct_p)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
