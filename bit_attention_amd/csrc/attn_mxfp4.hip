@@ -94,7 +94,7 @@ template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P, bool PV8>
 __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out) {
   static_assert(!(PV8 && DIRECT_P), "Direct-P is defined for MXFP4 P");
   constexpr int MX_NT = 64 * mx_waves<D>(), MX_BQ = 16 * mx_waves<D>();
   constexpr int KROW = D / 2 + 16;        // K code row pitch (bytes)
@@ -114,8 +114,9 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int work = xcd_work((int)blockIdx.x, nwork);
-  const int64_t bh = work / nqt;
-  const int qt = CAUSAL ? (nqt - 1 - work % nqt) : work % nqt;
+  int64_t bh = work / nqt;
+  int qt = work % nqt;
+  if (CAUSAL) causal_work(work, nqt, nwork / nqt, cgroup, bh, qt);
   const int q0 = qt * MX_BQ;
   const int qi = q0 + 16 * w + c;
 
@@ -370,9 +371,11 @@ static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, 
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   constexpr int BQ = 16 * mx_waves<D>();
   const int nqt = (N + BQ - 1) / BQ;
+  // K and V bytes per head: FP4 codes + E8M0 scales (FP8-PV: V codes are a byte each)
+  const int cgroup = causal_group(BH, Np * D * (PV8 ? 3 : 2) / 2 + Np * D / 16);
   attn_mxfp4_kernel<D, CAUSAL, F32, DP, PV8><<<dim3(nqt * BH), dim3(64 * mx_waves<D>()), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, cgroup, k2, out);
 }
 
 template <bool DP, bool PV8>

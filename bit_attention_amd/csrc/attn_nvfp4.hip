@@ -137,7 +137,7 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, int nwork, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out) {
   constexpr int KC = D / 8;        // 16-byte chunks per K-hat row (16 or 8)
   constexpr int CB = D / 4;        // code bytes each thread stages per tile, for K and for V
   constexpr int CW = CB / 4;       // ... in dwords (8 codes each; two dwords per 16-block)
@@ -151,8 +151,9 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int work = xcd_work((int)blockIdx.x, nwork);
-  const int64_t bh = work / nqt;
-  const int qt = CAUSAL ? (nqt - 1 - work % nqt) : work % nqt;  // heavy causal tiles first
+  int64_t bh = work / nqt;
+  int qt = work % nqt;
+  if (CAUSAL) causal_work(work, nqt, nwork / nqt, cgroup, bh, qt);
   const int q0 = qt * NV_BQ;
   const int qi0 = q0 + 32 * w + c;  // group a holds query qi0 + 16a
 
@@ -334,9 +335,10 @@ static void launch_nv(const void* const* p, int BH, int N, float k2, void* out, 
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + NV_BQ - 1) / NV_BQ;
   const int nwork = nqt * BH;
+  const int cgroup = causal_group(BH, Np * D * 9 / 8);  // K and V: codes + E4M3 scales
   attn_nvfp4_kernel<D, CAUSAL, F32><<<dim3(nwork), dim3(64 * NV_WAVES), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, cgroup, k2, out);
 }
 
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,

@@ -41,6 +41,32 @@ __device__ __forceinline__ int xcd_work(int L, int T) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
 }
 
+// Work item w of a causal launch -> (batch*head bh, query tile qt). Heads are taken in groups of
+// G (the last group may be smaller); inside a group the heaviest query tiles (those with the most
+// key tiles under the causal mask) of all its heads come first. Heavy and light items then mix
+// along the grid, while one group's K and V stay small enough to share an XCD's L2 (the host
+// picks G from the K/V bytes per head). G = 1 is head-major, heaviest tile first.
+__device__ __forceinline__ void causal_work(int w, int nqt, int BH, int G, int64_t& bh, int& qt) {
+  const int gsize = G * nqt, grp = w / gsize, base = grp * G;
+  const int Gg = min(G, BH - base), r = w - grp * gsize;
+  bh = base + r % Gg;
+  qt = nqt - 1 - r / Gg;
+}
+
+// Heads per causal group (measured on B4 H32 N4096 and B1 H32 N32768): groups must not straddle
+// the contiguous range of heads each XCD receives, so G is a power of two dividing the heads per
+// XCD (BH / 8; 1 when BH is not a multiple of 8), at most 8, and small enough that the group's K
+// and V (kv_bytes_per_head each) stay within 24 MiB.
+inline int causal_group(int BH, int64_t kv_bytes_per_head) {
+  if (BH % 8 != 0) return 1;
+  const int hx = BH / 8;
+  int64_t cap = (int64_t(24) << 20) / (kv_bytes_per_head > 0 ? kv_bytes_per_head : 1);
+  if (cap > 8) cap = 8;
+  int g = 1;
+  while (2 * g <= hx && 2 * g <= cap && hx % (2 * g) == 0) g *= 2;
+  return g;
+}
+
 __device__ __forceinline__ float as_f(unsigned u) { return __uint_as_float(u); }
 __device__ __forceinline__ unsigned as_u(float f) { return __float_as_uint(f); }
 
