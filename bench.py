@@ -250,7 +250,8 @@ def main():
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
         "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
         "quant_ms_3_tensors": quant_ms, "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
-        "copy_ceiling_gbs": copy_ceiling_gbs(torch),
+        # not in counter runs: their one calibration copy must be the only copy kernel
+        "copy_ceiling_gbs": None if args.calibrate_copy else copy_ceiling_gbs(torch),
         "flops_counted": flops, "flops_formula_4BHN2D": flops_formula,
         "roofline": roof,
     }
