@@ -33,7 +33,8 @@ namespace sage {
 template <int D> constexpr int mx_waves() { return D == 64 ? 4 : 8; }
 
 __device__ __forceinline__ unsigned pack_e4(const float* v, float scale) {
-  unsigned w = 0;
+  // every byte of w is written below, so its initial value is irrelevant (no register zeroing)
+  unsigned w = as_u(v[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
@@ -247,16 +248,19 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       tS = pair32_max(fmaxf(bmx, bmB));
     } else {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) bmx = fmaxf(bmx, fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])));
+      for (int t = 0; t < 8; t += 2) {  // three-input maxima: 16 instructions for 32 values
+        bmx = max3f(bmx, max3f(S[t][0], S[t][1], S[t][2]), max3f(S[t][3], S[t + 1][0], S[t + 1][1]));
+        bmx = max3f(bmx, S[t + 1][2], S[t + 1][3]);
+      }
       tS = xg_max(bmx);
     }
     const bool vis = tS > -INFINITY;
-    float T = 0.0f;  // tile maximum in log2 units, rounded toward -infinity
-    if (vis) {
-      T = tS * k2;
-      if (__builtin_fmaf(tS, k2, -T) < 0.0f)  // the product was rounded up: step one ulp down
-        T = T > 0.0f ? as_f(as_u(T) - 1u) : (T < 0.0f ? as_f(as_u(T) + 1u) : -0x1p-149f);
-    }
+    // tile maximum in log2 units, rounded toward -infinity: when the product was rounded up, step
+    // one ulp down (selects, no branches; an empty tile gives T = 0 and is not accepted)
+    const float T0 = tS * k2;
+    const float Tdn = T0 > 0.0f ? as_f(as_u(T0) - 1u) : (T0 < 0.0f ? as_f(as_u(T0) + 1u) : -0x1p-149f);
+    float T = __builtin_fmaf(tS, k2, -T0) < 0.0f ? Tdn : T0;
+    T = vis ? T : 0.0f;
     const float m_new = fmaxf(m_u, T);
     const bool accept = vis && (T >= m_new - 64.0f);
 

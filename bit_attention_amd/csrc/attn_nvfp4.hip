@@ -55,7 +55,7 @@ __device__ __forceinline__ void scales4(unsigned sw, _Float16* h) {
 }
 
 __device__ __forceinline__ unsigned pack_fp4_8(const float* q) {
-  unsigned w = 0;
+  unsigned w = __float_as_uint(q[0]);  // every byte is written below; no register zeroing
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
