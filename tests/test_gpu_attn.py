@@ -137,3 +137,17 @@ def test_accuracy_nvfp4_vs_mxfp4_against_full_precision():
         res[fmt] = _metrics(gr, ref)
     say(f"  workload 3 (sampled rows): NVFP4 {res[0]} | MXFP4 {res[1]}")
     assert res[0][0] > res[1][0]
+
+
+@pytest.mark.parametrize("fmt,direct_p", [(orc.NVFP4, False), (orc.MXFP4, False), (orc.MXFP4, True),
+                                          (orc.MX4_PV8, False)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bench_configuration_f16_output(fmt, direct_p, causal):
+    """bench.py times the fp16-output instances at B4 H32 N4096 D128. Their output must be the
+    fp32-output instance's (checked against the oracle above and in the Direct-P / FP8-PV files)
+    rounded to fp16, bit for bit, on every element."""
+    q, k, v = workload(2)
+    say(f"bench configuration fmt={fmt} direct_p={direct_p} causal={causal}")
+    a = gpu_attn(fmt, q, k, v, causal, direct_p=direct_p)
+    h = gpu_attn(fmt, q, k, v, causal, out_f32=False, direct_p=direct_p)
+    assert np.array_equal(h, a.astype(np.float16).astype(np.float32))
