@@ -16,6 +16,8 @@ import oracle as orc
 from bit_attention_amd import synth
 
 FMTS = [orc.NVFP4, orc.MXFP4]
+# the generic properties below also hold for the two MXFP4 variants: (format, Direct-P)
+VARIANTS = [(orc.NVFP4, False), (orc.MXFP4, False), (orc.MXFP4, True), (orc.MX4_PV8, False)]
 
 
 def vhat_tokens(fmt, v_codes, v_scales, N):
@@ -31,12 +33,13 @@ def vhat_tokens(fmt, v_codes, v_scales, N):
     return out[:, :, :N, :]
 
 
-def run(fmt, q, k, v, causal=False, rows=None, slack=False):
+def run(fmt, q, k, v, causal=False, rows=None, slack=False, direct_p=False):
     B, H, N, D = q.shape
     Q = orc.quant(orc.ROLE_Q, fmt, q)
     K = orc.quant(orc.ROLE_K, fmt, k)
     V = orc.quant(orc.ROLE_V, fmt, v)
-    return orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, rows=rows, want_slack=slack)
+    return orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, rows=rows, want_slack=slack,
+                        direct_p=direct_p)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -211,41 +214,41 @@ def test_one_hot_at_every_slot(fmt):
         np.testing.assert_allclose(out[0, h], np.broadcast_to(v[0, h, h].astype(np.float32), (N, D)), rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_key_tile_permutation_invariance(fmt):
+@pytest.mark.parametrize("fmt,direct_p", VARIANTS)
+def test_key_tile_permutation_invariance(fmt, direct_p):
     """Non-causal: permuting whole 128-key tiles of K and V together leaves each tile's P
     unchanged, so the output changes only by FP32 rounding of the rescaling order."""
     q, k, v = synth.make_qkv(1, N=512)
     perm = np.concatenate([np.arange(128) + 128 * t for t in [2, 0, 3, 1]])
-    a = run(fmt, q, k, v)
-    b = run(fmt, q, k[:, :, perm], v[:, :, perm])
+    a = run(fmt, q, k, v, direct_p=direct_p)
+    b = run(fmt, q, k[:, :, perm], v[:, :, perm], direct_p=direct_p)
     assert np.max(np.abs(a - b)) < 2e-6 * max(1.0, np.abs(a).max())
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_linearity_and_head_independence(fmt):
+@pytest.mark.parametrize("fmt,direct_p", VARIANTS)
+def test_linearity_and_head_independence(fmt, direct_p):
     q, k, v = synth.make_qkv(1, N=200)
-    a = run(fmt, q, k, v, causal=True)
-    b = run(fmt, q, k, (v.astype(np.float32) * 2).astype(np.float16), causal=True)
+    a = run(fmt, q, k, v, causal=True, direct_p=direct_p)
+    b = run(fmt, q, k, (v.astype(np.float32) * 2).astype(np.float16), causal=True, direct_p=direct_p)
     assert np.array_equal(b, 2 * a)  # scales double exactly, codes identical
     hp = [1, 0]
-    c = run(fmt, q[:, hp], k[:, hp], v[:, hp], causal=True)
+    c = run(fmt, q[:, hp], k[:, hp], v[:, hp], causal=True, direct_p=direct_p)
     assert np.array_equal(c, a[:, hp])
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_row_subset_matches_full(fmt):
+@pytest.mark.parametrize("fmt,direct_p", VARIANTS)
+def test_row_subset_matches_full(fmt, direct_p):
     q, k, v = synth.make_qkv(1, N=300)
-    full = run(fmt, q, k, v, causal=True)
+    full = run(fmt, q, k, v, causal=True, direct_p=direct_p)
     rows = np.array([0, 1, 127, 128, 299, 300, 450, 599])
-    sub = run(fmt, q, k, v, causal=True, rows=rows)
+    sub = run(fmt, q, k, v, causal=True, rows=rows, direct_p=direct_p)
     assert np.array_equal(sub, full.reshape(-1, 64)[rows])
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_causal_row_zero_is_vhat_zero(fmt):
+@pytest.mark.parametrize("fmt,direct_p", VARIANTS)
+def test_causal_row_zero_is_vhat_zero(fmt, direct_p):
     q, k, v = synth.make_qkv(1, N=256)
-    out = run(fmt, q, k, v, causal=True)
+    out = run(fmt, q, k, v, causal=True, direct_p=direct_p)
     Vc, Vs = orc.quant(orc.ROLE_V, fmt, v)
     vh = vhat_tokens(fmt, Vc, Vs, 256)
     np.testing.assert_allclose(out[:, :, 0], vh[:, :, 0], rtol=2e-7, atol=1e-7)
