@@ -256,16 +256,23 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     }
     const bool vis = tS > -INFINITY;
     // tile maximum in log2 units, rounded toward -infinity: when the product was rounded up, step
-    // one ulp down (selects, no branches; an empty tile gives T = 0 and is not accepted)
+    // one ulp down, i.e. subtract 1 from the bit pattern of a positive T0 and add 1 to that of a
+    // negative one (-0 gives -2^-149; +0 is exact whenever the residual is negative, since k2 > 0).
+    // Integer arithmetic and one select, no branches; an empty tile gives T = 0 and is not accepted.
     const float T0 = tS * k2;
-    const float Tdn = T0 > 0.0f ? as_f(as_u(T0) - 1u) : (T0 < 0.0f ? as_f(as_u(T0) + 1u) : -0x1p-149f);
+    const float Tdn = as_f(as_u(T0) - (unsigned)((__float_as_int(T0) >> 31) | 1));
     float T = __builtin_fmaf(tS, k2, -T0) < 0.0f ? Tdn : T0;
     T = vis ? T : 0.0f;
     const float m_new = fmaxf(m_u, T);
     const bool accept = vis && (T >= m_new - 64.0f);
 
     // the lane's block: E8M0 scale 2^(floor(log2 amax) - EMAX), amax = the block maximum of E
-    // (EMAX = 2 for E2M1, 8 for E4M3); then E chunk by chunk, summed and packed at once
+    // (EMAX = 2 for E2M1, 8 for E4M3); then E chunk by chunk, summed and packed at once. A block
+    // that is dropped (its tile rejected, or its amax below the E8M0 range) keeps its codes but
+    // takes the scale byte 0, i.e. 2^-127. Once a tile is accepted the normaliser is at least 1
+    // in the accumulator's frame (its maximal score has E = 1), and such a block adds at most
+    // 2^-127 * 448 * 32 times the largest V value to O, far below FP32 resolution; in exchange the
+    // codes need no select or branch.
     constexpr int EMAX = PV8 ? 8 : 2;
     constexpr float AMIN = PV8 ? 0x1p-118f : 0x1p-124f;  // below: X < -126, the block is dropped
     const float amax = exp2_01(__builtin_fmaf(bmx, k2, -T));
@@ -291,12 +298,11 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
           esum += E[i];
           E[i] = fminf(E[i], wd < 4 ? cap : capB);
         }
-        const bool kp = wd < 4 ? keep : keepB;
-        pf[wd] = kp ? (int)pack_e4m3(E[0], E[1], E[2], E[3], wd < 4 ? sc : scB) : 0;
+        pf[wd] = (int)pack_e4m3(E[0], E[1], E[2], E[3], wd < 4 ? sc : scB);
       }
       // the B operand's scale of K-block g: block 0 (1) is the first half of groups 0, 1 (2, 3),
       // block 2 (3) the second half; groups 1 and 2 take it from their partner across 32 lanes
-      const int sA = keep ? X + 127 : 127, sB = keepB ? XB + 127 : 127;
+      const int sA = keep ? X + 127 : 0, sB = keepB ? XB + 127 : 0;
       const unsigned send = (unsigned)(g < 2 ? sB : sA);
       const auto pr = __builtin_amdgcn_permlane32_swap(send, send, false, false);
       const int recv = (int)partner_of(send, pr[0], pr[1]);
@@ -310,9 +316,9 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
           E[e] = exp2_01(__builtin_fmaf(S[2 * wd + (e >> 2)][e & 3], k2, -T));
           if (!DIRECT_P) esum += E[e];
         }
-        pf[wd] = keep ? (int)pack_e4(E, sc) : 0;
+        pf[wd] = (int)pack_e4(E, sc);
       }
-      psc = keep ? X + 127 : 127;
+      psc = keep ? X + 127 : 0;
     }
     if (kt + 1 < kt_end) prefetch(kt + 1);
     if (!accept) esum = 0.0f;
