@@ -2,7 +2,8 @@
 
 One step = the whole hot path over one batch: sage_fp4_quant of Q, K and V, then
 sage_fp4_attn_fwd, with the fp16 inputs already resident in HBM. Workload: B=4, H=32, N=4096,
-D=128, NVFP4, non-causal (the kernel-sweep point), synthetic seeded inputs.
+D=128, NVFP4, non-causal (the kernel-sweep point), synthetic seeded inputs; --seq-len picks
+another point of the N sweep at the same B, H, D (1024, 2048, 8192, 16384).
 
 Prints one JSON line. `value` = 4*B*H*N^2*D / (step time) in TOPS (whole step, quantisation
 included); the attention kernel alone is reported in `attn_*` fields and `roofline`, timed with
@@ -150,6 +151,8 @@ def main():
     ap.add_argument("--fmt", choices=["nvfp4", "mxfp4", "mx4_pv8"], default="nvfp4",
                     help="mx4_pv8: MXFP4 Q and K, MXFP8 P and V")
     ap.add_argument("--direct-p", action="store_true", help="time sage_fp4_attn_fwd_direct_p (mxfp4 only)")
+    ap.add_argument("--seq-len", type=int, default=WORKLOAD["N"],
+                    help="N of the sweep at B=4 H=32 D=128 (default 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the post-run extra measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -170,11 +173,15 @@ def main():
     if args.direct_p and fmt != bnd.MXFP4:
         print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
         sys.exit(2)
-    B, H, N, D = (WORKLOAD[k] for k in "BHND")
+    B, H, D = (WORKLOAD[k] for k in "BHD")
+    N = args.seq_len
+    if N < 256 or N % 256:
+        print("bench.py: --seq-len must be a positive multiple of 256", file=sys.stderr)
+        sys.exit(2)
     shape = (B, H, N, D)
     log(f"bench: generating inputs {shape} ...")
     t0 = time.perf_counter()
-    q_np, k_np, v_np = synth.make_qkv(2)
+    q_np, k_np, v_np = synth.make_qkv(2, N=N)
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     q = torch.from_numpy(q_np).to(dev)
@@ -275,6 +282,18 @@ def main():
         res["copy_calibration_bytes"] = 256 << 20
 
     if not args.no_extras:
+        # the same attention launch alone, back to back (3 warm-ups, then 10 timed launches):
+        # the kernel-benchmark convention, without the quantisation kernels in between
+        for _ in range(3):
+            bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(10):
+            bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        res["attn_alone_ms"] = a0.elapsed_time(a1) / 10
+        res["attn_alone_tops"] = flops / (res["attn_alone_ms"] * 1e-3) / 1e12
         extras = {}
         for name, f2, c2, dp in (("nvfp4_causal", bnd.NVFP4, True, False),
                                  ("mxfp4_noncausal", bnd.MXFP4, False, False),
