@@ -23,7 +23,10 @@ hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bo
 namespace {
 
 constexpr int kMaxN = 1 << 20;
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// B*H*N*D < 2^36 keeps every launch grid below 2^32 work-items (the attention kernels run up to
+// 4 work-items per query, the Q/K quantiser one per 16 elements); three fp16 tensors of that
+// size would not fit in HBM anyway.
+constexpr int64_t kMaxElems = int64_t(1) << 36;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -116,9 +116,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   scales[b] = (uint8_t)sb;
 }
 
-// V: one workgroup per (batch*head, 128-token tile). The tile, a contiguous D*256-byte run of
-// fp16, is staged in LDS with 16-byte loads and stores (row pitch D+8 halves keeps 16-byte
-// alignment). Item (channel d, block) gathers its values in slot order from LDS; the blocks of a
+// V: one workgroup per (batch*head, run of `tpw` consecutive 128-token tiles). Each tile, a
+// contiguous D*256-byte run of fp16, is loaded into registers with 16-byte loads while the
+// previous tile is encoded, then staged in LDS (row pitch D+8 halves keeps 16-byte alignment). Item (channel d, block) gathers its values in slot order from LDS; the blocks of a
 // channel sit in consecutive lanes, so their code bytes form one contiguous run per channel, and
 // every fourth lane writes four blocks' scale bytes as one dword. Token positions >= N are zero.
 // FMT 0: NVFP4 (16-slot blocks, E4M3 scale of amax/6); 1: MXFP4 (32-slot blocks, E8M0 scale;
@@ -126,65 +126,86 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
 // codes the E4M3 value nearest x / 2^X, ties to even, clamped to +-448; sign the input's).
 template <int D, int FMT>
 __global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales, int N, int64_t Np) {
+                                                           uint8_t* __restrict__ scales, int N, int64_t Np, int tpw) {
   constexpr bool F8 = FMT == 2;
   constexpr int PITCH = D + 8;  // halves
   constexpr int BLK = FMT == 0 ? 16 : 32, NB = KV_TILE / BLK;
   constexpr int CPB = F8 ? BLK : BLK / 2;  // code bytes per block
+  constexpr int PPT = KV_TILE * D / 8 / 256;  // 16-byte pieces of a tile per thread
   __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
-  const int kt = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  const int tok0 = kt * KV_TILE;
-  const __half* xs = x + (bh * N + tok0) * (int64_t)D;
-  const int ntok = min(KV_TILE, N - tok0);
-  for (int e = threadIdx.x; e < KV_TILE * D / 8; e += blockDim.x) {
-    const int tok = e / (D / 8), c8 = e % (D / 8);
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (tok < ntok) u = reinterpret_cast<const uint4*>(xs)[(int64_t)tok * (D / 8) + c8];
-    *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c8]) = u;
-  }
-  __syncthreads();
-  static_assert((D * NB) % 256 == 0, "every lane of a quad takes part in each pass");
-  for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
-    const int d = it / NB, blk = it % NB;
-    float v[BLK];
+  const int ntiles = (int)(Np / KV_TILE);
+  const int kt0 = blockIdx.x * tpw, kt1 = min(ntiles, kt0 + tpw);
+  uint4 pre[PPT];
+  // the tile's fp16 pieces into registers (token positions >= N read as zero)
+  auto load = [&](int kt) {
+    const int tok0 = kt * KV_TILE, ntok = min(KV_TILE, N - tok0);
+    const uint4* xs = reinterpret_cast<const uint4*>(x + (bh * N + tok0) * (int64_t)D);
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) v[u] = (float)tile[slot_token(blk * BLK + u) * PITCH + d];
-    float amax = 0.0f;
+    for (int i = 0; i < PPT; ++i) {
+      const int e = threadIdx.x + 256 * i, tok = e / (D / 8);
+      pre[i] = tok < ntok ? xs[e] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load(kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    __syncthreads();  // the previous tile's LDS reads are complete
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
-    float s;
-    const unsigned sb = FMT == 2 ? mx8_scale(amax, &s) : FMT == 1 ? mx_scale(amax, &s) : nv_scale(amax, &s);
-    unsigned words[CPB / 4];
-    if (F8) {
-      const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
+    for (int i = 0; i < PPT; ++i) {
+      const int e = threadIdx.x + 256 * i, tok = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c8]) = pre[i];
+    }
+    __syncthreads();
+    if (kt + 1 < kt1) load(kt + 1);  // in flight while this tile is encoded and stored
+    static_assert((D * NB) % 256 == 0, "every lane of a quad takes part in each pass");
+    for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
+      const int d = it / NB, blk = it % NB;
+      float v[BLK];
 #pragma unroll
-      for (int w = 0; w < CPB / 4; ++w) {
-        float q[4];
+      for (int u = 0; u < BLK; ++u) v[u] = (float)tile[slot_token(blk * BLK + u) * PITCH + d];
+      float amax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
-        words[w] = (unsigned)word;
+      for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
+      float s;
+      const unsigned sb = FMT == 2 ? mx8_scale(amax, &s) : FMT == 1 ? mx_scale(amax, &s) : nv_scale(amax, &s);
+      unsigned words[CPB / 4];
+      if (F8) {
+        const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
+#pragma unroll
+        for (int w = 0; w < CPB / 4; ++w) {
+          float q[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+          words[w] = (unsigned)word;
+        }
+      } else {
+        encode_block<BLK>(v, s, FMT == 1, words);
       }
-    } else {
-      encode_block<BLK>(v, s, FMT == 1, words);
-    }
-    uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * (F8 ? Np : Np / 2) +
-                                           (int64_t)kt * (F8 ? KV_TILE : KV_TILE / 2) + blk * CPB);
-    if (CPB == 8) {
-      *reinterpret_cast<uint2*>(crow) = make_uint2(words[0], words[CPB / 4 > 1 ? 1 : 0]);
-    } else {
+      uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * (F8 ? Np : Np / 2) +
+                                             (int64_t)kt * (F8 ? KV_TILE : KV_TILE / 2) + blk * CPB);
+      if (CPB == 8) {
+        *reinterpret_cast<uint2*>(crow) = make_uint2(words[0], words[CPB / 4 > 1 ? 1 : 0]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < CPB / 16; ++q)
-        crow[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
+        for (int q = 0; q < CPB / 16; ++q)
+          crow[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
+      }
+      // four consecutive blocks' scale bytes, gathered into the lane of the first
+      const unsigned s1 = __shfl_down(sb, 1, 4), s2 = __shfl_down(sb, 2, 4), s3 = __shfl_down(sb, 3, 4);
+      if ((blk & 3) == 0)
+        *reinterpret_cast<unsigned*>(scales + (bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk) =
+            sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
     }
-    // four consecutive blocks' scale bytes, gathered into the lane of the first
-    const unsigned s1 = __shfl_down(sb, 1, 4), s2 = __shfl_down(sb, 2, 4), s3 = __shfl_down(sb, 3, 4);
-    if ((blk & 3) == 0)
-      *reinterpret_cast<unsigned*>(scales + (bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk) =
-          sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
   }
+}
+
+// tiles per workgroup of the V quantiser: up to 4, keeping at least 2048 workgroups
+inline int v_tiles_per_wg(int64_t ntiles, int BH) {
+  int tpw = 4;
+  while (tpw > 1 && ((ntiles + tpw - 1) / tpw) * BH < 2048) tpw /= 2;
+  return tpw;
 }
 
 // ---- launchers (arguments already validated by the C ABI layer) ----
@@ -198,10 +219,11 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
 }
 
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
-  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
-  const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
-  if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
-  else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np);
+  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE, nt = Np / KV_TILE;
+  const int tpw = v_tiles_per_wg(nt, BH);
+  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(256);
+  if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
+  else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
   return hipGetLastError();
 }
 
@@ -209,13 +231,15 @@ hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* co
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const __half* xp = (const __half*)x;
   uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
-  const dim3 grid((unsigned)(Np / KV_TILE), (unsigned)BH), block(256);
+  const int64_t nt = Np / KV_TILE;
+  const int tpw = v_tiles_per_wg(nt, BH);
+  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(256);
   if (mx) {
-    if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np);
-    else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
+    else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
   } else {
-    if (D == 64) quant_v_tile_kernel<64, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np);
-    else quant_v_tile_kernel<128, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np);
+    if (D == 64) quant_v_tile_kernel<64, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
+    else quant_v_tile_kernel<128, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
   }
   return hipGetLastError();
 }

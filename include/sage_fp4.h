@@ -41,7 +41,8 @@
  *     is returned on error and nothing is launched. SAGE_ERR_HIP reports a launch failure
  *     (hipGetLastError after the launch).
  *   - every pointer must be 16-byte aligned; tensors are dense and row-major.
- *   - supported: D in {64, 128}; 1 <= N <= 1048576; B*H*N*D < 2^40. N_q == N_k, no GQA.
+ *   - supported: D in {64, 128}; 1 <= N <= 1048576; B*H <= 65535; B*H*N*D < 2^36 (a launch
+ *     grid limit, larger than three fp16 tensors that fit in HBM). N_q == N_k, no GQA.
  */
 #ifndef SAGE_FP4_H
 #define SAGE_FP4_H

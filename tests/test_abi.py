@@ -68,6 +68,17 @@ def test_quant_validation():
     assert q(0, 0, FAKE, 1, 1, 0, 64, FAKE, FAKE, None) == -2
     assert q(0, 0, FAKE, 1, 1, (1 << 20) + 1, 64, FAKE, FAKE, None) == -2
     assert q(0, 0, MIS, 1, 1, 16, 64, FAKE, FAKE, None) == -4
+    # B*H*N*D < 2^36: B*H = 1024, N = 2^20, D = 64 is exactly 2^36
+    assert q(0, 0, FAKE, 1, 1024, 1 << 20, 64, FAKE, FAKE, None) == -2
+    assert q(2, 1, FAKE, 2, 512, 1 << 20, 64, FAKE, FAKE, None) == -2
+
+
+def test_element_limit_in_size_queries():
+    """The size queries accept the largest shape under 2^36 elements and reject 2^36."""
+    assert bnd.sage_fp4_codes_bytes(0, 0, 1, 1023, 1 << 20, 64) == 1023 * (1 << 20) * 32
+    assert bnd.sage_fp4_codes_bytes(0, 0, 1, 1024, 1 << 20, 64) == 0
+    assert bnd.sage_fp4_scales_bytes(2, 1, 1, 511, 1 << 20, 128) == 511 * 128 * ((1 << 20) // 32)
+    assert bnd.sage_fp4_scales_bytes(2, 1, 1, 512, 1 << 20, 128) == 0
 
 
 def test_attn_validation():
