@@ -30,6 +30,11 @@ FP8_PEAK_TOPS = 5033.0       # MI355X dense FP8 MFMA (half the FP4 rate)
 FP16_PEAK_TFLOPS = 2516.6    # dense fp16 MFMA
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(B=4, H=32, N=4096, D=128)
+WORKLOAD_NAMES = {2: "kernel sweep point", 3: "video-DiT shape", 4: "long-context causal"}
+DATA_NOTES = {
+    2: "synthetic (seeded SplitMix64/Box-Muller N(0,1) fp16)",
+    3: "synthetic (seeded N(0,1) fp16; K plus per-(head, channel) offsets drawn N(0, sd 3))",
+    4: "synthetic (seeded N(0,1) fp16; each entry +-20 with probability 0.001)"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -167,6 +172,9 @@ def main():
     ap.add_argument("--direct-p", action="store_true", help="time sage_fp4_attn_fwd_direct_p (mxfp4 only)")
     ap.add_argument("--seq-len", type=int, default=WORKLOAD["N"],
                     help="N of the sweep at B=4 H=32 D=128 (default 4096)")
+    ap.add_argument("--workload", type=int, choices=[2, 3, 4], default=2,
+                    help="3: video-DiT shape B1 H48 N17776 D64 with K channel offsets; 4: long causal "
+                         "B1 H32 N32768 D128 with +-20 outliers (implies --causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the post-run extra measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -187,15 +195,20 @@ def main():
     if args.direct_p and fmt != bnd.MXFP4:
         print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
         sys.exit(2)
-    B, H, D = (WORKLOAD[k] for k in "BHD")
-    N = args.seq_len
-    if N < 256 or N % 256:
-        print("bench.py: --seq-len must be a positive multiple of 256", file=sys.stderr)
-        sys.exit(2)
+    if args.workload == 2:
+        B, H, D = (WORKLOAD[k] for k in "BHD")
+        N = args.seq_len
+        if N < 256 or N % 256:
+            print("bench.py: --seq-len must be a positive multiple of 256", file=sys.stderr)
+            sys.exit(2)
+    else:
+        w = synth.WORKLOADS[args.workload]
+        B, H, N, D = w["B"], w["H"], w["N"], w["D"]
+        args.causal = args.causal or w["causal"]
     shape = (B, H, N, D)
     log(f"bench: generating inputs {shape} ...")
     t0 = time.perf_counter()
-    q_np, k_np, v_np = synth.make_qkv(2, N=N)
+    q_np, k_np, v_np = synth.make_qkv(2, N=N) if args.workload == 2 else synth.make_qkv(args.workload)
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     q = torch.from_numpy(q_np).to(dev)
@@ -264,8 +277,8 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": args.fmt, "data": "synthetic (seeded SplitMix64/Box-Muller N(0,1) fp16)",
-        "config": {"workload": f"kernel sweep point B={B} H={H} N={N} D={D} {args.fmt}"
+        "vs_baseline": None, "dtype": args.fmt, "data": DATA_NOTES[args.workload],
+        "config": {"workload": f"{WORKLOAD_NAMES[args.workload]} B={B} H={H} N={N} D={D} {args.fmt}"
                                f"{' direct-p' if args.direct_p else ''} {'causal' if causal else 'non-causal'}",
                    "B": B, "H": H, "N": N, "D": D, "causal": causal, "format": args.fmt,
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
@@ -280,7 +293,7 @@ def main():
     # accuracy against a plain PyTorch fp32 reference on sampled rows of three heads
     torch.cuda.synchronize()
     heads = [0, B * H // 2 + 1, B * H - 1]
-    rows = torch.arange(0, N, N // 256, device=dev)
+    rows = torch.arange(0, N, max(1, N // 256), device=dev)
     ref = torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D))  # non-causal
     if not causal:
         got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
