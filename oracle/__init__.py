@@ -65,6 +65,8 @@ def lib():
         L.orc_attn_fwd.restype = I
         L.orc_attn_fwd_direct_p.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I64, P, P, D, I]
         L.orc_attn_fwd_direct_p.restype = I
+        L.orc_attn_fwd_lse.argtypes = [I, I, P, P, P, P, P, P, I, I, I, I, I, F, P, I64, P, P, P, P, D, I]
+        L.orc_attn_fwd_lse.restype = I
         L.orc_attn_ref_f64.argtypes = [P, P, P, I, I, I, I, I, D, P, I64, P, I]
         L.orc_attn_ref_f64.restype = I
         L.orc_max_threads.argtypes = []; L.orc_max_threads.restype = I
@@ -103,11 +105,13 @@ def quant(role: int, fmt: int, x: np.ndarray):
 
 
 def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, rows=None, want_slack=False,
-             delta=2.0 ** -14, nthreads=0, direct_p=False):
+             delta=2.0 ** -14, nthreads=0, direct_p=False, want_lse=False):
     """q, k, v: (codes, scales) tuples from quant(); shape = (B,H,N,D). direct_p selects the
     Direct-P normaliser (MXFP4 operands only).
 
-    Returns out float32 ([B,H,N,D], or [len(rows), D]) and, if want_slack, per-row slack."""
+    Returns out float32 ([B,H,N,D], or [len(rows), D]); if want_slack, then per-row slack; if
+    want_lse, then the per-row log-sum-exp (float64, [B*H*N] or [len(rows)]) and, with
+    want_slack too, its per-row slack."""
     if direct_p and fmt != MXFP4:
         raise ValueError("Direct-P takes MXFP4 operands")
     B, H, N, D = shape
@@ -122,6 +126,15 @@ def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, rows=None, want_sl
         rp, nr = _p(rows), len(rows)
         nslack = len(rows)
     slack = np.zeros(nslack, np.float64) if want_slack else None
+    if want_lse:
+        lse = np.zeros(nslack, np.float64)
+        lse_slack = np.zeros(nslack, np.float64) if want_slack else None
+        rc = lib().orc_attn_fwd_lse(fmt, int(direct_p), *[_p(a) for a in arrs], B, H, N, D, int(causal),
+                                    float(sm_scale), rp, nr, _p(out), _p(lse), _p(slack) if want_slack else None,
+                                    _p(lse_slack) if want_slack else None, float(delta), int(nthreads))
+        if rc != 0:
+            raise ValueError(f"orc_attn_fwd_lse failed ({rc})")
+        return (out, slack, lse, lse_slack) if want_slack else (out, lse)
     tail = (B, H, N, D, int(causal), float(sm_scale), rp, nr, _p(out), _p(slack) if want_slack else None,
             float(delta), int(nthreads))
     if direct_p:

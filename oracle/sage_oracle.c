@@ -356,7 +356,7 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
                          const uint8_t* v_codes, const uint8_t* v_scales,
                          int B, int H, int N, int D, int causal, float sm_scale,
                          const int64_t* rows, int64_t n_rows, float* out,
-                         double* slack, double delta, int nthreads) {
+                         double* slack, double* lse, double* lse_slack, double delta, int nthreads) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out) return ORC_ERR_ARG;
   if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return ORC_ERR_ARG;
   if (!valid_fmt(fmt)) return ORC_ERR_ARG;
@@ -386,6 +386,7 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
     float* O = (float*)calloc((size_t)D, sizeof(float));
     double* tile_t = (double*)malloc(sizeof(double) * (size_t)ntiles);
     double* tile_amb = (double*)malloc(sizeof(double) * (size_t)ntiles);
+    double* tile_pamb = (double*)malloc(sizeof(double) * (size_t)ntiles);
     int ntile_used = 0;
     float m = -INFINITY, l = 0.0f;
     float x[ORC_KV_TILE], E[ORC_KV_TILE];
@@ -457,7 +458,7 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
         O[d] = alpha * O[d] + w * acc;
       }
       m = mn;
-      if (slack) {
+      if (slack || lse_slack) {
         double vmax[ORC_KV_TILE];
         float P2[ORC_KV_TILE];
         for (int s = 0; s < ORC_KV_TILE; ++s) {
@@ -484,11 +485,17 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
           else second = fmaxf(second, E[s]);
         }
         if (top >= 0 && (double)second < 1.0 - delta) exact[top] = 1;
-        double amb = 0.0;
-        for (int b = 0; b < ORC_KV_TILE / blk; ++b)
+        double amb = 0.0, pamb = 0.0;
+        double ones[ORC_KV_TILE];
+        for (int s = 0; s < ORC_KV_TILE; ++s) ones[s] = 1.0;
+        for (int b = 0; b < ORC_KV_TILE / blk; ++b) {
           amb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], vmax + b * blk, exact + b * blk, delta);
+          /* with unit weights: how far the tile's sum of dequantised P can move (Direct-P lse) */
+          if (direct_p) pamb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], ones, exact + b * blk, delta);
+        }
         tile_t[ntile_used] = t;
         tile_amb[ntile_used] = amb;
+        tile_pamb[ntile_used] = pamb;
         ++ntile_used;
       }
     }
@@ -499,9 +506,18 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
       for (int u = 0; u < ntile_used; ++u) sl += exp(tile_t[u] - (double)m) * tile_amb[u];
       slack[r] = sl / ((double)Kp * (double)l);
     }
+    /* the row's log-sum-exp: l sums E (Direct-P: the dequantised P) in the frame of m */
+    if (lse) lse[r] = (double)m + log((double)l);
+    if (lse_slack) {
+      /* |d ln l| <= |dl| / l; only Direct-P's l depends on rounding decisions */
+      double sl = 0.0;
+      for (int u = 0; u < ntile_used; ++u) sl += exp(tile_t[u] - (double)m) * tile_pamb[u];
+      lse_slack[r] = sl / (double)l;
+    }
     free(O);
     free(tile_t);
     free(tile_amb);
+    free(tile_pamb);
   }
   return ORC_OK;
 }
@@ -513,7 +529,7 @@ int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
                  const int64_t* rows, int64_t n_rows, float* out,
                  double* slack, double delta, int nthreads) {
   return attn_fwd_impl(fmt, 0, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, B, H, N, D, causal,
-                       sm_scale, rows, n_rows, out, slack, delta, nthreads);
+                       sm_scale, rows, n_rows, out, slack, NULL, NULL, delta, nthreads);
 }
 
 int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
@@ -523,7 +539,18 @@ int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
                           const int64_t* rows, int64_t n_rows, float* out,
                           double* slack, double delta, int nthreads) {
   return attn_fwd_impl(ORC_MXFP4, 1, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, B, H, N, D,
-                       causal, sm_scale, rows, n_rows, out, slack, delta, nthreads);
+                       causal, sm_scale, rows, n_rows, out, slack, NULL, NULL, delta, nthreads);
+}
+
+int orc_attn_fwd_lse(int fmt, int direct_p, const uint8_t* q_codes, const uint8_t* q_scales,
+                     const uint8_t* k_codes, const uint8_t* k_scales,
+                     const uint8_t* v_codes, const uint8_t* v_scales,
+                     int B, int H, int N, int D, int causal, float sm_scale,
+                     const int64_t* rows, int64_t n_rows, float* out, double* lse,
+                     double* slack, double* lse_slack, double delta, int nthreads) {
+  if (!lse || (direct_p && fmt != ORC_MXFP4)) return ORC_ERR_ARG;
+  return attn_fwd_impl(fmt, direct_p ? 1 : 0, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, B, H, N,
+                       D, causal, sm_scale, rows, n_rows, out, slack, lse, lse_slack, delta, nthreads);
 }
 
 int orc_attn_ref_f64(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -105,6 +105,18 @@ int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
                           const int64_t* rows, int64_t n_rows, float* out,
                           double* slack, double delta, int nthreads);
 
+/* ---- the forward with each row's log-sum-exp (plain or Direct-P): lse[r] = m + ln l, with m
+ * the row's maximum scaled score and l the normaliser the output row is divided by (the sum of
+ * E = exp(x - m), or with Direct-P of the dequantised P, each tile weighted by exp(t - m)).
+ * lse_slack (may be NULL): per row, a bound on how far lse may move because a P rounding
+ * decision lies within delta of its boundary (0 except with Direct-P). ---- */
+int orc_attn_fwd_lse(int fmt, int direct_p, const uint8_t* q_codes, const uint8_t* q_scales,
+                     const uint8_t* k_codes, const uint8_t* k_scales,
+                     const uint8_t* v_codes, const uint8_t* v_scales,
+                     int B, int H, int N, int D, int causal, float sm_scale,
+                     const int64_t* rows, int64_t n_rows, float* out, double* lse,
+                     double* slack, double* lse_slack, double delta, int nthreads);
+
 /* ---- unquantised reference: softmax(c Q K^T) V in double from fp16 inputs ---- */
 int orc_attn_ref_f64(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      int B, int H, int N, int D, int causal, double sm_scale,
