@@ -18,7 +18,7 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
-           "sage_fp4_status_string"]
+           "sage_fp4_attn_fwd_lse", "sage_fp4_status_string"]
 
 _lib = None
 
@@ -48,6 +48,8 @@ def lib():
         L.sage_fp4_attn_fwd.restype = I
         L.sage_fp4_attn_fwd_direct_p.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, I, P]
         L.sage_fp4_attn_fwd_direct_p.restype = I
+        L.sage_fp4_attn_fwd_lse.argtypes = [I, I, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, P]
+        L.sage_fp4_attn_fwd_lse.restype = I
         L.sage_fp4_status_string.argtypes = [I]; L.sage_fp4_status_string.restype = C.c_char_p
         _lib = L
     return _lib
@@ -88,6 +90,12 @@ def sage_fp4_attn_fwd_direct_p(qc, qs, kc, ks, vc, vs, B, H, N, D, causal, sm_sc
                                stream_ptr) -> int:
     return lib().sage_fp4_attn_fwd_direct_p(qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal), float(sm_scale),
                                             out_ptr, out_dtype, stream_ptr)
+
+
+def sage_fp4_attn_fwd_lse(fmt, direct_p, qc, qs, kc, ks, vc, vs, B, H, N, D, causal, sm_scale, out_ptr,
+                          out_dtype, lse_ptr, stream_ptr) -> int:
+    return lib().sage_fp4_attn_fwd_lse(fmt, int(direct_p), qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal),
+                                       float(sm_scale), out_ptr, out_dtype, lse_ptr, stream_ptr)
 
 
 def status_string(status: int) -> str:
@@ -146,12 +154,22 @@ def _out_code(out):
     raise TypeError("out must be float16 or float32")
 
 
-def attn_fwd_into(fmt, q, k, v, shape, out, causal=False, sm_scale=0.0, stream=None, direct_p=False):
-    """direct_p=True calls sage_fp4_attn_fwd_direct_p (MXFP4 operands only)."""
+def attn_fwd_into(fmt, q, k, v, shape, out, causal=False, sm_scale=0.0, stream=None, direct_p=False, lse=None):
+    """direct_p=True calls sage_fp4_attn_fwd_direct_p (MXFP4 operands only); a float32 tensor
+    `lse` of B*H*N elements calls sage_fp4_attn_fwd_lse, which also writes each row's
+    log-sum-exp."""
+    import torch
     B, H, N, D = shape
     od = _out_code(out)
     ptrs = [C.c_void_p(t.data_ptr()) for pair in (q, k, v) for t in pair]
-    if direct_p:
+    if lse is not None:
+        _check(lse, torch.float32, "lse")
+        if lse.numel() != B * H * N:
+            raise ValueError("lse must hold B*H*N elements")
+        rc = sage_fp4_attn_fwd_lse(fmt, direct_p, *ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()),
+                                   od, C.c_void_p(lse.data_ptr()), _stream_ptr(stream))
+        what = "sage_fp4_attn_fwd_lse"
+    elif direct_p:
         if fmt != MXFP4:
             raise ValueError("Direct-P takes MXFP4 operands")
         rc = sage_fp4_attn_fwd_direct_p(*ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()), od,

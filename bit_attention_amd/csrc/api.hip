@@ -10,14 +10,15 @@ namespace sage {
 hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* codes, void* scales, hipStream_t st);
 hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
+// lse: NULL, or [B*H*N] fp32 that receives each row's log-sum-exp
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, hipStream_t st);
+                             void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, hipStream_t st);
+                             void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
-                                      float sm_scale, void* out, bool out_f32, hipStream_t st);
+                                      float sm_scale, void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                               void* out, bool out_f32, hipStream_t st);
+                               void* out, bool out_f32, float* lse, hipStream_t st);
 }  // namespace sage
 
 namespace {
@@ -45,7 +46,7 @@ int64_t padded(int N) { return ((int64_t)N + sage::KV_TILE - 1) / sage::KV_TILE 
 
 extern "C" {
 
-int sage_fp4_version(void) { return 300; }
+int sage_fp4_version(void) { return 400; }
 
 int sage_fp4_kv_tile(void) { return sage::KV_TILE; }
 
@@ -101,6 +102,20 @@ static float scale_or_default(float sm_scale, int D) {
   return sm_scale > 0.0f ? sm_scale : (float)(1.0 / __builtin_sqrt((double)D));
 }
 
+// One attention launch of any format; lse may be NULL (validated by the callers).
+static int attn_any(int fmt, bool direct_p, const void* const* ptrs, int B, int H, int N, int D, int causal,
+                    float sm_scale, void* out, int out_dtype, float* lse, void* stream) {
+  const float c = scale_or_default(sm_scale, D);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool f32 = out_dtype == SAGE_OUT_F32, cz = causal != 0;
+  const int BH = B * H;
+  const hipError_t e = direct_p                  ? sage::launch_attn_mxfp4_direct_p(ptrs, BH, N, D, cz, c, out, f32, lse, st)
+                       : fmt == SAGE_FMT_NVFP4   ? sage::launch_attn_nvfp4(ptrs, BH, N, D, cz, c, out, f32, lse, st)
+                       : fmt == SAGE_FMT_MXFP4   ? sage::launch_attn_mxfp4(ptrs, BH, N, D, cz, c, out, f32, lse, st)
+                                                 : sage::launch_attn_mx4_pv8(ptrs, BH, N, D, cz, c, out, f32, lse, st);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                       const void* k_scales, const void* v_codes, const void* v_scales, int B, int H, int N,
                       int D, int causal, float sm_scale, void* out, int out_dtype, void* stream) {
@@ -108,13 +123,7 @@ int sage_fp4_attn_fwd(int fmt, const void* q_codes, const void* q_scales, const 
   const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
   const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
   if (chk != SAGE_OK) return chk;
-  const float c = scale_or_default(sm_scale, D);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool f32 = out_dtype == SAGE_OUT_F32, cz = causal != 0;
-  const hipError_t e = fmt == SAGE_FMT_NVFP4   ? sage::launch_attn_nvfp4(ptrs, B * H, N, D, cz, c, out, f32, st)
-                       : fmt == SAGE_FMT_MXFP4 ? sage::launch_attn_mxfp4(ptrs, B * H, N, D, cz, c, out, f32, st)
-                                               : sage::launch_attn_mx4_pv8(ptrs, B * H, N, D, cz, c, out, f32, st);
-  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+  return attn_any(fmt, false, ptrs, B, H, N, D, causal, sm_scale, out, out_dtype, nullptr, stream);
 }
 
 int sage_fp4_attn_fwd_direct_p(const void* q_codes, const void* q_scales, const void* k_codes,
@@ -124,11 +133,19 @@ int sage_fp4_attn_fwd_direct_p(const void* q_codes, const void* q_scales, const 
   const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
   const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
   if (chk != SAGE_OK) return chk;
-  const float c = scale_or_default(sm_scale, D);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e =
-      sage::launch_attn_mxfp4_direct_p(ptrs, B * H, N, D, causal != 0, c, out, out_dtype == SAGE_OUT_F32, st);
-  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+  return attn_any(SAGE_FMT_MXFP4, true, ptrs, B, H, N, D, causal, sm_scale, out, out_dtype, nullptr, stream);
+}
+
+int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void* q_scales, const void* k_codes,
+                          const void* k_scales, const void* v_codes, const void* v_scales, int B, int H, int N,
+                          int D, int causal, float sm_scale, void* out, int out_dtype, float* lse, void* stream) {
+  if (!valid_fmt(fmt) || (direct_p != 0 && fmt != SAGE_FMT_MXFP4)) return SAGE_ERR_ENUM;
+  const void* ptrs[6] = {q_codes, q_scales, k_codes, k_scales, v_codes, v_scales};
+  const int chk = check_attn(ptrs, B, H, N, D, out, out_dtype);
+  if (chk != SAGE_OK) return chk;
+  if (!lse) return SAGE_ERR_NULL;
+  if (!aligned16(lse)) return SAGE_ERR_ALIGN;
+  return attn_any(fmt, direct_p != 0, ptrs, B, H, N, D, causal, sm_scale, out, out_dtype, lse, stream);
 }
 
 const char* sage_fp4_status_string(int status) {

@@ -95,7 +95,8 @@ template <int D, bool CAUSAL, bool OUT_F32, bool DIRECT_P, bool PV8>
 __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out,
+    float* __restrict__ lse) {
   static_assert(!(PV8 && DIRECT_P), "Direct-P is defined for MXFP4 P");
   constexpr int MX_NT = 64 * mx_waves<D>(), MX_BQ = 16 * mx_waves<D>();
   constexpr int KROW = D / 2 + 16;        // K code row pitch (bytes)
@@ -362,6 +363,8 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
   if (qi < N) {
     const float inv = 1.0f / L;
     const int64_t row = bh * N + qi;
+    // the row's log-sum-exp (Direct-P: of the rounded P), ln(2^R * L): L sums E in R's frame
+    if (lse && g == 0) lse[row] = (R + __builtin_amdgcn_logf(L)) * 0.6931471805599453f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const v4f o = O[dt] * inv;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
 }
 
 template <int D, bool CAUSAL, bool F32, bool DP, bool PV8>
-static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
+static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, float* lse, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   constexpr int BQ = 16 * mx_waves<D>();
   const int nqt = (N + BQ - 1) / BQ;
@@ -385,15 +388,15 @@ static void launch_mx(const void* const* p, int BH, int N, float k2, void* out, 
   const int cgroup = causal_group(BH, Np * D * (PV8 ? 3 : 2) / 2 + Np * D / 16);
   attn_mxfp4_kernel<D, CAUSAL, F32, DP, PV8><<<dim3(nqt * BH), dim3(64 * mx_waves<D>()), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, cgroup, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nqt * BH, cgroup, k2, out, lse);
 }
 
 template <bool DP, bool PV8>
 static hipError_t launch_mx_any(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                                void* out, bool out_f32, hipStream_t st) {
+                                void* out, bool out_f32, float* lse, hipStream_t st) {
   const float k2 = sm_scale * 1.4426950408889634f;
 #define SAGE_MX_CASE(DD, CC, FF) \
-  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF, DP, PV8>(ptrs, BH, N, k2, out, st);
+  if (D == DD && causal == CC && out_f32 == FF) launch_mx<DD, CC, FF, DP, PV8>(ptrs, BH, N, k2, out, lse, st);
   SAGE_MX_CASE(64, false, false) SAGE_MX_CASE(64, false, true) SAGE_MX_CASE(64, true, false)
   SAGE_MX_CASE(64, true, true) SAGE_MX_CASE(128, false, false) SAGE_MX_CASE(128, false, true)
   SAGE_MX_CASE(128, true, false) SAGE_MX_CASE(128, true, true)
@@ -402,18 +405,18 @@ static hipError_t launch_mx_any(const void* const* ptrs, int BH, int N, int D, b
 }
 
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, hipStream_t st) {
-  return launch_mx_any<false, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+                             void* out, bool out_f32, float* lse, hipStream_t st) {
+  return launch_mx_any<false, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, lse, st);
 }
 
 hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
-                                      float sm_scale, void* out, bool out_f32, hipStream_t st) {
-  return launch_mx_any<true, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+                                      float sm_scale, void* out, bool out_f32, float* lse, hipStream_t st) {
+  return launch_mx_any<true, false>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, lse, st);
 }
 
 hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                               void* out, bool out_f32, hipStream_t st) {
-  return launch_mx_any<false, true>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, st);
+                               void* out, bool out_f32, float* lse, hipStream_t st) {
+  return launch_mx_any<false, true>(ptrs, BH, N, D, causal, sm_scale, out, out_f32, lse, st);
 }
 
 }  // namespace sage

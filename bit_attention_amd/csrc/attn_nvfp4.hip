@@ -137,7 +137,8 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out) {
+    int N, int64_t Np, int nqt, int nwork, int cgroup, float k2, void* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int KC = D / 8;        // 16-byte chunks per K-hat row (16 or 8)
   constexpr int CB = D / 4;        // code bytes each thread stages per tile, for K and for V
   constexpr int CW = CB / 4;       // ... in dwords (8 codes each; two dwords per 16-block)
@@ -307,7 +308,9 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     }
   }
 
-  // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of its query in each group
+  // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of its query in each group.
+  // lse (when given): the row's log-sum-exp of the scaled scores, ln(2^R * l2 / 2688), since l2
+  // sums P2 = 2688 E in the frame of the reference R (log2 units)
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const float L = xg_sum(st[a].l2);
@@ -315,6 +318,8 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     if (qi < N) {
       const float inv = 1.0f / L;
       const int64_t row = bh * N + qi;
+      if (lse && g == 0)
+        lse[row] = (st[a].R + __builtin_amdgcn_logf(L) - LOG2_2688) * 0.6931471805599453f;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const v4f o = st[a].O[dt] * inv;
@@ -331,21 +336,21 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
 }
 
 template <int D, bool CAUSAL, bool F32>
-static void launch_nv(const void* const* p, int BH, int N, float k2, void* out, hipStream_t st) {
+static void launch_nv(const void* const* p, int BH, int N, float k2, void* out, float* lse, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + NV_BQ - 1) / NV_BQ;
   const int nwork = nqt * BH;
   const int cgroup = causal_group(BH, Np * D * 9 / 8);  // K and V: codes + E4M3 scales
   attn_nvfp4_kernel<D, CAUSAL, F32><<<dim3(nwork), dim3(64 * NV_WAVES), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
-      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, cgroup, k2, out);
+      (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, cgroup, k2, out, lse);
 }
 
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, hipStream_t st) {
+                             void* out, bool out_f32, float* lse, hipStream_t st) {
   const float k2 = sm_scale * 1.4426950408889634f;  // scores in log2 units
 #define SAGE_NV_CASE(DD, CC, FF) \
-  if (D == DD && causal == CC && out_f32 == FF) launch_nv<DD, CC, FF>(ptrs, BH, N, k2, out, st);
+  if (D == DD && causal == CC && out_f32 == FF) launch_nv<DD, CC, FF>(ptrs, BH, N, k2, out, lse, st);
   SAGE_NV_CASE(64, false, false) SAGE_NV_CASE(64, false, true) SAGE_NV_CASE(64, true, false)
   SAGE_NV_CASE(64, true, true) SAGE_NV_CASE(128, false, false) SAGE_NV_CASE(128, false, true)
   SAGE_NV_CASE(128, true, false) SAGE_NV_CASE(128, true, true)

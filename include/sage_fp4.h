@@ -116,6 +116,27 @@ int sage_fp4_attn_fwd_direct_p(const void* q_codes, const void* q_scales,
                                int B, int H, int N, int D, int causal, float sm_scale,
                                void* out, int out_dtype, void* stream);
 
+/* Attention forward that also returns each row's softmax normaliser as a log-sum-exp: the
+ * statistic of the online softmax the pages fuse with the P quantisation (DeepTech article,
+ * section on FP4 inference and its hardware implementation), kept for a backward pass of the
+ * pages' 8-bit training attention (abstract, second contribution) and for merging partial
+ * results. Same operands, output, validation and errors as sage_fp4_attn_fwd (direct_p == 0) or
+ * sage_fp4_attn_fwd_direct_p (direct_p != 0, which needs fmt = SAGE_FMT_MXFP4, else
+ * SAGE_ERR_ENUM), plus:
+ *   lse  device pointer, fp32 [B,H,N], 16-byte aligned, caller-owned; NULL is SAGE_ERR_NULL.
+ *        lse[b,h,i] = ln sum_j exp(x_ij) over the keys j visible to query i, x = sm_scale * S
+ *        with S from the quantised Q and K, i.e. the normaliser the output row was divided by;
+ *        with direct_p, ln sum over tiles of exp(t) * (sum of the tile's dequantised P values),
+ *        t the tile's row maximum of x.
+ * For key ranges that are unions of whole 128-key tiles, results computed separately over each
+ * range r merge exactly (up to FP32 rounding) as out = sum_r exp(lse_r - lse) out_r with
+ * lse = ln sum_r exp(lse_r), because P is quantised per tile. One kernel launch. */
+int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void* q_scales,
+                          const void* k_codes, const void* k_scales,
+                          const void* v_codes, const void* v_scales,
+                          int B, int H, int N, int D, int causal, float sm_scale,
+                          void* out, int out_dtype, float* lse, void* stream);
+
 /* Static description of a status code. */
 const char* sage_fp4_status_string(int status);
 

@@ -62,6 +62,12 @@ int main(void) {
                           SAGE_OUT_F16, NULL) == SAGE_ERR_SHAPE);
   CHECK(sage_fp4_attn_fwd_direct_p(fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, mis, SAGE_OUT_F16,
                                    NULL) == SAGE_ERR_ALIGN);
+  CHECK(sage_fp4_attn_fwd_lse(SAGE_FMT_NVFP4, 0, fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, fake,
+                              SAGE_OUT_F32, NULL, NULL) == SAGE_ERR_NULL);
+  CHECK(sage_fp4_attn_fwd_lse(SAGE_FMT_NVFP4, 1, fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, fake,
+                              SAGE_OUT_F32, (float*)fake, NULL) == SAGE_ERR_ENUM);
+  CHECK(sage_fp4_attn_fwd_lse(SAGE_FMT_MXFP4, 1, fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, fake,
+                              SAGE_OUT_F32, (float*)mis, NULL) == SAGE_ERR_ALIGN);
   for (s = -6; s <= 0; ++s) CHECK(sage_fp4_status_string(s) != NULL && strlen(sage_fp4_status_string(s)) > 0);
   CHECK(strcmp(sage_fp4_status_string(SAGE_OK), "ok") == 0);
 
