@@ -141,21 +141,21 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + MX_BQ - 1) / KV_TILE + 1) : ntiles;
 
-  // Staging: each thread owns a few 16-byte pieces of the K and V codes, the scale bytes of one
-  // key and one V channel's four scale bytes. The next tile's pieces are loaded into registers
-  // once the current tile's scores are consumed, so the loads are in flight during the PV
-  // products and the barrier.
+  // Staging: each thread owns a few 16-byte pieces of the K and V codes and exactly one K and one
+  // V scale byte, so every wave does the same staging work before the barrier. The next tile's
+  // pieces are loaded into registers once the current tile's scores are consumed, so the loads
+  // are in flight during the PV products and the barrier.
   constexpr int TPK = D / 32;  // 16-byte pieces per key row
   constexpr int KPIECES = KV_TILE * TPK;
   constexpr int KPT = (KPIECES + MX_NT - 1) / MX_NT;
   constexpr int VPR = VB / 16;  // 16-byte pieces per V channel row
-  static_assert(MX_NT >= KV_TILE && MX_NT >= D, "one thread per key and per V channel for the scales");
+  static_assert(MX_NT == KV_TILE * NBD && MX_NT == 4 * D, "one K and one V scale byte per thread and tile");
   const uint8_t* kc_h = kc + bh * N * (D / 2);
   const uint8_t* ks_h = ks + bh * N * NBD;
   const int64_t vrow_bytes = PV8 ? Np : Np / 2;
   const uint8_t* vc_h = vc + bh * D * vrow_bytes;   // uniform base; per-thread offsets are 32-bit
   const uint8_t* vs_h = vs + bh * D * (Np / 32);
-  const unsigned vs_off = (unsigned)(tid * (Np / 32));
+  const unsigned vs_off = (unsigned)((tid >> 2) * (Np / 32) + (tid & 3));  // channel tid/4, block tid%4
   uint4 rk[KPT], rv[VPT];
   unsigned rks = 0, rvs = 0;
 #pragma unroll
@@ -171,10 +171,9 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
         if (j < N) rk[i] = *reinterpret_cast<const uint4*>(kc_h + (int64_t)j * (D / 2) + 16 * (e % TPK));
       }
     }
-    if (tid < KV_TILE) {
-      const int jj = kt * KV_TILE + tid;
-      if (NBD == 4) rks = jj < N ? *reinterpret_cast<const unsigned*>(ks_h + (int64_t)jj * 4) : 0x7F7F7F7Fu;
-      else rks = jj < N ? *reinterpret_cast<const unsigned short*>(ks_h + (int64_t)jj * 2) : 0x7F7Fu;
+    {
+      const int jj = kt * KV_TILE + tid / NBD;  // key of this thread's scale byte (block tid % NBD)
+      rks = jj < N ? ks_h[(int64_t)kt * KV_TILE * NBD + tid] : 0x7Fu;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
         rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)((e / VPR) * vrow_bytes + 16 * (e % VPR)) +
                                                 (unsigned)kt * (unsigned)VB);
     }
-    if (tid < D) rvs = *reinterpret_cast<const unsigned*>(vs_h + vs_off + (unsigned)kt * 4u);
+    rvs = vs_h[vs_off + (unsigned)kt * 4u];
   };
   prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
@@ -193,19 +192,18 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       const int e = tid + MX_NT * i, key = e / TPK;
       if (e < KPIECES) *reinterpret_cast<uint4*>(sKc + (PV8 ? pv8_rho(key) : key) * KROW + 16 * (e % TPK)) = rk[i];
     }
-    if (tid < KV_TILE) {
-      const int r = PV8 ? pv8_rho(tid) : tid;  // LDS row of this key
-#pragma unroll
-      for (int b = 0; b < NBD; ++b) sKs[((r & 15) * 4 + b) * 8 + (r >> 4)] = (uint8_t)(rks >> (8 * b));
+    {
+      const int r = PV8 ? pv8_rho(tid / NBD) : tid / NBD;  // LDS row of this thread's key
+      sKs[((r & 15) * 4 + tid % NBD) * 8 + (r >> 4)] = (uint8_t)rks;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int e = tid + MX_NT * i;
       if (e < VPIECES) *reinterpret_cast<uint4*>(sVc + (e / VPR) * VROW + 16 * (e % VPR)) = rv[i];
     }
-    if (tid < D) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) sVs[((tid & 15) * 4 + b) * 8 + (tid >> 4)] = (uint8_t)(rvs >> (8 * b));
+    {
+      const int d = tid >> 2;  // channel d's block tid & 3
+      sVs[((d & 15) * 4 + (tid & 3)) * 8 + (d >> 4)] = (uint8_t)rvs;
     }
     __syncthreads();
 
