@@ -19,7 +19,7 @@
 //     current tile is computed, then dequantised into LDS between two barriers.
 //   - MFMA operands are read from LDS two MFMA pairs ahead through a ring of three fragments
 //     (a scheduling barrier per step stops the compiler from hoisting further, which would
-//     cost registers: the kernel sits at the 256-VGPR limit of two waves per SIMD).
+//     cost registers: the kernel sits close to the 256-VGPR limit of two waves per SIMD).
 //   - each group computes S^T = K Q^T for its 16 queries: after 8 subtiles a lane holds the 32
 //     scores of one query at keys 16t + 4g + i, exactly the slot order the quantisation kernel
 //     stores V in, so P's 1x16 blocks are lane-local (two per lane per tile), their maxima come
@@ -27,8 +27,8 @@
 //   - the row max needs two cross-lane swaps (permlane16/32); everything else is lane-local.
 //   - accumulator reference: O and l are kept relative to the current tile's maximum, so the
 //     MFMA accumulates P2-hat * V-hat directly; one multiply rescales them per tile. A tile whose
-//     maximum lies more than 2^64 below the running maximum is dropped for that row (relative
-//     weight below 2^-64).
+//     weight relative to the running maximum is below 2^-64 (its maximum more than 64 below it
+//     in log2 units) is dropped for that row.
 //   - workgroups are ordered so that each XCD walks through whole heads (K/V stay in its L2).
 #include "device.h"
 
