@@ -78,16 +78,19 @@ def torch_reference_rows(q, k, v, heads, rows, sm_scale):
     return torch.cat(outs).double().cpu().numpy()
 
 
-def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15.0):
+def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15.0, gpu_out=None):
     """The oracle, as it stands, on a bounded sample of the same workload: head after head, the
     quantisation of the head's Q, K and V and the attention of every 4th query row of it, until
     about `seconds_target` seconds of CPU time; the quantisation is charged pro rata to the rows
-    computed. Throughput by the same 4*N*D-per-row count as the GPU figure."""
+    computed. Throughput by the same 4*N*D-per-row count as the GPU figure. If `gpu_out` (the
+    non-causal GPU output, [B*H, N, D] on the host) is given, the largest |GPU - oracle| over the
+    sampled rows is returned as well."""
     import oracle as orc
     B, H, N, D = shape
     nthreads = orc.max_threads()
     rows = np.arange(0, N, 4, dtype=np.int64)
     total_t, total_rows, heads = 0.0, 0, 0
+    max_abs = 0.0
     for bh in range(B * H):
         b, h = divmod(bh, H)
         t0 = time.perf_counter()
@@ -99,6 +102,8 @@ def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15
         out = orc.attn_fwd(fmt, Q, K, V, (1, 1, N, D), rows=rows, nthreads=nthreads, direct_p=direct_p)
         t_attn = time.perf_counter() - t0
         assert np.all(np.isfinite(out))
+        if gpu_out is not None:
+            max_abs = max(max_abs, float(np.abs(gpu_out[bh][rows].astype(np.float64) - out).max()))
         total_t += t_attn + t_quant * len(rows) / N
         total_rows += len(rows)
         heads += 1
@@ -109,7 +114,7 @@ def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15
             "sample": f"{heads} heads x {len(rows)} query rows (every 4th row; non-causal, N={N}, "
                       f"D={D}), format {fmt}{' Direct-P' if direct_p else ''}: per head the quantisation of Q, K, V (charged "
                       f"{len(rows)}/{N}) and the attention rows; {total_t:.1f} s of CPU time",
-            "seconds": total_t}
+            "seconds": total_t, "max_abs_gpu_vs_oracle": max_abs if gpu_out is not None else None}
 
 
 def cpu_one_thread_small(fmt, direct_p=False):
@@ -355,7 +360,14 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample ...")
         ofmt = {bnd.NVFP4: 0, bnd.MXFP4: 1, bnd.MX4_PV8: 2}[fmt]
-        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p)
+        gpu_out = None
+        if not causal:  # the sample is non-causal; the GPU output of the last timed step
+            bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=False, direct_p=args.direct_p)
+            torch.cuda.synchronize()
+            gpu_out = out.view(B * H, N, D).float().cpu().numpy()
+        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p, gpu_out=gpu_out)
+        # fp16 output: the GPU side is rounded once more (half an fp16 ulp, ~1e-3 at |o| ~ 2)
+        res["max_abs_vs_oracle_f16_out"] = res["cpu_baseline"]["max_abs_gpu_vs_oracle"]
         res["cpu_one_thread_small_workload"] = cpu_one_thread_small(ofmt, args.direct_p)
     else:
         res["cpu_baseline"] = None
