@@ -325,6 +325,22 @@ def main():
         torch.cuda.synchronize()
         res["attn_alone_ms"] = a0.elapsed_time(a1) / 10
         res["attn_alone_tops"] = flops / (res["attn_alone_ms"] * 1e-3) / 1e12
+        # the same step captured once as a HIP graph and replayed (no host launch gaps between
+        # its four kernels); the library allocates, synchronises and memsets nothing
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        warm(graph.replay, torch)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(20):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = g0.elapsed_time(g1) / 20
+        res["graph_value"] = flops / (res["graph_ms_per_step"] * 1e-3) / 1e12
+        del graph
         extras = {}
         for name, f2, c2, dp in (("nvfp4_causal", bnd.NVFP4, True, False),
                                  ("mxfp4_noncausal", bnd.MXFP4, False, False),
