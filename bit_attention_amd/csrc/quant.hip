@@ -116,11 +116,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   scales[b] = (uint8_t)sb;
 }
 
-// V: one workgroup per (batch*head, run of `tpw` consecutive 128-token tiles). Each tile, a
+// V: one workgroup per (batch*head, run of `tpw` <= 4 consecutive 128-token tiles). Each tile, a
 // contiguous D*256-byte run of fp16, is loaded into registers with 16-byte loads while the
-// previous tile is encoded, then staged in LDS (row pitch D+8 halves keeps 16-byte alignment). Item (channel d, block) gathers its values in slot order from LDS; the blocks of a
-// channel sit in consecutive lanes, so their code bytes form one contiguous run per channel, and
-// every fourth lane writes four blocks' scale bytes as one dword. Token positions >= N are zero.
+// previous tile is encoded, then staged in LDS (row pitch D+8 halves keeps 16-byte alignment).
+// Item (channel d, block) gathers its values in slot order from LDS; the blocks of a channel sit
+// in consecutive lanes, so their code bytes form one contiguous run per channel. Four blocks'
+// scale bytes are gathered into one dword per tile, and after the run the lane of block 0 stores
+// the channel's scale bytes of all the run's tiles together. Token positions >= N are zero.
 // FMT 0: NVFP4 (16-slot blocks, E4M3 scale of amax/6); 1: MXFP4 (32-slot blocks, E8M0 scale;
 // codes are the E2M1 value nearest the exact quotient, ties to even); 2: MXFP8 (32-slot blocks;
 // codes the E4M3 value nearest x / 2^X, ties to even, clamped to +-448; sign the input's).
@@ -137,6 +139,10 @@ __global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restr
   const int ntiles = (int)(Np / KV_TILE);
   const int kt0 = blockIdx.x * tpw, kt1 = min(ntiles, kt0 + tpw);
   uint4 pre[PPT];
+  // scale dwords of this thread's items, one per tile of the run (tpw <= 4, see v_tiles_per_wg),
+  // stored once at the end so that each channel's scale bytes of the run leave as one burst
+  constexpr int ITEMS = D * NB / 256;
+  unsigned sacc[ITEMS][4] = {};
   // the tile's fp16 pieces into registers (token positions >= N read as zero)
   auto load = [&](int kt) {
     const int tok0 = kt * KV_TILE, ntok = min(KV_TILE, N - tok0);
@@ -149,6 +155,7 @@ __global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restr
   };
   load(kt0);
   for (int kt = kt0; kt < kt1; ++kt) {
+    const int tix = kt - kt0;
     __syncthreads();  // the previous tile's LDS reads are complete
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -158,7 +165,9 @@ __global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restr
     __syncthreads();
     if (kt + 1 < kt1) load(kt + 1);  // in flight while this tile is encoded and stored
     static_assert((D * NB) % 256 == 0, "every lane of a quad takes part in each pass");
-    for (int it = threadIdx.x; it < D * NB; it += blockDim.x) {
+#pragma unroll
+    for (int ii = 0; ii < ITEMS; ++ii) {
+      const int it = threadIdx.x + 256 * ii;
       const int d = it / NB, blk = it % NB;
       float v[BLK];
 #pragma unroll
@@ -194,9 +203,35 @@ __global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restr
       }
       // four consecutive blocks' scale bytes, gathered into the lane of the first
       const unsigned s1 = __shfl_down(sb, 1, 4), s2 = __shfl_down(sb, 2, 4), s3 = __shfl_down(sb, 3, 4);
-      if ((blk & 3) == 0)
-        *reinterpret_cast<unsigned*>(scales + (bh * D + d) * (Np / BLK) + (int64_t)kt * NB + blk) =
-            sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+      const unsigned wv = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u == tix) sacc[ii][u] = wv;
+    }
+  }
+  // the run's scale bytes of each channel are contiguous: NB bytes per tile. NVFP4 (NB = 8):
+  // the lane of blocks 0..3 takes the partner dword (blocks 4..7) from the lane 4 above it.
+  const int nt = kt1 - kt0;
+#pragma unroll
+  for (int ii = 0; ii < ITEMS; ++ii) {
+    const int it = threadIdx.x + 256 * ii;
+    const int d = it / NB, blk = it % NB;
+    unsigned w[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (NB == 8) {
+        const unsigned hi = __shfl_down(sacc[ii][u], 4, 8);
+        w[2 * u] = sacc[ii][u]; w[2 * u + 1] = hi;
+      } else {
+        w[u] = sacc[ii][u];
+      }
+    }
+    if (blk == 0) {
+      uint8_t* dst = scales + (bh * D + d) * (Np / BLK) + (int64_t)kt0 * NB;
+      const int nw = nt * NB / 4;  // dwords to store
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < nw) reinterpret_cast<unsigned*>(dst)[q] = w[q];
     }
   }
 }
