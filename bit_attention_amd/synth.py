@@ -7,7 +7,7 @@ the top 53 bits, standard normals by the Box-Muller transform, rounded to fp16 (
 even). Element i of stream `seed` is mix(seed + (i + 1) * 0x9E3779B97F4A7C15 mod 2^64), so any
 sub-range can be generated independently of numpy's or torch's own generators.
 
-Workloads (seed = 1000 * workload + tensor id; Q=0, K=1, V=2, channel offsets=3,
+Workloads (seed = 1000 * workload + tensor id; Q=0, K=1, V=2, channel offsets=3, dO=4,
 outlier mask = 10 + tensor, outlier sign = 20 + tensor):
   1 tiny:      B=1 H=2  N=256   D=64,  Q,K,V ~ N(0,1)
   2 sweep:     B=4 H=32 N=4096  D=128 (N also 1024..16384), Q,K,V ~ N(0,1)
@@ -123,3 +123,17 @@ def make_qkv(wl: int, B=None, H=None, N=None, D=None, heads=None):
             x[u] = flat.reshape(N, D)
         out.append(x.reshape(B, H, N, D) if heads is None else x.reshape(1, len(hs), N, D))
     return tuple(out)
+
+
+def make_do(wl: int, B=None, H=None, N=None, D=None, heads=None):
+    """The output gradient dO ~ N(0,1), float16 [B,H,N,D], of workload `wl` (stream id 4; the
+    same head slicing as make_qkv)."""
+    base = 1 if wl == 5 else wl
+    cfg = WORKLOADS[wl]
+    B = B or cfg["B"]; H = H or cfg["H"]; N = N or cfg["N"]; D = D or cfg["D"]
+    hs = list(range(B * H)) if heads is None else [int(h) for h in heads]
+    per = N * D
+    x = np.empty((len(hs), N, D), np.float16)
+    for u, bh in enumerate(hs):
+        x[u] = normal_f16(1000 * base + 4, per, start=bh * per).reshape(N, D)
+    return x.reshape(B, H, N, D) if heads is None else x.reshape(1, len(hs), N, D)
