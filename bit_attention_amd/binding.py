@@ -2,7 +2,7 @@
 of the computation runs in the library's HIP kernels. PyTorch supplies device memory and streams.
 
 The functions named like the C entry points take raw pointers/ints; the convenience wrappers
-(`quant`, `attn_fwd`) allocate outputs with torch and pass the current stream."""
+(`quant`, `attn_fwd`, `attn_bwd_into`) take torch tensors and pass the current stream."""
 from __future__ import annotations
 
 import ctypes as C
@@ -15,10 +15,11 @@ NVFP4, MXFP4, MX4_PV8 = 0, 1, 2
 ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
 STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR_HEAD_DIM",
-          -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP"}
+          -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP", -7: "SAGE_ERR_WORKSPACE"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
-           "sage_fp4_attn_fwd_lse", "sage_fp4_status_string"]
+           "sage_fp4_attn_fwd_lse", "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
+           "sage_fp4_status_string"]
 
 _lib = None
 
@@ -50,6 +51,10 @@ def lib():
         L.sage_fp4_attn_fwd_direct_p.restype = I
         L.sage_fp4_attn_fwd_lse.argtypes = [I, I, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, P]
         L.sage_fp4_attn_fwd_lse.restype = I
+        L.sage_fp4_attn_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        L.sage_fp4_attn_bwd_workspace_bytes.restype = S
+        L.sage_fp4_attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, P, I, P, S, P]
+        L.sage_fp4_attn_bwd.restype = I
         L.sage_fp4_status_string.argtypes = [I]; L.sage_fp4_status_string.restype = C.c_char_p
         _lib = L
     return _lib
@@ -96,6 +101,17 @@ def sage_fp4_attn_fwd_lse(fmt, direct_p, qc, qs, kc, ks, vc, vs, B, H, N, D, cau
                           out_dtype, lse_ptr, stream_ptr) -> int:
     return lib().sage_fp4_attn_fwd_lse(fmt, int(direct_p), qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal),
                                        float(sm_scale), out_ptr, out_dtype, lse_ptr, stream_ptr)
+
+
+def sage_fp4_attn_bwd_workspace_bytes(B, H, N, D) -> int:
+    return lib().sage_fp4_attn_bwd_workspace_bytes(B, H, N, D)
+
+
+def sage_fp4_attn_bwd(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D, causal, sm_scale,
+                      dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr, ws_bytes, stream_ptr) -> int:
+    return lib().sage_fp4_attn_bwd(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D, int(causal),
+                                   float(sm_scale), dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr, ws_bytes,
+                                   stream_ptr)
 
 
 def status_string(status: int) -> str:
@@ -190,3 +206,37 @@ def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, out_dtype=None, st
     dt = torch.float32 if out_dtype is None else out_dtype
     out = torch.empty(shape, dtype=dt, device=q[0].device)
     return attn_fwd_into(fmt, q, k, v, shape, out, causal, sm_scale, stream, direct_p)
+
+
+def alloc_bwd_workspace(B, H, N, D, device="cuda"):
+    import torch
+    n = sage_fp4_attn_bwd_workspace_bytes(B, H, N, D)
+    if n == 0:
+        raise SageError(-2, "sage_fp4_attn_bwd_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False, sm_scale=0.0, stream=None):
+    """q, k: (codes, scales) pairs of the forward's Q and K; v, o, do: fp16 [B,H,N,D]; lse: fp32
+    with B*H*N elements; dq, dk, dv: outputs of one dtype (fp16 or fp32); workspace: uint8 of at
+    least sage_fp4_attn_bwd_workspace_bytes bytes. Calls sage_fp4_attn_bwd."""
+    import torch
+    for t, n in ((v, "v"), (o, "o"), (do, "do")):
+        _check(t, torch.float16, n)
+    _check(lse, torch.float32, "lse")
+    B, H, N, D = v.shape
+    if o.shape != v.shape or do.shape != v.shape or lse.numel() != B * H * N:
+        raise ValueError("o and do must match v's shape and lse must hold B*H*N elements")
+    od = _out_code(dq)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, dq.dtype, n)
+        if t.shape != v.shape:
+            raise ValueError(f"{n} must have v's shape")
+    ptrs = [C.c_void_p(t.data_ptr()) for pair in (q, k) for t in pair]
+    rc = sage_fp4_attn_bwd(fmt, *ptrs, C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()),
+                           C.c_void_p(do.data_ptr()), C.c_void_p(lse.data_ptr()), B, H, N, D, causal, sm_scale,
+                           C.c_void_p(dq.data_ptr()), C.c_void_p(dk.data_ptr()), C.c_void_p(dv.data_ptr()), od,
+                           C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_ptr(stream))
+    if rc != 0:
+        raise SageError(rc, "sage_fp4_attn_bwd")
+    return dq, dk, dv

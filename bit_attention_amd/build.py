@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage_fp4.so")
-SOURCES = ["api.hip", "quant.hip", "attn_nvfp4.hip", "attn_mxfp4.hip"]
+SOURCES = ["api.hip", "quant.hip", "attn_nvfp4.hip", "attn_mxfp4.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 VALU forms are disabled for every device compilation.

@@ -19,6 +19,10 @@ hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, in
                                       float sm_scale, void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                                void* out, bool out_f32, float* lse, hipStream_t st);
+hipError_t launch_attn_bwd(bool mx, const void* qc, const void* qs, const void* kc, const void* ks, const void* v,
+                           const void* o, const void* dout, const float* lse, int BH, int N, int D, bool causal,
+                           float c, void* dq, void* dk, void* dv, bool out_f32, void* ws, hipStream_t st);
+size_t bwd_workspace_bytes(int64_t BH, int N, int D);
 }  // namespace sage
 
 namespace {
@@ -46,7 +50,7 @@ int64_t padded(int N) { return ((int64_t)N + sage::KV_TILE - 1) / sage::KV_TILE 
 
 extern "C" {
 
-int sage_fp4_version(void) { return 400; }
+int sage_fp4_version(void) { return 500; }
 
 int sage_fp4_kv_tile(void) { return sage::KV_TILE; }
 
@@ -148,6 +152,33 @@ int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void
   return attn_any(fmt, direct_p != 0, ptrs, B, H, N, D, causal, sm_scale, out, out_dtype, lse, stream);
 }
 
+size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D) {
+  if (check_shape(B, H, N, D) != SAGE_OK) return 0;
+  return sage::bwd_workspace_bytes((int64_t)B * H, N, D);
+}
+
+int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes, const void* k_scales,
+                      const void* v, const void* o, const void* dout, const float* lse, int B, int H, int N, int D,
+                      int causal, float sm_scale, void* dq, void* dk, void* dv, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!valid_fmt(fmt) || (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32)) return SAGE_ERR_ENUM;
+  const void* in[11] = {q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : in)
+    if (!p) return SAGE_ERR_NULL;
+  if (!workspace) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  for (const void* p : in)
+    if (!aligned16(p)) return SAGE_ERR_ALIGN;
+  if (!aligned16(workspace)) return SAGE_ERR_ALIGN;
+  if (workspace_bytes < sage::bwd_workspace_bytes((int64_t)B * H, N, D)) return SAGE_ERR_WORKSPACE;
+  const hipError_t e = sage::launch_attn_bwd(fmt != SAGE_FMT_NVFP4, q_codes, q_scales, k_codes, k_scales, v, o, dout,
+                                             lse, B * H, N, D, causal != 0, scale_or_default(sm_scale, D), dq, dk,
+                                             dv, out_dtype == SAGE_OUT_F32, workspace,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 const char* sage_fp4_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "ok";
@@ -157,6 +188,7 @@ const char* sage_fp4_status_string(int status) {
     case SAGE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SAGE_ERR_ENUM: return "bad format, role or output type";
     case SAGE_ERR_HIP: return "HIP runtime error at launch";
+    case SAGE_ERR_WORKSPACE: return "workspace smaller than the call needs";
     default: return "unknown status";
   }
 }

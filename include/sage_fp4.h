@@ -1,5 +1,6 @@
 /*
- * sage_fp4.h — C ABI of libsage_fp4.so: microscaling-FP4 attention forward on AMD MI355X (gfx950).
+ * sage_fp4.h — C ABI of libsage_fp4.so: microscaling-FP4 attention forward, and its 8-bit
+ * backward, on AMD MI355X (gfx950).
  *
  * The operation (SageAttention3, "Microscaling FP4 Attention for Inference and An Exploration
  * of 8-Bit Training", arXiv 2505.11594; abstract, and the DeepTech article's sections on the two
@@ -66,7 +67,8 @@ typedef enum {
   SAGE_ERR_HEAD_DIM = -3, /* D not in {64, 128} */
   SAGE_ERR_ALIGN = -4,    /* a pointer is not 16-byte aligned */
   SAGE_ERR_ENUM = -5,     /* bad format, role or output type */
-  SAGE_ERR_HIP = -6       /* the HIP runtime reported an error for the launch */
+  SAGE_ERR_HIP = -6,      /* the HIP runtime reported an error for the launch */
+  SAGE_ERR_WORKSPACE = -7 /* the workspace is smaller than the call needs */
 } sage_status_t;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -139,6 +141,47 @@ int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void
                           const void* v_codes, const void* v_scales,
                           int B, int H, int N, int D, int causal, float sm_scale,
                           void* out, int out_dtype, float* lse, void* stream);
+
+/* Bytes of device workspace sage_fp4_attn_bwd needs for this shape (0 for invalid arguments).
+ * About 4*B*H*N*D + 3*B*H*D*Np64 bytes, Np64 = ceil(N/64)*64. */
+size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D);
+
+/* 8-bit attention backward (SageAttention3's SageBwd: DeepTech article, sections on the third
+ * difficulty and on INT8 attention for training; the rit.work page on FP4 FlashAttention-4,
+ * section on what was done, for the forward handing the backward its quantised Q and K, their
+ * scales and the normaliser). Gradients of the attention whose forward is sage_fp4_attn_fwd_lse,
+ * with c = sm_scale (<= 0 selects fl32(1/sqrt(D))) and the same causal mask:
+ *   S = Q^ K^T from the FP4 codes (exact), P = exp(c S - lse), dP = dO V^T (16-bit operands,
+ *   fp32 accumulation), D_i = sum_d dO_id O_id, dS = P (dP - D),
+ *   dV = P^T dO, dK = c dS^T Q^, dQ = c dS K^ on INT8 operands. Each INT8 operand carries one
+ *   fp32 scale per row (the index not contracted) and per block of 64 contraction indices:
+ *   P^T and dS^T per (key, 64-query block), dS per (query, 64-key block), dO, Q^ and K^ per
+ *   (channel, 64-token block); the 64 values x of a block with a = max|x| get the scale
+ *   fl32(a/127) and codes rne(fl32(x * fl32(127/a))) in [-127, 127]. Codes that lie within a
+ *   few ulp of a rounding boundary may round either way (fp32 summation order).
+ * Arguments:
+ *   fmt                  format of the forward's Q and K codes (NVFP4; MXFP4 and MX4_PV8 both
+ *                        have MXFP4 Q and K); codes and scales as from sage_fp4_quant.
+ *   v, o, dout           fp16 [B,H,N,D]: V, the forward's output and the output gradient.
+ *   lse                  fp32 [B,H,N] from sage_fp4_attn_fwd_lse.
+ *   dq, dk, dv           [B,H,N,D] outputs, fp16 or fp32 per out_dtype, fully written.
+ *   workspace            device memory of at least sage_fp4_attn_bwd_workspace_bytes(B,H,N,D)
+ *                        bytes (workspace_bytes), 16-byte aligned, caller-owned; its contents
+ *                        on entry are ignored, and on return it holds, at 256-byte aligned
+ *                        offsets in this order: Q^ and K^ as bf16 [B,H,N,D]; the INT8 codes of
+ *                        Q^, K^ and dO, each [B,H,D,Np64] with the tokens of every 64-token
+ *                        block in slot order (slot 16g + 4s + i holds token 16s + 4g + i, zero
+ *                        past N); their scales, fp32 [B,H,D,Np64/64] each; D, fp32 [B,H,N].
+ *                        Calls that share a workspace must not overlap.
+ * Errors as for the forward; a workspace below the needed size is SAGE_ERR_WORKSPACE. Five
+ * kernel launches on `stream` (three operand preparations, dK/dV, dQ); no atomics, so results
+ * are deterministic. */
+int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales,
+                      const void* k_codes, const void* k_scales,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      int B, int H, int N, int D, int causal, float sm_scale,
+                      void* dq, void* dk, void* dv, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* sage_fp4_status_string(int status);

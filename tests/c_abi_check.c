@@ -68,7 +68,32 @@ int main(void) {
                               SAGE_OUT_F32, (float*)fake, NULL) == SAGE_ERR_ENUM);
   CHECK(sage_fp4_attn_fwd_lse(SAGE_FMT_MXFP4, 1, fake, fake, fake, fake, fake, fake, 1, 1, 16, 64, 0, 0.0f, fake,
                               SAGE_OUT_F32, (float*)mis, NULL) == SAGE_ERR_ALIGN);
-  for (s = -6; s <= 0; ++s) CHECK(sage_fp4_status_string(s) != NULL && strlen(sage_fp4_status_string(s)) > 0);
+  /* backward: workspace size (B=2 H=3 N=300 D=128: Np64 = 320, 5 blocks) and validation */
+  {
+    const size_t qh = 2 * 3 * 300 * 128 * 2, i8 = 2 * 3 * 128 * 320, sc = 2 * 3 * 128 * 5 * 4, dl = 2 * 3 * 300 * 4;
+#define A256(x) (((x) + 255) / 256 * 256)
+    CHECK(sage_fp4_attn_bwd_workspace_bytes(2, 3, 300, 128) == 2 * A256(qh) + 3 * A256(i8) + 3 * A256(sc) + A256(dl));
+#undef A256
+    CHECK(sage_fp4_attn_bwd_workspace_bytes(2, 3, 300, 96) == 0);
+    size_t need = sage_fp4_attn_bwd_workspace_bytes(1, 1, 16, 64);
+    CHECK(need > 0);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
+                            64, 0, 0.0f, fake, fake, fake, SAGE_OUT_F32, fake, need - 1, NULL) == SAGE_ERR_WORKSPACE);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, NULL, (const float*)fake, 1, 1, 16,
+                            64, 0, 0.0f, fake, fake, fake, SAGE_OUT_F32, fake, need, NULL) == SAGE_ERR_NULL);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
+                            64, 0, 0.0f, fake, fake, fake, SAGE_OUT_F32, NULL, need, NULL) == SAGE_ERR_NULL);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_MXFP4, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
+                            64, 0, 0.0f, fake, mis, fake, SAGE_OUT_F16, fake, need, NULL) == SAGE_ERR_ALIGN);
+    CHECK(sage_fp4_attn_bwd(3, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16, 64, 0, 0.0f,
+                            fake, fake, fake, SAGE_OUT_F16, fake, need, NULL) == SAGE_ERR_ENUM);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_MX4_PV8, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
+                            64, 0, 0.0f, fake, fake, fake, 2, fake, need, NULL) == SAGE_ERR_ENUM);
+    CHECK(sage_fp4_attn_bwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
+                            80, 0, 0.0f, fake, fake, fake, SAGE_OUT_F32, fake, need, NULL) == SAGE_ERR_HEAD_DIM);
+  }
+  for (s = -7; s <= 0; ++s) CHECK(sage_fp4_status_string(s) != NULL && strlen(sage_fp4_status_string(s)) > 0);
+  CHECK(strcmp(sage_fp4_status_string(SAGE_ERR_WORKSPACE), "unknown status") != 0);
   CHECK(strcmp(sage_fp4_status_string(SAGE_OK), "ok") == 0);
 
   if (failures) return 1;

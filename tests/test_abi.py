@@ -118,3 +118,35 @@ def test_library_does_not_link_the_oracle():
     assert "orc_" not in out
     deps = subprocess.run(["readelf", "-d", bnd.LIB_PATH], capture_output=True, text=True).stdout
     assert "sage_oracle" not in deps
+
+
+def test_bwd_workspace_and_validation():
+    """Backward entry point: documented workspace size, and every argument check (no launch)."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    B, H, N, D = 2, 3, 300, 128
+    np64, nb = 320, 5
+    want = (2 * a256(B * H * N * D * 2) + 3 * a256(B * H * D * np64) + 3 * a256(B * H * D * nb * 4)
+            + a256(B * H * N * 4))
+    assert bnd.sage_fp4_attn_bwd_workspace_bytes(B, H, N, D) == want
+    assert bnd.sage_fp4_attn_bwd_workspace_bytes(B, H, N, 96) == 0
+    assert bnd.sage_fp4_attn_bwd_workspace_bytes(1, 1024, 1 << 20, 64) == 0
+    need = bnd.sage_fp4_attn_bwd_workspace_bytes(1, 1, 16, 64)
+    b = bnd.sage_fp4_attn_bwd
+    ok = [FAKE] * 8
+
+    def call(fmt=0, ptrs=ok, D=64, outs=(FAKE, FAKE, FAKE), od=1, ws=FAKE, wsb=need, N=16):
+        return b(fmt, *ptrs, 1, 1, N, D, 0, 0.0, *outs, od, ws, wsb, None)
+
+    assert call(wsb=need - 1) == -7
+    assert call(ws=None) == -1
+    assert call(ptrs=ok[:7] + [None]) == -1
+    assert call(outs=(FAKE, None, FAKE)) == -1
+    assert call(ptrs=ok[:4] + [MIS] + ok[5:]) == -4
+    assert call(outs=(FAKE, FAKE, MIS)) == -4
+    assert call(ws=MIS) == -4
+    assert call(fmt=3) == -5
+    assert call(od=2) == -5
+    assert call(D=96) == -3
+    assert call(N=0) == -2
+    assert bnd.status_string(-7) != bnd.status_string(99)

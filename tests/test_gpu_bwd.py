@@ -1,0 +1,204 @@
+"""GPU parity of the 8-bit attention backward (sage_fp4_attn_bwd) against the oracle
+(oracle/bwd.py).
+
+Both sides get the same O and lse: the oracle forward's output (fp16) and log-sum-exp (fp32),
+so the comparison isolates the backward. Each side quantises Q and K for itself (those codes are
+bit-exact, checked here too). The bar, per element of dQ, dK and dV:
+    |gpu - oracle| <= slack + 1e-4 * mag (+ 2^-11 |oracle| for fp16 outputs)
+where the oracle's slack bounds the effect of P and dS codes that lie within float32 rounding of
+a rounding boundary and mag is the sum of the magnitudes of the element's terms (float32 sums
+and scale products differ from the oracle's float64 by far less than 1e-4 of it).
+
+The workspace the call leaves behind is compared bit-exactly: the bf16 Q^ and K^, the INT8
+codes of Q^, K^ and dO with their fp32 scales (slot order undone), and D = rowsum(dO * O) within
+float32 rounding.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from oracle import bwd as obwd
+from bit_attention_amd import synth
+from helpers import say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SLOT64 = np.array([16 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3) for p in range(64)])
+
+
+def _inputs(fmt, B, H, N, D, causal, wl=1):
+    q, k, v = synth.make_qkv(wl, B=B, H=H, N=N, D=D)
+    do = synth.make_do(wl, B=B, H=H, N=N, D=D)
+    fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
+    Q = orc.quant(orc.ROLE_Q, fq, q)
+    K = orc.quant(orc.ROLE_K, fq, k)
+    V = orc.quant(orc.ROLE_V, fmt, v)
+    o, lse = orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), causal=causal, want_lse=True)
+    return q, k, v, do, Q, K, o.astype(np.float16), lse.astype(np.float32).reshape(B, H, N)
+
+
+def _gpu_bwd(fmt, q, k, v, o, do, lse, causal, out_f32=True, keep_ws=False):
+    import torch
+    from bit_attention_amd import binding as bnd
+    B, H, N, D = v.shape
+    fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
+    Qg = bnd.quant(to_gpu(q), 0, fq)
+    Kg = bnd.quant(to_gpu(k), 1, fq)
+    dt = torch.float32 if out_f32 else torch.float16
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=dt, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    ws.fill_(0xA5)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), to_gpu(o), to_gpu(do), to_gpu(lse), *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    res = [t.float().cpu().numpy().astype(np.float64) for t in outs]
+    codes = [t.cpu().numpy() for pair in (Qg, Kg) for t in pair]
+    return res, codes, (ws.cpu().numpy() if keep_ws else None)
+
+
+def _check_grads(got, ref, bd, f16_out=False, heads=None):
+    names = ("dq", "dk", "dv")
+    for t in range(3):
+        g, r = got[t], ref[t]
+        bound = bd["slack"][t] + 1e-4 * bd["mag"][t] + 1e-30
+        if f16_out:
+            bound = bound + 2.0 ** -11 * np.abs(r) + 2.0 ** -24
+        if heads is not None:
+            sel = tuple(np.array(x) for x in zip(*heads))
+            g, r, bound = g[sel], r[sel], bound[sel]
+        assert np.all(np.isfinite(g)), names[t]
+        err = np.abs(g - r)
+        worst = float(np.max(err / bound))
+        say(f"  {names[t]}: max err {err.max():.3e}, max err/bound {worst:.3f}, max |ref| {np.abs(r).max():.3e}")
+        assert worst <= 1.0, names[t]
+
+
+def _ws_views(ws, B, H, N, D):
+    def a256(x):
+        return (x + 255) // 256 * 256
+    BH, Np = B * H, -(-N // 64) * 64
+    nb = Np // 64
+    sizes = [BH * N * D * 2] * 2 + [BH * D * Np] * 3 + [BH * D * nb * 4] * 3 + [BH * N * 4]
+    offs = np.cumsum([0] + [a256(s) for s in sizes])
+    raw = [ws[offs[i]:offs[i] + sizes[i]] for i in range(len(sizes))]
+    bf = [(r.view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(B, H, N, D) for r in raw[:2]]
+    i8 = [r.view(np.int8).reshape(B, H, D, Np) for r in raw[2:5]]
+    sc = [r.view(np.float32).reshape(B, H, D, nb) for r in raw[5:8]]
+    dl = raw[8].view(np.float32).reshape(B, H, N)
+    return bf, i8, sc, dl
+
+
+CASES = [
+    (orc.NVFP4, 1, 2, 256, 64, False),
+    (orc.NVFP4, 2, 2, 200, 128, True),
+    (orc.MXFP4, 1, 2, 130, 128, False),
+    (orc.MXFP4, 1, 3, 192, 64, True),
+    (orc.MX4_PV8, 1, 2, 100, 64, True),
+    (orc.NVFP4, 1, 1, 1, 64, False),
+    (orc.MXFP4, 1, 1, 65, 128, True),
+]
+
+
+@pytest.mark.parametrize("fmt,B,H,N,D,causal", CASES)
+def test_bwd_matches_oracle(fmt, B, H, N, D, causal):
+    say(f"bwd parity fmt={fmt} B={B} H={H} N={N} D={D} causal={causal}")
+    q, k, v, do, Q, K, o, lse = _inputs(fmt, B, H, N, D, causal)
+    got, codes, ws = _gpu_bwd(fmt, q, k, v, o, do, lse, causal, keep_ws=True)
+    for a, b in zip(codes, (Q[0], Q[1], K[0], K[1])):
+        assert np.array_equal(a.reshape(b.shape), b)
+    ref, bd = obwd.attn_bwd(fmt, Q, K, v, o, do, lse, causal=causal, want_bounds=True)
+    say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
+    _check_grads(got, ref, bd)
+
+    # the workspace: bf16 Q^, K^; INT8 codes and scales of Q^, K^, dO; D
+    fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
+    bf, i8, sc, dl = _ws_views(ws, B, H, N, D)
+    xs = (orc.dequant(fq, *Q), orc.dequant(fq, *K), do.astype(np.float64))
+    for t in range(2):
+        assert np.array_equal(bf[t], xs[t].astype(np.float32))
+    for t in range(3):
+        for b in range(B):
+            for h in range(H):
+                codes_o, scales_o = obwd.q8_tokens(xs[t][b, h])
+                Np = codes_o.shape[1]
+                slots = i8[t][b, h].reshape(D, Np // 64, 64)
+                tok = np.empty_like(slots)
+                tok[:, :, SLOT64] = slots
+                assert np.array_equal(tok.reshape(D, Np).astype(np.int32), codes_o), (t, b, h)
+                assert np.array_equal(sc[t][b, h].astype(np.float64), scales_o), (t, b, h)
+    dref = np.sum(do.astype(np.float64) * o.astype(np.float64), axis=3)
+    gsum = D * 2.0 ** -24 * np.sum(np.abs(do.astype(np.float64) * o.astype(np.float64)), axis=3)
+    assert np.all(np.abs(dl - dref) <= gsum + 1e-30)
+
+
+def test_bwd_fp16_outputs_and_determinism():
+    fmt, B, H, N, D, causal = orc.NVFP4, 1, 2, 160, 128, True
+    say("bwd fp16 outputs and repeat determinism")
+    q, k, v, do, Q, K, o, lse = _inputs(fmt, B, H, N, D, causal)
+    ref, bd = obwd.attn_bwd(fmt, Q, K, v, o, do, lse, causal=causal, want_bounds=True)
+    got16, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal, out_f32=False)
+    _check_grads(got16, ref, bd, f16_out=True)
+    a, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal)
+    b, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_sm_scale():
+    fmt, B, H, N, D, causal = orc.MXFP4, 1, 2, 128, 64, False
+    say("bwd with an explicit sm_scale")
+    import torch
+    from bit_attention_amd import binding as bnd
+    q, k, v, do = *synth.make_qkv(1, B=B, H=H, N=N, D=D), synth.make_do(1, B=B, H=H, N=N, D=D)
+    Q = orc.quant(0, fmt, q)
+    K = orc.quant(1, fmt, k)
+    o, lse = orc.attn_fwd(fmt, Q, K, orc.quant(2, fmt, v), (B, H, N, D), sm_scale=0.05, want_lse=True)
+    o = o.astype(np.float16)
+    lse = lse.astype(np.float32).reshape(B, H, N)
+    ref, bd = obwd.attn_bwd(fmt, Q, K, v, o, do, lse, sm_scale=0.05, want_bounds=True)
+    Qg, Kg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt)
+    outs = [torch.empty((B, H, N, D), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), to_gpu(o), to_gpu(do), to_gpu(lse), *outs, ws, sm_scale=0.05)
+    torch.cuda.synchronize()
+    _check_grads([t.cpu().numpy().astype(np.float64) for t in outs], ref, bd)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_full_size_sampled_heads(causal):
+    """B4 H32 N4096 D128 (NVFP4), the size the benchmark times: every head runs on the GPU with
+    the GPU forward's O and lse, except two heads that get the oracle forward's; those two are
+    checked against the oracle in full."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    B, H, N, D, fmt = 4, 32, 4096, 128, orc.NVFP4
+    heads = [(0, 0), (3, 31)]
+    flat = [b * H + h for b, h in heads]
+    say(f"bwd full size B{B} H{H} N{N} D{D} causal={causal}, oracle heads {heads}")
+    q, k, v = synth.make_qkv(2)
+    do = synth.make_do(2)
+    Qg = bnd.quant(to_gpu(q), 0, fmt)
+    Kg = bnd.quant(to_gpu(k), 1, fmt)
+    Vg = bnd.quant(to_gpu(v), 2, fmt)
+    og = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
+    lg = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    bnd.attn_fwd_into(fmt, Qg, Kg, Vg, (B, H, N, D), og, causal=causal, lse=lg)
+    # the sampled heads: oracle forward on the oracle's own quantisation
+    qs, ks, vs = (x.reshape(B * H, N, D)[flat][None] for x in (q, k, v))
+    Qs, Ks, Vs = orc.quant(0, fmt, qs), orc.quant(1, fmt, ks), orc.quant(2, fmt, vs)
+    o_s, l_s = orc.attn_fwd(fmt, Qs, Ks, Vs, qs.shape, causal=causal, want_lse=True)
+    o_s = o_s.astype(np.float16)
+    l_s = l_s.astype(np.float32).reshape(1, len(flat), N)
+    for u, (b, h) in enumerate(heads):
+        og[b, h] = torch.from_numpy(o_s[0, u]).cuda()
+        lg[b, h] = torch.from_numpy(l_s[0, u]).cuda()
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), og, to_gpu(do), lg, *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    got = [t.reshape(B * H, N, D)[flat].cpu().numpy().astype(np.float64)[None] for t in outs]
+    for t in outs:
+        assert bool(torch.isfinite(t).all())
+    dos = do.reshape(B * H, N, D)[flat][None]
+    ref, bd = obwd.attn_bwd(fmt, Qs, Ks, vs, o_s, dos, l_s, causal=causal, want_bounds=True)
+    say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
+    _check_grads(got, ref, bd)
