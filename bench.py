@@ -184,6 +184,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the post-run extra measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the 8-bit backward instead (sage_fp4_attn_bwd, as its three stages)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -211,6 +213,8 @@ def main():
         B, H, N, D = w["B"], w["H"], w["N"], w["D"]
         args.causal = args.causal or w["causal"]
     shape = (B, H, N, D)
+    if args.backward:
+        return bench_backward(args, shape, fmt, torch, bnd, synth)
     log(f"bench: generating inputs {shape} ...")
     t0 = time.perf_counter()
     q_np, k_np, v_np = synth.make_qkv(2, N=N) if args.workload == 2 else synth.make_qkv(args.workload)
@@ -388,6 +392,117 @@ def main():
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+BWD_METRIC = "8-bit attention bwd TOPS (10·B·H·N²·D/t: the five backward matmuls)"
+INT8_PEAK_TOPS = 5033.0      # MI355X dense INT8 MFMA
+
+
+def bench_backward(args, shape, fmt, torch, bnd, synth):
+    """One step = sage_fp4_attn_bwd over the workload (its three stages, each bracketed by HIP
+    events on the launch stream): operand preparation, dK/dV, dQ. Inputs resident in HBM: the
+    forward's FP4 Q/K codes and its output and log-sum-exp (computed once, untimed), fp16 V and dO.
+    Gradients are written in fp16."""
+    B, H, N, D = shape
+    causal = args.causal
+    wl = args.workload
+    log(f"bench: generating inputs {shape} ...")
+    q_np, k_np, v_np = synth.make_qkv(2, N=N) if wl == 2 else synth.make_qkv(wl)
+    do_np = synth.make_do(2, N=N) if wl == 2 else synth.make_do(wl)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x).to(dev) for x in (q_np, k_np, v_np, do_np))
+    Q = bnd.quant(q, bnd.ROLE_Q, fmt)
+    K = bnd.quant(k, bnd.ROLE_K, fmt)
+    V = bnd.quant(v, bnd.ROLE_V, fmt)
+    o = torch.empty(shape, dtype=torch.float16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    bnd.attn_fwd_into(fmt, Q, K, V, shape, o, causal=causal, lse=lse)
+    grads = [torch.empty(shape, dtype=torch.float16, device=dev) for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(i=None):
+        for s_, stage in enumerate((bnd.BWD_PREP, bnd.BWD_DKDV, bnd.BWD_DQ)):
+            if i is not None:
+                ev[i][s_].record(stream)
+            bnd.attn_bwd_into(fmt, Q, K, v, o, do, lse, *grads, ws, causal=causal, stage=stage)
+        if i is not None:
+            ev[i][3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    st_ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(3)]
+
+    pairs = B * H * N * N / (2 if causal else 1)                 # visible (query, key) pairs, tile-level
+    flops = 10.0 * B * H * N * N * D / (2 if causal else 1)      # dS-side: S, dP, dV, dK, dQ
+    value = flops / (ms_step * 1e-3) / 1e12
+    # the dK/dV kernel: per pair S and dP at 16 bits (4D flops) and dV, dK on INT8 (4D ops)
+    dkdv_ops = 8.0 * D * pairs
+    dkdv_tops = dkdv_ops / (st_ms[1] * 1e-3) / 1e12
+    mixed = 2.0 / (1.0 / FP16_PEAK_TFLOPS + 1.0 / INT8_PEAK_TOPS)
+    kname = f"attn_bwd_dkdv_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
+    roof = {"bound": "mfma", "achieved": dkdv_tops, "peak": mixed, "unit": "TFLOP/s",
+            "frac": dkdv_tops / mixed, "traffic": load_traffic("attn_bwd.hip", kname),
+            "kernel": "bwd_dkdv_kernel (bf16/fp16 MFMA for S and dP, INT8 MFMA for dV and dK; peak "
+                      "= harmonic mean of the 16-bit and INT8 dense peaks, equal op counts)"}
+    res = {
+        "metric": BWD_METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+bf16/fp16", "data": DATA_NOTES[wl] + "; dO ~ N(0,1) fp16",
+        "config": {"workload": f"backward, {WORKLOAD_NAMES[wl]} B={B} H={H} N={N} D={D} {args.fmt} Q/K "
+                               f"{'causal' if causal else 'non-causal'}",
+                   "B": B, "H": H, "N": N, "D": D, "causal": causal, "format": args.fmt, "grad_dtype": "f16"},
+        "prep_ms": st_ms[0], "dkdv_ms": st_ms[1], "dq_ms": st_ms[2],
+        "dq_tops": 6.0 * D * pairs / (st_ms[2] * 1e-3) / 1e12,
+        "flops_counted": flops, "roofline": roof,
+    }
+    torch.cuda.synchronize()
+    # accuracy: gradients of one head against float64 autograd of unquantised attention
+    h0 = B * H - 1
+    import torch as T
+    qh, kh, vh, doh = (T.from_numpy(x.reshape(B * H, N, D)[h0].astype(np.float64)).requires_grad_(x is not do_np)
+                       for x in (q_np, k_np, v_np, do_np))
+    sc = (qh @ kh.T) / np.sqrt(D)
+    if causal:
+        sc = sc.masked_fill(T.ones(N, N, dtype=T.bool).triu(1), float("-inf"))
+    (T.softmax(sc, -1) @ vh * doh).sum().backward()
+    for name, g, r in (("dq", grads[0], qh.grad), ("dk", grads[1], kh.grad), ("dv", grads[2], vh.grad)):
+        a = g.view(B * H, N, D)[h0].double().cpu().numpy().reshape(-1)
+        b = r.numpy().reshape(-1)
+        res[f"cos_sim_{name}_vs_fp64"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_bwd(q_np, k_np, v_np, do_np, shape, fmt, causal)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_bwd(q_np, k_np, v_np, do_np, shape, fmt, causal):
+    """The backward oracle (numpy, INT8 mode) on one head of the workload; its forward O and lse
+    come from the oracle forward first (not timed)."""
+    import oracle as orc
+    from oracle import bwd as obwd
+    B, H, N, D = shape
+    h = B * H - 1
+    qs, ks, vs, dos = (x.reshape(B * H, N, D)[h][None, None] for x in (q_np, k_np, v_np, do_np))
+    fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
+    Qs, Ks = orc.quant(0, fq, qs), orc.quant(1, fq, ks)
+    o, lse = orc.attn_fwd(fmt, Qs, Ks, orc.quant(2, fmt, vs), qs.shape, causal=causal, want_lse=True)
+    t0 = time.perf_counter()
+    obwd.attn_bwd(fmt, Qs, Ks, vs, o.astype(np.float16), dos, lse.astype(np.float32).reshape(1, 1, N),
+                  causal=causal)
+    sec = time.perf_counter() - t0
+    fl = 10.0 * N * N * D / (2 if causal else 1)
+    return {"value": fl / sec / 1e12, "unit": "TOPS", "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"one (batch, head) of the workload: N={N} D={D}, {sec:.1f} s (numpy float64 "
+                      f"with BLAS threads; INT8 decisions in float32)"}
 
 
 if __name__ == "__main__":

@@ -14,12 +14,13 @@ LIB_PATH = os.path.join(HERE, "libsage_fp4.so")
 NVFP4, MXFP4, MX4_PV8 = 0, 1, 2
 ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
 OUT_F16, OUT_F32 = 0, 1
+BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR_HEAD_DIM",
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP", -7: "SAGE_ERR_WORKSPACE"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
            "sage_fp4_attn_fwd_lse", "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
-           "sage_fp4_status_string"]
+           "sage_fp4_attn_bwd_stage", "sage_fp4_status_string"]
 
 _lib = None
 
@@ -55,6 +56,8 @@ def lib():
         L.sage_fp4_attn_bwd_workspace_bytes.restype = S
         L.sage_fp4_attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, P, I, P, S, P]
         L.sage_fp4_attn_bwd.restype = I
+        L.sage_fp4_attn_bwd_stage.argtypes = [I] + L.sage_fp4_attn_bwd.argtypes
+        L.sage_fp4_attn_bwd_stage.restype = I
         L.sage_fp4_status_string.argtypes = [I]; L.sage_fp4_status_string.restype = C.c_char_p
         _lib = L
     return _lib
@@ -112,6 +115,13 @@ def sage_fp4_attn_bwd(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, 
     return lib().sage_fp4_attn_bwd(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D, int(causal),
                                    float(sm_scale), dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr, ws_bytes,
                                    stream_ptr)
+
+
+def sage_fp4_attn_bwd_stage(stage, fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D, causal,
+                            sm_scale, dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr, ws_bytes, stream_ptr) -> int:
+    return lib().sage_fp4_attn_bwd_stage(stage, fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D,
+                                         int(causal), float(sm_scale), dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr,
+                                         ws_bytes, stream_ptr)
 
 
 def status_string(status: int) -> str:
@@ -216,10 +226,12 @@ def alloc_bwd_workspace(B, H, N, D, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False, sm_scale=0.0, stream=None):
+def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False, sm_scale=0.0, stream=None,
+                  stage=None):
     """q, k: (codes, scales) pairs of the forward's Q and K; v, o, do: fp16 [B,H,N,D]; lse: fp32
     with B*H*N elements; dq, dk, dv: outputs of one dtype (fp16 or fp32); workspace: uint8 of at
-    least sage_fp4_attn_bwd_workspace_bytes bytes. Calls sage_fp4_attn_bwd."""
+    least sage_fp4_attn_bwd_workspace_bytes bytes. Calls sage_fp4_attn_bwd, or with `stage`
+    (BWD_PREP, BWD_DKDV, BWD_DQ) sage_fp4_attn_bwd_stage."""
     import torch
     for t, n in ((v, "v"), (o, "o"), (do, "do")):
         _check(t, torch.float16, n)
@@ -232,11 +244,15 @@ def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False,
         _check(t, dq.dtype, n)
         if t.shape != v.shape:
             raise ValueError(f"{n} must have v's shape")
-    ptrs = [C.c_void_p(t.data_ptr()) for pair in (q, k) for t in pair]
-    rc = sage_fp4_attn_bwd(fmt, *ptrs, C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()),
-                           C.c_void_p(do.data_ptr()), C.c_void_p(lse.data_ptr()), B, H, N, D, causal, sm_scale,
-                           C.c_void_p(dq.data_ptr()), C.c_void_p(dk.data_ptr()), C.c_void_p(dv.data_ptr()), od,
-                           C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_ptr(stream))
+    args = [C.c_void_p(t.data_ptr()) for pair in (q, k) for t in pair]
+    args += [C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), C.c_void_p(do.data_ptr()),
+             C.c_void_p(lse.data_ptr()), B, H, N, D, causal, sm_scale, C.c_void_p(dq.data_ptr()),
+             C.c_void_p(dk.data_ptr()), C.c_void_p(dv.data_ptr()), od, C.c_void_p(workspace.data_ptr()),
+             workspace.numel(), _stream_ptr(stream)]
+    if stage is None:
+        rc, what = sage_fp4_attn_bwd(fmt, *args), "sage_fp4_attn_bwd"
+    else:
+        rc, what = sage_fp4_attn_bwd_stage(stage, fmt, *args), "sage_fp4_attn_bwd_stage"
     if rc != 0:
-        raise SageError(rc, "sage_fp4_attn_bwd")
+        raise SageError(rc, what)
     return dq, dk, dv

@@ -19,9 +19,10 @@ hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, in
                                       float sm_scale, void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mx4_pv8(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                                void* out, bool out_f32, float* lse, hipStream_t st);
-hipError_t launch_attn_bwd(bool mx, const void* qc, const void* qs, const void* kc, const void* ks, const void* v,
-                           const void* o, const void* dout, const float* lse, int BH, int N, int D, bool causal,
-                           float c, void* dq, void* dk, void* dv, bool out_f32, void* ws, hipStream_t st);
+hipError_t launch_attn_bwd(int stages, bool mx, const void* qc, const void* qs, const void* kc, const void* ks,
+                           const void* v, const void* o, const void* dout, const float* lse, int BH, int N, int D,
+                           bool causal, float c, void* dq, void* dk, void* dv, bool out_f32, void* ws,
+                           hipStream_t st);
 size_t bwd_workspace_bytes(int64_t BH, int N, int D);
 }  // namespace sage
 
@@ -157,10 +158,11 @@ size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D) {
   return sage::bwd_workspace_bytes((int64_t)B * H, N, D);
 }
 
-int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes, const void* k_scales,
-                      const void* v, const void* o, const void* dout, const float* lse, int B, int H, int N, int D,
-                      int causal, float sm_scale, void* dq, void* dk, void* dv, int out_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// The backward, all stages (mask 7) or one (1 prep, 2 dK/dV, 4 dQ).
+static int attn_bwd_stages(int stages, int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
+                           const void* k_scales, const void* v, const void* o, const void* dout, const float* lse,
+                           int B, int H, int N, int D, int causal, float sm_scale, void* dq, void* dk, void* dv,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_fmt(fmt) || (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32)) return SAGE_ERR_ENUM;
   const void* in[11] = {q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, dq, dk, dv};
   for (const void* p : in)
@@ -172,11 +174,28 @@ int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const 
     if (!aligned16(p)) return SAGE_ERR_ALIGN;
   if (!aligned16(workspace)) return SAGE_ERR_ALIGN;
   if (workspace_bytes < sage::bwd_workspace_bytes((int64_t)B * H, N, D)) return SAGE_ERR_WORKSPACE;
-  const hipError_t e = sage::launch_attn_bwd(fmt != SAGE_FMT_NVFP4, q_codes, q_scales, k_codes, k_scales, v, o, dout,
-                                             lse, B * H, N, D, causal != 0, scale_or_default(sm_scale, D), dq, dk,
-                                             dv, out_dtype == SAGE_OUT_F32, workspace,
+  const hipError_t e = sage::launch_attn_bwd(stages, fmt != SAGE_FMT_NVFP4, q_codes, q_scales, k_codes, k_scales, v,
+                                             o, dout, lse, B * H, N, D, causal != 0, scale_or_default(sm_scale, D),
+                                             dq, dk, dv, out_dtype == SAGE_OUT_F32, workspace,
                                              reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes, const void* k_scales,
+                      const void* v, const void* o, const void* dout, const float* lse, int B, int H, int N, int D,
+                      int causal, float sm_scale, void* dq, void* dk, void* dv, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return attn_bwd_stages(7, fmt, q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, B, H, N, D, causal, sm_scale,
+                         dq, dk, dv, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int sage_fp4_attn_bwd_stage(int stage, int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
+                            const void* k_scales, const void* v, const void* o, const void* dout, const float* lse,
+                            int B, int H, int N, int D, int causal, float sm_scale, void* dq, void* dk, void* dv,
+                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage != SAGE_BWD_PREP && stage != SAGE_BWD_DKDV && stage != SAGE_BWD_DQ) return SAGE_ERR_ENUM;
+  return attn_bwd_stages(1 << stage, fmt, q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, B, H, N, D, causal,
+                         sm_scale, dq, dk, dv, out_dtype, workspace, workspace_bytes, stream);
 }
 
 const char* sage_fp4_status_string(int status) {

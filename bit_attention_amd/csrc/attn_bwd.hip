@@ -29,6 +29,8 @@
 //     stored in that slot order. Two workgroups fit on a CU (57 KB of LDS each at D = 128).
 //   - dQ kernel: the mirror image, one wave per 16 queries looping over 64-key tiles. dQ gets
 //     a kernel of its own instead of atomic adds, so every result is deterministic.
+#include <type_traits>
+
 #include "device.h"
 
 namespace sage {
@@ -208,15 +210,24 @@ __device__ __forceinline__ void stage_tile(int tid, int64_t bh, int N, int Np, i
 }
 
 // Codes of 16 values held by a lane (four subtiles s of four elements i) with a common
-// reciprocal scale r; byte 4s + i of the result is value [s][i].
+// reciprocal scale r; byte 4s + i of the result is the code of value [s][i]. One fma adds
+// 1.5 * 2^23 to the exact product x * r, which rounds it to the nearest integer (ties to even)
+// in the low mantissa bits; the low byte of the result's bits is the two's complement byte of
+// that integer. This is rne(fl32(x * r)) except when x * r lies within half an fp32 ulp of a
+// half-integer, where either rounding is within the contract. |x| <= the block maximum a and
+// r = fl32(127 / a) keep |x * r| below 127.5, so the code lies in [-127, 127] without a clamp.
+// v_perm_b32 gathers four bytes into one dword.
 __device__ __forceinline__ v4i codes16(const float (&x)[4][4], float r) {
+  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
   v4i out;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    int q[4];
+    unsigned w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = (int)fminf(fmaxf(__builtin_rintf(x[s][i] * r), -127.0f), 127.0f);
-    out[s] = pack4(q[0], q[1], q[2], q[3]);
+    for (int i = 0; i < 4; ++i) w[i] = as_u(__builtin_fmaf(x[s][i], r, MAGIC));
+    const unsigned lo = __builtin_amdgcn_perm(w[1], w[0], 0x0C0C0400u);  // bytes w0.b0, w1.b0, 0, 0
+    const unsigned hi = __builtin_amdgcn_perm(w[3], w[2], 0x04000C0Cu);  // bytes 0, 0, w2.b0, w3.b0
+    out[s] = (int)(lo | hi);
   }
   return out;
 }
@@ -241,7 +252,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) f16 sdO[BB * T::RP];
   __shared__ __attribute__((aligned(16))) int8_t sQ8[D * T::CP];
   __shared__ __attribute__((aligned(16))) int8_t sdO8[D * T::CP];
-  __shared__ float sQs[D], sdOs[D], sL[BB], sD[BB];
+  __shared__ float sQs[D], sdOs[D];
+  __shared__ __attribute__((aligned(16))) float sL[BB], sD[BB];
 
   const int nb = Np / BB;
   const int w = xcd_work(blockIdx.x, BH * nb);
@@ -267,7 +279,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   for (int n = 0; n < T::NN; ++n) accK[n] = accV[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  for (int qt = CAUSAL ? kb : 0; qt < nb; ++qt) {
+  // non-causal: each workgroup starts at its own query tile (kb) and wraps around, so the
+  // workgroups of a head do not all read the same tile at the same time
+  const int it0 = CAUSAL ? kb : 0, nit = CAUSAL ? nb - kb : nb;
+  for (int it = 0; it < nit; ++it) {
+    const int qt = CAUSAL ? it0 + it : (kb + it) % nb;
     const int q0 = qt * BB;
     __syncthreads();
     stage_tile<D>(tid, bh, N, Np, q0, qt, qh, dout, q8, q8s, sQ, sdO, sQ8, sQs);
@@ -285,55 +301,64 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     }
     __syncthreads();
 
-    float P[4][4], dS[4][4];
-    float pmax = 0.0f, smax = 0.0f;
+    auto tile = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      float P[4][4], dS[4][4];
+      float pmax = 0.0f, smax = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < 4; ++s) {
+        v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(sQ + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], sc, 0, 0, 0);
-        const v8h b = *reinterpret_cast<const v8h*>(sdO + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, vreg[kk], dp, 0, 0, 0);
+        for (int kk = 0; kk < T::KK; ++kk) {
+          const v8bf a = *reinterpret_cast<const v8bf*>(sQ + (16 * s + col) * T::RP + 32 * kk + 8 * g);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], sc, 0, 0, 0);
+          const v8h b = *reinterpret_cast<const v8h*>(sdO + (16 * s + col) * T::RP + 32 * kk + 8 * g);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, vreg[kk], dp, 0, 0, 0);
+        }
+        const v4f L4 = *reinterpret_cast<const v4f*>(sL + 16 * s + 4 * g);
+        const v4f D4 = *reinterpret_cast<const v4f*>(sD + 16 * s + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qi = q0 + 16 * s + 4 * g + i;
+          const bool ok = FULL || (qi < N && key < N && (!CAUSAL || key <= qi));
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -L4[i]));
+          const float p = ok ? e : 0.0f;
+          P[s][i] = p;
+          dS[s][i] = p * (dp[i] - D4[i]);
+          pmax = fmaxf(pmax, p);
+          smax = fmaxf(smax, fabsf(dS[s][i]));
+        }
       }
+      pmax = xg_max(pmax);
+      smax = xg_max(smax);
+      const v4i aP = codes16(P, pmax > 0.0f ? div_rn(127.0f, pmax) : 0.0f);
+      const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
+      const float sP = pmax > 0.0f ? div_rn(pmax, 127.0f) : 0.0f;
+      const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
+      // the accumulator rows are keys 16 * wave + 4g + i; lane 4g + i holds their scales
+      float rP[4], rS[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ql = 16 * s + 4 * g + i, qi = q0 + ql;
-        const bool ok = qi < N && key < N && (!CAUSAL || key <= qi);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -sL[ql])) : 0.0f;
-        P[s][i] = p;
-        dS[s][i] = p * (dp[i] - sD[ql]);
-        pmax = fmaxf(pmax, p);
-        smax = fmaxf(smax, fabsf(dS[s][i]));
+        rP[i] = __shfl(sP, 4 * g + i);
+        rS[i] = __shfl(sS, 4 * g + i);
       }
-    }
-    pmax = xg_max(pmax);
-    smax = xg_max(smax);
-    const v4i aP = codes16(P, pmax > 0.0f ? div_rn(127.0f, pmax) : 0.0f);
-    const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
-    const float sP = pmax > 0.0f ? div_rn(pmax, 127.0f) : 0.0f;
-    const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
-    // the accumulator rows are keys 16 * wave + 4g + i; lane 4g + i holds their scales
-    float rP[4], rS[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rP[i] = __shfl(sP, 4 * g + i);
-      rS[i] = __shfl(sS, 4 * g + i);
-    }
+      for (int n = 0; n < T::NN; ++n) {
+        const v4i bo = *reinterpret_cast<const v4i*>(sdO8 + (16 * n + col) * T::CP + 16 * g);
+        const v4i bq = *reinterpret_cast<const v4i*>(sQ8 + (16 * n + col) * T::CP + 16 * g);
+        const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, bo, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bq, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const float co = sdOs[16 * n + col], cq = sQs[16 * n + col];
 #pragma unroll
-    for (int n = 0; n < T::NN; ++n) {
-      const v4i bo = *reinterpret_cast<const v4i*>(sdO8 + (16 * n + col) * T::CP + 16 * g);
-      const v4i bq = *reinterpret_cast<const v4i*>(sQ8 + (16 * n + col) * T::CP + 16 * g);
-      const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, bo, v4i{0, 0, 0, 0}, 0, 0, 0);
-      const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bq, v4i{0, 0, 0, 0}, 0, 0, 0);
-      const float co = sdOs[16 * n + col], cq = sQs[16 * n + col];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        accV[n][i] = __builtin_fmaf((float)rv[i], rP[i] * co, accV[n][i]);
-        accK[n][i] = __builtin_fmaf((float)rk[i], rS[i] * cq, accK[n][i]);
+        for (int i = 0; i < 4; ++i) {
+          accV[n][i] = __builtin_fmaf((float)rv[i], rP[i] * co, accV[n][i]);
+          accK[n][i] = __builtin_fmaf((float)rk[i], rS[i] * cq, accK[n][i]);
+        }
       }
-    }
+    };
+    // one variant with the per-element mask: a second, mask-free one for interior tiles
+    // raises the register count past 256
+    tile(std::false_type{});
   }
 
 #pragma unroll
@@ -393,48 +418,57 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   for (int n = 0; n < T::NN; ++n) acc[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  const int kt_end = CAUSAL ? qb + 1 : nb;
-  for (int kt = 0; kt < kt_end; ++kt) {
+  // non-causal: each workgroup starts at its own key tile (qb) and wraps around
+  const int nit = CAUSAL ? qb + 1 : nb;
+  for (int it = 0; it < nit; ++it) {
+    const int kt = CAUSAL ? it : (qb + it) % nb;
     const int k0 = kt * BB;
     __syncthreads();
     stage_tile<D>(tid, bh, N, Np, k0, kt, kh, v, k8, k8s, sK, sV, sK8, sKs);
     __syncthreads();
 
-    float dS[4][4];
-    float smax = 0.0f;
+    const bool full = k0 + BB <= N && qb * BB + BB <= N && (!CAUSAL || kt < qb);
+    auto tile = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      float dS[4][4];
+      float smax = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < 4; ++s) {
+        v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(sK + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], sc, 0, 0, 0);
-        const v8h b = *reinterpret_cast<const v8h*>(sV + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, oreg[kk], dp, 0, 0, 0);
+        for (int kk = 0; kk < T::KK; ++kk) {
+          const v8bf a = *reinterpret_cast<const v8bf*>(sK + (16 * s + col) * T::RP + 32 * kk + 8 * g);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], sc, 0, 0, 0);
+          const v8h b = *reinterpret_cast<const v8h*>(sV + (16 * s + col) * T::RP + 32 * kk + 8 * g);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, oreg[kk], dp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kj = k0 + 16 * s + 4 * g + i;
+          const bool ok = FULL || (kj < N && query < N && (!CAUSAL || kj <= query));
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -Lq));
+          const float p = ok ? e : 0.0f;
+          dS[s][i] = p * (dp[i] - Dq);
+          smax = fmaxf(smax, fabsf(dS[s][i]));
+        }
       }
+      smax = xg_max(smax);
+      const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
+      const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
+      float rS[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = k0 + 16 * s + 4 * g + i;
-        const bool ok = kj < N && query < N && (!CAUSAL || kj <= query);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -Lq)) : 0.0f;
-        dS[s][i] = p * (dp[i] - Dq);
-        smax = fmaxf(smax, fabsf(dS[s][i]));
+      for (int i = 0; i < 4; ++i) rS[i] = __shfl(sS, 4 * g + i);
+#pragma unroll
+      for (int n = 0; n < T::NN; ++n) {
+        const v4i bk = *reinterpret_cast<const v4i*>(sK8 + (16 * n + col) * T::CP + 16 * g);
+        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bk, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const float ck = sKs[16 * n + col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_fmaf((float)r[i], rS[i] * ck, acc[n][i]);
       }
-    }
-    smax = xg_max(smax);
-    const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
-    const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
-    float rS[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rS[i] = __shfl(sS, 4 * g + i);
-#pragma unroll
-    for (int n = 0; n < T::NN; ++n) {
-      const v4i bk = *reinterpret_cast<const v4i*>(sK8 + (16 * n + col) * T::CP + 16 * g);
-      const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bk, v4i{0, 0, 0, 0}, 0, 0, 0);
-      const float ck = sKs[16 * n + col];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_fmaf((float)r[i], rS[i] * ck, acc[n][i]);
-    }
+    };
+    if (full) tile(std::true_type{});
+    else tile(std::false_type{});
   }
 
 #pragma unroll
@@ -452,6 +486,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 namespace {
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
+
+enum { BWD_PREP = 1, BWD_DKDV = 2, BWD_DQ = 4 };
 
 // Workspace layout (offsets in bytes, each 256-aligned; Np = ceil(N/64)*64, nb = Np/64):
 //   Q^ bf16 [BH,N,D] | K^ bf16 [BH,N,D] | Q8, K8, dO8 int8 [BH,D,Np] each |
@@ -480,7 +516,7 @@ BwdWs bwd_ws_layout(int64_t BH, int N, int D) {
 size_t bwd_workspace_bytes(int64_t BH, int N, int D) { return (size_t)bwd_ws_layout(BH, N, D).total; }
 
 template <int D>
-static hipError_t launch_bwd_d(bool mx, const void* qc, const void* qs, const void* kc, const void* ks,
+static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* qs, const void* kc, const void* ks,
                                const void* v, const void* o, const void* dout, const float* lse, int BH, int N,
                                bool causal, float c, void* dq, void* dk, void* dv, bool out_f32, void* ws,
                                hipStream_t st) {
@@ -504,20 +540,24 @@ static hipError_t launch_bwd_d(bool mx, const void* qc, const void* qs, const vo
   const f16* vh = reinterpret_cast<const f16*>(v);
   const f16* oh = reinterpret_cast<const f16*>(o);
   const f16* doh = reinterpret_cast<const f16*>(dout);
-  if (mx) {
-    bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
-    bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
-  } else {
-    bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
-    bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
+  if (stages & BWD_PREP) {
+    if (mx) {
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
+    } else {
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
+    }
+    bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, dl);
   }
-  bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, dl);
   const int grid = BH * nb;
-#define SAGE_BWD_LAUNCH(CZ, F32)                                                                        \
-  do {                                                                                                  \
-    bwd_dkdv_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, lse, dl, N, Np, \
-                                                      BH, c, dk, dv);                                   \
-    bwd_dq_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, k8, k8s, lse, dl, N, Np, BH, c, dq); \
+#define SAGE_BWD_LAUNCH(CZ, F32)                                                                          \
+  do {                                                                                                    \
+    if (stages & BWD_DKDV)                                                                                \
+      bwd_dkdv_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, lse, dl, N, Np, \
+                                                        BH, c, dk, dv);                                   \
+    if (stages & BWD_DQ)                                                                                  \
+      bwd_dq_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, k8, k8s, lse, dl, N, Np, BH, c, dq); \
   } while (0)
   if (causal) {
     if (out_f32) SAGE_BWD_LAUNCH(true, true);
@@ -530,11 +570,15 @@ static hipError_t launch_bwd_d(bool mx, const void* qc, const void* qs, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(bool mx, const void* qc, const void* qs, const void* kc, const void* ks, const void* v,
-                           const void* o, const void* dout, const float* lse, int BH, int N, int D, bool causal,
-                           float c, void* dq, void* dk, void* dv, bool out_f32, void* ws, hipStream_t st) {
-  if (D == 64) return launch_bwd_d<64>(mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
-  return launch_bwd_d<128>(mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
+// stages: a mask of BWD_PREP (the three operand preparations), BWD_DKDV and BWD_DQ, launched in
+// that order; the gradient stages read what the preparation left in the workspace.
+hipError_t launch_attn_bwd(int stages, bool mx, const void* qc, const void* qs, const void* kc, const void* ks,
+                           const void* v, const void* o, const void* dout, const float* lse, int BH, int N, int D,
+                           bool causal, float c, void* dq, void* dk, void* dv, bool out_f32, void* ws,
+                           hipStream_t st) {
+  if (D == 64)
+    return launch_bwd_d<64>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
+  return launch_bwd_d<128>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
 }
 
 }  // namespace sage

@@ -60,6 +60,7 @@ extern "C" {
 typedef enum { SAGE_FMT_NVFP4 = 0, SAGE_FMT_MXFP4 = 1, SAGE_FMT_MX4_PV8 = 2 } sage_fmt_t;
 typedef enum { SAGE_ROLE_Q = 0, SAGE_ROLE_K = 1, SAGE_ROLE_V = 2 } sage_role_t;
 typedef enum { SAGE_OUT_F16 = 0, SAGE_OUT_F32 = 1 } sage_out_t;
+typedef enum { SAGE_BWD_PREP = 0, SAGE_BWD_DKDV = 1, SAGE_BWD_DQ = 2 } sage_bwd_stage_t;
 typedef enum {
   SAGE_OK = 0,
   SAGE_ERR_NULL = -1,     /* a required pointer is NULL */
@@ -182,6 +183,21 @@ int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales,
                       int B, int H, int N, int D, int causal, float sm_scale,
                       void* dq, void* dk, void* dv, int out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* One stage of sage_fp4_attn_bwd, for callers that time or schedule the stages separately: the
+ * full call is exactly SAGE_BWD_PREP, SAGE_BWD_DKDV, SAGE_BWD_DQ in that order on one stream
+ * with one workspace. Same arguments, validation and errors (a bad `stage` is SAGE_ERR_ENUM).
+ *   SAGE_BWD_PREP  three launches: fills the workspace from the Q/K codes, dout and o.
+ *   SAGE_BWD_DKDV  one launch: writes dk and dv from the workspace, v, dout and lse.
+ *   SAGE_BWD_DQ    one launch: writes dq from the workspace, v, dout and lse.
+ * A gradient stage reads a workspace filled by a preparation stage of the same arguments;
+ * pointers a stage does not use are still validated. */
+int sage_fp4_attn_bwd_stage(int stage, int fmt, const void* q_codes, const void* q_scales,
+                            const void* k_codes, const void* k_scales,
+                            const void* v, const void* o, const void* dout, const float* lse,
+                            int B, int H, int N, int D, int causal, float sm_scale,
+                            void* dq, void* dk, void* dv, int out_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* sage_fp4_status_string(int status);

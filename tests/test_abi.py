@@ -150,3 +150,8 @@ def test_bwd_workspace_and_validation():
     assert call(D=96) == -3
     assert call(N=0) == -2
     assert bnd.status_string(-7) != bnd.status_string(99)
+    st = bnd.sage_fp4_attn_bwd_stage
+    assert st(3, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, FAKE, FAKE, 1, FAKE, need, None) == -5
+    assert st(-1, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, FAKE, FAKE, 1, FAKE, need, None) == -5
+    assert st(1, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, FAKE, FAKE, 1, FAKE, need - 1, None) == -7
+    assert st(2, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, None, FAKE, 1, FAKE, need, None) == -1

@@ -202,3 +202,22 @@ def test_bwd_full_size_sampled_heads(causal):
     ref, bd = obwd.attn_bwd(fmt, Qs, Ks, vs, o_s, dos, l_s, causal=causal, want_bounds=True)
     say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
     _check_grads(got, ref, bd)
+
+
+def test_bwd_stages_equal_full_call():
+    """SAGE_BWD_PREP, SAGE_BWD_DKDV, SAGE_BWD_DQ in order give the full call's results bit for bit."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    fmt, B, H, N, D, causal = orc.MXFP4, 1, 2, 300, 128, True
+    say("bwd staged calls against the full call")
+    q, k, v, do, Q, K, o, lse = _inputs(fmt, B, H, N, D, causal)
+    full, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal)
+    Qg, Kg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt)
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    args = (fmt, Qg, Kg, to_gpu(v), to_gpu(o), to_gpu(do), to_gpu(lse), *outs, ws)
+    for stage in (bnd.BWD_PREP, bnd.BWD_DKDV, bnd.BWD_DQ):
+        bnd.attn_bwd_into(*args, causal=causal, stage=stage)
+    torch.cuda.synchronize()
+    for a, b in zip(full, outs):
+        assert np.array_equal(a, b.cpu().numpy().astype(np.float64))
