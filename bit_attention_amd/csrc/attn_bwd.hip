@@ -19,14 +19,15 @@
 //     from FP4 to bf16 (exact: a code times its scale has at most 6 significant bits and lies
 //     in bf16's exponent range), and Q^, K^ and dO are encoded to INT8 per (channel, block),
 //     stored channel-major in the token order below; the dO prep also forms D_i in fp32.
-//   - dK/dV kernel, one workgroup of 4 waves per (batch*head, 64-key block): each wave owns 16
-//     keys and keeps their K^ (bf16) and V (fp16) rows as MFMA B operands in registers while the
-//     workgroup stages 64-query tiles through LDS. S = Q^ K^T and dP = dO V^T take 16x16x32
+//   - dK/dV kernel, one workgroup of 8 waves per (batch*head, 128-key block): each wave owns 16
+//     keys and keeps their K^ (bf16) and V (fp16) rows as MFMA B operands in registers while
+//     64-query tiles stream into LDS by asynchronous global-to-LDS copies (global_load_lds),
+//     double-buffered, one barrier per tile. S = Q^ K^T and dP = dO V^T take 16x16x32
 //     MFMAs; a lane then holds 16 (query, key) values of one key, at queries 16s + 4g + i
 //     (subtile s, lane group g, element i). P and dS are therefore lane-local, a key's block
 //     maximum takes two cross-lane swaps, and a lane's 16 codes are directly the A operand of a
 //     16x16x64 INT8 MFMA whose K slots 16g + 4s + i hold those queries; the INT8 dO and Q^ are
-//     stored in that slot order. Two workgroups fit on a CU (57 KB of LDS each at D = 128).
+//     stored in that slot order. One workgroup per CU (two 49 KB tile buffers at D = 128).
 //   - dQ kernel: the mirror image, one wave per 16 queries looping over 64-key tiles. dQ gets
 //     a kernel of its own instead of atomic adds, so every result is deterministic.
 #include <type_traits>
@@ -59,7 +60,8 @@ __device__ __forceinline__ int pack4(int a, int b, int c, int d) {
 
 // ---------------------------------------------------------------------------------------------
 // Prep: one workgroup per (block of 64 tokens, batch*head). SRC 0: NVFP4 codes, 1: MXFP4 codes
-// (both also write the bf16 values), 2: fp16 dO (also writes D_i from dO and O).
+// (both also write the bf16 values), 2: fp16 dO (also writes D_i from dO and O, and lse * log2 e;
+// both [.., Np], zero past N). INT8 scales are stored block-major, [.., Np / 64, D].
 // ---------------------------------------------------------------------------------------------
 template <int D, int SRC>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ codes,
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
                                                        const f16* __restrict__ x, const f16* __restrict__ o,
                                                        int N, int Np, __bf16* __restrict__ xh,
                                                        int8_t* __restrict__ q8, float* __restrict__ q8s,
+                                                       const float* __restrict__ lse, float* __restrict__ l2,
                                                        float* __restrict__ dl) {
   constexpr int VPT = D / 4;      // values per thread in the row phase (64 rows x D / 256)
   constexpr int TPR = D / VPT;    // threads per token row (4)
@@ -99,7 +102,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
         }
         dot += __shfl_xor(dot, 1);
         dot += __shfl_xor(dot, 2);
-        if (ch == 0) dl[row] = dot;
+        if (ch == 0) {
+          dl[bh * Np + tok] = dot;
+          l2[bh * Np + tok] = lse[row] * LOG2E;
+        }
       } else {
         constexpr int blkv = SRC == 0 ? 16 : 32;
         const unsigned* cw = reinterpret_cast<const unsigned*>(codes + row * (D / 2) + ch * (VPT / 2));
@@ -133,6 +139,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
     } else {
 #pragma unroll
       for (int u = 0; u < VPT; ++u) v[u] = 0.0f;
+      if constexpr (SRC == 2) {
+        if (ch == 0 && tok < Np) {
+          dl[bh * Np + tok] = 0.0f;
+          l2[bh * Np + tok] = 0.0f;
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) sx[n][ch * VPT + u] = v[u];
@@ -162,51 +174,71 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
       for (int e = 0; e < 4; ++e) wv[e] = pack4(cq[16 * u + 4 * e], cq[16 * u + 4 * e + 1], cq[16 * u + 4 * e + 2], cq[16 * u + 4 * e + 3]);
       *reinterpret_cast<v4i*>(dst + 16 * u) = wv;
     }
-    if (h == 0) q8s[(bh * D + d) * nb + blk] = a > 0.0f ? div_rn(a, 127.0f) : 0.0f;
+    if (h == 0) q8s[(bh * nb + blk) * D + d] = a > 0.0f ? div_rn(a, 127.0f) : 0.0f;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Shared pieces of the two gradient kernels.
 // ---------------------------------------------------------------------------------------------
+constexpr int NWAVE = 8;        // waves per workgroup: two per SIMD, one workgroup per CU
+constexpr int WB = 16 * NWAVE;  // keys (dK/dV) or queries (dQ) per workgroup
+
 template <int D>
 struct BwdTile {
-  static constexpr int RP = D + 8;        // LDS row pitch (elements) of the 16-bit tiles
-  static constexpr int CP = BB + 16;      // LDS row pitch (bytes) of the INT8 tiles
+  static constexpr int T16 = BB * 2 * D;  // bytes of a 16-bit tile (64 tokens x D)
+  static constexpr int T8 = D * BB;       // bytes of an INT8 tile (D channels x 64 slots)
+  static constexpr int W16 = T16 / 1024;  // wave-wide copies (16 bytes per lane) per 16-bit tile
+  static constexpr int W8 = T8 / 1024;    // ... per INT8 tile
   static constexpr int KK = D / 32;       // k steps of the 16x16x32 MFMAs
   static constexpr int NN = D / 16;       // 16-channel output subtiles
 };
 
-// Stage one 64-token tile: rows [t0, t0 + 64) of a bf16 and an fp16 [.., N, D] tensor (zero past
-// N), the INT8 codes [D][64] of the block and its per-channel scales.
+// LDS tiles carry no padding. An MFMA operand read has 16 lanes fetch one 16-byte chunk from
+// each of 16 consecutive rows; storing chunk c of row r at chunk slot c ^ swz(r) gives those 16
+// reads 16 different bank groups.
 template <int D>
-__device__ __forceinline__ void stage_tile(int tid, int64_t bh, int N, int Np, int t0, int blk,
-                                           const __bf16* __restrict__ a16, const f16* __restrict__ b16,
-                                           const int8_t* __restrict__ c8, const float* __restrict__ c8s,
-                                           __bf16* sA, f16* sB, int8_t* sC, float* sCs) {
-  using T = BwdTile<D>;
-#pragma unroll
-  for (int u = 0; u < BB * D / 8 / 256; ++u) {
-    const int idx = tid + 256 * u, row = idx / (D / 8), ch = idx % (D / 8);
-    const int tok = t0 + row;
-    v4u va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-    if (tok < N) {
-      va = *reinterpret_cast<const v4u*>(a16 + (bh * N + tok) * D + 8 * ch);
-      vb = *reinterpret_cast<const v4u*>(b16 + (bh * N + tok) * D + 8 * ch);
-    }
-    *reinterpret_cast<v4u*>(sA + row * T::RP + 8 * ch) = va;
-    *reinterpret_cast<v4u*>(sB + row * T::RP + 8 * ch) = vb;
+__device__ __forceinline__ int swz16(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int swz8(int d) { return (d >> 2) & 3; }
+
+// Asynchronous copy of 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
+// lane i writes lds + 16 i, lds being the same for the whole wave; vmcnt counts completion.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Copy j of a 16-bit tile: rows [t0, t0 + 64) of one head of a [.., N, D] tensor starting at
+// `head`; a row past N reads row N - 1 (its results are masked).
+template <int D>
+__device__ __forceinline__ void copy16_job(int j, int lane, const uint8_t* head, int t0, int N, uint8_t* tile) {
+  int r, cs;
+  if constexpr (D == 128) {
+    r = 4 * j + (lane >> 4);
+    cs = lane & 15;
+  } else {
+    r = 8 * j + (lane >> 3);
+    cs = lane & 7;
   }
-#pragma unroll
-  for (int u = 0; u < (D * 4 + 255) / 256; ++u) {
-    const int idx = tid + 256 * u;
-    if (idx < D * 4) {
-      const int d = idx >> 2, ch = idx & 3;
-      *reinterpret_cast<v4u*>(sC + d * T::CP + 16 * ch) =
-          *reinterpret_cast<const v4u*>(c8 + (bh * D + d) * Np + t0 + 16 * ch);
-    }
-  }
-  if (tid < D) sCs[tid] = c8s[(bh * D + tid) * (Np / BB) + blk];
+  const int row = min(t0 + r, N - 1);
+  lds_copy16(head + (int64_t)row * (2 * D) + 16 * (cs ^ swz16<D>(r)), tile + 1024 * j);
+}
+
+// Copy j of an INT8 tile: 64 slots of every channel, starting at blk0 = codes + (bh D) Np + t0.
+__device__ __forceinline__ void copy8_job(int j, int lane, const int8_t* blk0, int Np, uint8_t* tile) {
+  const int d = 16 * j + (lane >> 2);
+  lds_copy16(blk0 + (int64_t)d * Np + 16 * ((lane & 3) ^ swz8(d)), tile + 1024 * j);
+}
+
+// MFMA A operand (8 x 16 bits) of tile row r, channels 32 kk + 8 g .. + 7; sw = swz16(r), which
+// for r = 16 s + col equals swz16(col).
+template <int D, typename V>
+__device__ __forceinline__ V read16(const uint8_t* tile, int r, int kk, int g, int sw) {
+  return *reinterpret_cast<const V*>(tile + r * (2 * D) + 16 * ((4 * kk + g) ^ sw));
+}
+// INT8 MFMA B operand of channel d, slots 16 g .. + 15; sw8 = swz8(d) = swz8(col) for d = 16 n + col.
+__device__ __forceinline__ v4i read8(const uint8_t* tile, int d, int g, int sw8) {
+  return *reinterpret_cast<const v4i*>(tile + d * BB + 16 * (g ^ sw8));
 }
 
 // Codes of 16 values held by a lane (four subtiles s of four elements i) with a common
@@ -239,28 +271,30 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK and dV: one workgroup per (batch*head, 64-key block).
+// dK and dV: one workgroup of 8 waves per (batch*head, 128-key block); 64-query tiles arrive in
+// LDS through asynchronous copies, double-buffered: tile t + 1 is copied while tile t is used.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ q8, const float* __restrict__ q8s,
-    const int8_t* __restrict__ do8, const float* __restrict__ do8s, const float* __restrict__ lse,
+    const int8_t* __restrict__ do8, const float* __restrict__ do8s, const float* __restrict__ l2,
     const float* __restrict__ dl, int N, int Np, int BH, float c, void* __restrict__ dk, void* __restrict__ dv) {
   using T = BwdTile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[BB * T::RP];
-  __shared__ __attribute__((aligned(16))) f16 sdO[BB * T::RP];
-  __shared__ __attribute__((aligned(16))) int8_t sQ8[D * T::CP];
-  __shared__ __attribute__((aligned(16))) int8_t sdO8[D * T::CP];
-  __shared__ float sQs[D], sdOs[D];
-  __shared__ __attribute__((aligned(16))) float sL[BB], sD[BB];
+  constexpr int O_DO = T::T16, O_Q8 = 2 * T::T16, O_DO8 = O_Q8 + T::T8, O_QS = O_DO8 + T::T8;
+  constexpr int O_DOS = O_QS + 4 * D, O_L = O_DOS + 4 * D, O_D = O_L + 4 * BB, BUF = O_D + 4 * BB;
+  constexpr int NJ = 2 * T::W16 + 2 * T::W8 + 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
 
-  const int nb = Np / BB;
-  const int w = xcd_work(blockIdx.x, BH * nb);
-  const int64_t bh = w / nb;
-  const int kb = w % nb;  // causal: the heaviest key blocks (most query tiles) of a head first
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, g = l >> 4, col = l & 15;
-  const int key = kb * BB + wave * 16 + col;
+  const int nq = Np / BB;
+  const int nkb = (N + WB - 1) / WB;
+  const int w = xcd_work(blockIdx.x, BH * nkb);
+  const int64_t bh = w / nkb;
+  const int kb = w % nkb;  // causal: the heaviest key blocks (most query tiles) of a head first
+  // the wave index is uniform across a wave: readfirstlane lets the copy schedule branch on scalars
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, col = l & 15;
+  const int key = kb * WB + wave * 16 + col;
+  const int sw = swz16<D>(col), sw8 = swz8(col);
 
   v8bf kreg[T::KK];
   v8h vreg[T::KK];
@@ -279,91 +313,96 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   for (int n = 0; n < T::NN; ++n) accK[n] = accV[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  // non-causal: each workgroup starts at its own query tile (kb) and wraps around, so the
-  // workgroups of a head do not all read the same tile at the same time
-  const int it0 = CAUSAL ? kb : 0, nit = CAUSAL ? nb - kb : nb;
-  for (int it = 0; it < nit; ++it) {
-    const int qt = CAUSAL ? it0 + it : (kb + it) % nb;
-    const int q0 = qt * BB;
-    __syncthreads();
-    stage_tile<D>(tid, bh, N, Np, q0, qt, qh, dout, q8, q8s, sQ, sdO, sQ8, sQs);
-    if (tid >= 128 && tid < 128 + D) sdOs[tid - 128] = do8s[(bh * D + tid - 128) * nb + qt];
-    if (tid < BB) sL[tid] = q0 + tid < N ? lse[bh * N + q0 + tid] * LOG2E : 0.0f;
-    else if (tid < 2 * BB) sD[tid - BB] = q0 + tid - BB < N ? dl[bh * N + q0 + tid - BB] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < (D * 4 + 255) / 256; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < D * 4) {
-        const int d = idx >> 2, ch = idx & 3;
-        *reinterpret_cast<v4u*>(sdO8 + d * T::CP + 16 * ch) =
-            *reinterpret_cast<const v4u*>(do8 + (bh * D + d) * Np + q0 + 16 * ch);
+  // causal: query tiles from the one holding the block's first key; non-causal: every tile,
+  // starting at the block's own position and wrapping, so the blocks of a head spread out
+  const int qt0 = CAUSAL ? kb * (WB / BB) : 0, nit = nq - qt0;
+  auto tile_of = [&](int it) { return CAUSAL ? qt0 + it : (kb * (WB / BB) + it) % nq; };
+  auto issue = [&](int it, uint8_t* buf) {
+    const int qt = tile_of(it), t0 = qt * BB;
+    for (int j = wave; j < NJ; j += NWAVE) {
+      if (j < T::W16) {
+        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(qh + bh * N * D), t0, N, buf);
+      } else if (j < 2 * T::W16) {
+        copy16_job<D>(j - T::W16, l, reinterpret_cast<const uint8_t*>(dout + bh * N * D), t0, N, buf + O_DO);
+      } else if (j < 2 * T::W16 + T::W8) {
+        copy8_job(j - 2 * T::W16, l, q8 + bh * D * Np + t0, Np, buf + O_Q8);
+      } else if (j < 2 * T::W16 + 2 * T::W8) {
+        copy8_job(j - 2 * T::W16 - T::W8, l, do8 + bh * D * Np + t0, Np, buf + O_DO8);
+      } else {
+        const int k = j - 2 * T::W16 - 2 * T::W8;  // scales of Q8, of dO8; lse * log2(e); D
+        const float* src = k == 0 ? q8s + (bh * nq + qt) * D
+                           : k == 1 ? do8s + (bh * nq + qt) * D
+                           : k == 2 ? l2 + bh * Np + t0
+                                    : dl + bh * Np + t0;
+        const int off = k == 0 ? O_QS : k == 1 ? O_DOS : k == 2 ? O_L : O_D;
+        if (l < (k < 2 ? D / 4 : BB / 4)) lds_copy16(src + 4 * l, buf + off);
       }
     }
-    __syncthreads();
+  };
 
-    auto tile = [&](auto full_c) {
-      constexpr bool FULL = decltype(full_c)::value;
-      float P[4][4], dS[4][4];
-      float pmax = 0.0f, smax = 0.0f;
+  issue(0, lds[0]);
+  for (int it = 0; it < nit; ++it) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile it have landed
+    __syncthreads();                // every wave's have, and every wave is done with tile it - 1
+    if (it + 1 < nit) issue(it + 1, lds[(it + 1) & 1]);
+    const uint8_t* buf = lds[it & 1];
+    const int q0 = tile_of(it) * BB;
+
+    float P[4][4], dS[4][4];
+    float pmax = 0.0f, smax = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < 4; ++s) {
+      v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) {
-          const v8bf a = *reinterpret_cast<const v8bf*>(sQ + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[kk], sc, 0, 0, 0);
-          const v8h b = *reinterpret_cast<const v8h*>(sdO + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, vreg[kk], dp, 0, 0, 0);
-        }
-        const v4f L4 = *reinterpret_cast<const v4f*>(sL + 16 * s + 4 * g);
-        const v4f D4 = *reinterpret_cast<const v4f*>(sD + 16 * s + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qi = q0 + 16 * s + 4 * g + i;
-          const bool ok = FULL || (qi < N && key < N && (!CAUSAL || key <= qi));
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -L4[i]));
-          const float p = ok ? e : 0.0f;
-          P[s][i] = p;
-          dS[s][i] = p * (dp[i] - D4[i]);
-          pmax = fmaxf(pmax, p);
-          smax = fmaxf(smax, fabsf(dS[s][i]));
-        }
+      for (int kk = 0; kk < T::KK; ++kk) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), kreg[kk], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_DO, 16 * s + col, kk, g, sw), vreg[kk], dp, 0, 0, 0);
       }
-      pmax = xg_max(pmax);
-      smax = xg_max(smax);
-      const v4i aP = codes16(P, pmax > 0.0f ? div_rn(127.0f, pmax) : 0.0f);
-      const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
-      const float sP = pmax > 0.0f ? div_rn(pmax, 127.0f) : 0.0f;
-      const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
-      // the accumulator rows are keys 16 * wave + 4g + i; lane 4g + i holds their scales
-      float rP[4], rS[4];
+      const v4f L4 = *reinterpret_cast<const v4f*>(buf + O_L + 4 * (16 * s + 4 * g));
+      const v4f D4 = *reinterpret_cast<const v4f*>(buf + O_D + 4 * (16 * s + 4 * g));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        rP[i] = __shfl(sP, 4 * g + i);
-        rS[i] = __shfl(sS, 4 * g + i);
+        const int qi = q0 + 16 * s + 4 * g + i;
+        const bool ok = qi < N && key < N && (!CAUSAL || key <= qi);
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -L4[i]));
+        const float p = ok ? e : 0.0f;
+        P[s][i] = p;
+        dS[s][i] = p * (dp[i] - D4[i]);
+        pmax = fmaxf(pmax, p);
+        smax = fmaxf(smax, fabsf(dS[s][i]));
       }
+    }
+    pmax = xg_max(pmax);
+    smax = xg_max(smax);
+    const v4i aP = codes16(P, pmax > 0.0f ? div_rn(127.0f, pmax) : 0.0f);
+    const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
+    const float sP = pmax > 0.0f ? div_rn(pmax, 127.0f) : 0.0f;
+    const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
+    // the accumulator rows are keys 16 * wave + 4g + i; lane 4g + i holds their scales
+    float rP[4], rS[4];
 #pragma unroll
-      for (int n = 0; n < T::NN; ++n) {
-        const v4i bo = *reinterpret_cast<const v4i*>(sdO8 + (16 * n + col) * T::CP + 16 * g);
-        const v4i bq = *reinterpret_cast<const v4i*>(sQ8 + (16 * n + col) * T::CP + 16 * g);
-        const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, bo, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bq, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const float co = sdOs[16 * n + col], cq = sQs[16 * n + col];
+    for (int i = 0; i < 4; ++i) {
+      rP[i] = __shfl(sP, 4 * g + i);
+      rS[i] = __shfl(sS, 4 * g + i);
+    }
+    const float* qs = reinterpret_cast<const float*>(buf + O_QS);
+    const float* os = reinterpret_cast<const float*>(buf + O_DOS);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accV[n][i] = __builtin_fmaf((float)rv[i], rP[i] * co, accV[n][i]);
-          accK[n][i] = __builtin_fmaf((float)rk[i], rS[i] * cq, accK[n][i]);
-        }
+    for (int n = 0; n < T::NN; ++n) {
+      const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, read8(buf + O_DO8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
+      const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_Q8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
+      const float co = os[16 * n + col], cq = qs[16 * n + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accV[n][i] = __builtin_fmaf((float)rv[i], rP[i] * co, accV[n][i]);
+        accK[n][i] = __builtin_fmaf((float)rk[i], rS[i] * cq, accK[n][i]);
       }
-    };
-    // one variant with the per-element mask: a second, mask-free one for interior tiles
-    // raises the register count past 256
-    tile(std::false_type{});
+    }
   }
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int kr = kb * BB + wave * 16 + 4 * g + i;
+    const int kr = kb * WB + wave * 16 + 4 * g + i;
     if (kr >= N) continue;
 #pragma unroll
     for (int n = 0; n < T::NN; ++n) {
@@ -375,26 +414,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup per (batch*head, 64-query block).
+// dQ: one workgroup of 8 waves per (batch*head, 128-query block); 64-key tiles double-buffered
+// through asynchronous copies as in the dK/dV kernel.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ k8, const float* __restrict__ k8s,
-    const float* __restrict__ lse, const float* __restrict__ dl, int N, int Np, int BH, float c,
+    const float* __restrict__ l2, const float* __restrict__ dl, int N, int Np, int BH, float c,
     void* __restrict__ dq) {
   using T = BwdTile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BB * T::RP];
-  __shared__ __attribute__((aligned(16))) f16 sV[BB * T::RP];
-  __shared__ __attribute__((aligned(16))) int8_t sK8[D * T::CP];
-  __shared__ float sKs[D];
+  constexpr int O_V = T::T16, O_K8 = 2 * T::T16, O_KS = O_K8 + T::T8, BUF = O_KS + 4 * D;
+  constexpr int NJ = 2 * T::W16 + T::W8 + 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
 
-  const int nb = Np / BB;
-  const int w = xcd_work(blockIdx.x, BH * nb);
-  const int64_t bh = w / nb;
-  const int qb = CAUSAL ? nb - 1 - w % nb : w % nb;  // causal: the heaviest query blocks first
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, g = l >> 4, col = l & 15;
-  const int query = qb * BB + wave * 16 + col;
+  const int nk = Np / BB;
+  const int nqb = (N + WB - 1) / WB;
+  const int w = xcd_work(blockIdx.x, BH * nqb);
+  const int64_t bh = w / nqb;
+  const int qb = CAUSAL ? nqb - 1 - w % nqb : w % nqb;  // causal: the heaviest query blocks first
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, col = l & 15;
+  const int query = qb * WB + wave * 16 + col;
+  const int sw = swz16<D>(col), sw8 = swz8(col);
 
   v8bf qreg[T::KK];
   v8h oreg[T::KK];
@@ -410,24 +451,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
   }
   if (query < N) {
-    Lq = lse[bh * N + query] * LOG2E;
-    Dq = dl[bh * N + query];
+    Lq = l2[bh * Np + query];
+    Dq = dl[bh * Np + query];
   }
   v4f acc[T::NN];
 #pragma unroll
   for (int n = 0; n < T::NN; ++n) acc[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  // non-causal: each workgroup starts at its own key tile (qb) and wraps around
-  const int nit = CAUSAL ? qb + 1 : nb;
-  for (int it = 0; it < nit; ++it) {
-    const int kt = CAUSAL ? it : (qb + it) % nb;
-    const int k0 = kt * BB;
-    __syncthreads();
-    stage_tile<D>(tid, bh, N, Np, k0, kt, kh, v, k8, k8s, sK, sV, sK8, sKs);
-    __syncthreads();
+  // causal: key tiles up to the one holding the block's last query
+  const int nit = CAUSAL ? min(nk, (qb * WB + WB - 1) / BB + 1) : nk;
+  auto tile_of = [&](int it) { return CAUSAL ? it : (qb * (WB / BB) + it) % nk; };
+  auto issue = [&](int it, uint8_t* buf) {
+    const int kt = tile_of(it), t0 = kt * BB;
+    for (int j = wave; j < NJ; j += NWAVE) {
+      if (j < T::W16) {
+        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(kh + bh * N * D), t0, N, buf);
+      } else if (j < 2 * T::W16) {
+        copy16_job<D>(j - T::W16, l, reinterpret_cast<const uint8_t*>(v + bh * N * D), t0, N, buf + O_V);
+      } else if (j < 2 * T::W16 + T::W8) {
+        copy8_job(j - 2 * T::W16, l, k8 + bh * D * Np + t0, Np, buf + O_K8);
+      } else if (l < D / 4) {
+        lds_copy16(k8s + (bh * nk + kt) * D + 4 * l, buf + O_KS);
+      }
+    }
+  };
 
-    const bool full = k0 + BB <= N && qb * BB + BB <= N && (!CAUSAL || kt < qb);
+  issue(0, lds[0]);
+  for (int it = 0; it < nit; ++it) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < nit) issue(it + 1, lds[(it + 1) & 1]);
+    const uint8_t* buf = lds[it & 1];
+    const int k0 = tile_of(it) * BB;
+    // every (query, key) pair of the tile is visible: no per-element mask
+    const bool full = k0 + BB <= N && qb * WB + WB <= N && (!CAUSAL || k0 + BB - 1 <= qb * WB);
     auto tile = [&](auto full_c) {
       constexpr bool FULL = decltype(full_c)::value;
       float dS[4][4];
@@ -437,10 +495,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk) {
-          const v8bf a = *reinterpret_cast<const v8bf*>(sK + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], sc, 0, 0, 0);
-          const v8h b = *reinterpret_cast<const v8h*>(sV + (16 * s + col) * T::RP + 32 * kk + 8 * g);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, oreg[kk], dp, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), qreg[kk], sc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_V, 16 * s + col, kk, g, sw), oreg[kk], dp, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -458,11 +514,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       float rS[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rS[i] = __shfl(sS, 4 * g + i);
+      const float* ks = reinterpret_cast<const float*>(buf + O_KS);
 #pragma unroll
       for (int n = 0; n < T::NN; ++n) {
-        const v4i bk = *reinterpret_cast<const v4i*>(sK8 + (16 * n + col) * T::CP + 16 * g);
-        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, bk, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const float ck = sKs[16 * n + col];
+        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_K8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
+        const float ck = ks[16 * n + col];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_fmaf((float)r[i], rS[i] * ck, acc[n][i]);
       }
@@ -473,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int qr = qb * BB + wave * 16 + 4 * g + i;
+    const int qr = qb * WB + wave * 16 + 4 * g + i;
     if (qr >= N) continue;
 #pragma unroll
     for (int n = 0; n < T::NN; ++n) store_out<OUT_F32>(dq, (bh * N + qr) * D + 16 * n + col, c * acc[n][i]);
@@ -491,9 +547,9 @@ enum { BWD_PREP = 1, BWD_DKDV = 2, BWD_DQ = 4 };
 
 // Workspace layout (offsets in bytes, each 256-aligned; Np = ceil(N/64)*64, nb = Np/64):
 //   Q^ bf16 [BH,N,D] | K^ bf16 [BH,N,D] | Q8, K8, dO8 int8 [BH,D,Np] each |
-//   Q8, K8, dO8 scales fp32 [BH,D,nb] each | D fp32 [BH,N]
+//   Q8, K8, dO8 scales fp32 [BH,nb,D] each | D fp32 [BH,Np] | lse * log2(e) fp32 [BH,Np]
 struct BwdWs {
-  int64_t qh, kh, q8, k8, do8, q8s, k8s, do8s, dl, total;
+  int64_t qh, kh, q8, k8, do8, q8s, k8s, do8s, dl, l2, total;
 };
 
 BwdWs bwd_ws_layout(int64_t BH, int N, int D) {
@@ -508,7 +564,8 @@ BwdWs bwd_ws_layout(int64_t BH, int N, int D) {
   w.q8s = off; off += align256(BH * D * nb * 4);
   w.k8s = off; off += align256(BH * D * nb * 4);
   w.do8s = off; off += align256(BH * D * nb * 4);
-  w.dl = off; off += align256(BH * N * 4);
+  w.dl = off; off += align256(BH * Np * 4);
+  w.l2 = off; off += align256(BH * Np * 4);
   w.total = off;
   return w;
 }
@@ -531,6 +588,7 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
   float* k8s = reinterpret_cast<float*>(base + L.k8s);
   float* do8s = reinterpret_cast<float*>(base + L.do8s);
   float* dl = reinterpret_cast<float*>(base + L.dl);
+  float* l2 = reinterpret_cast<float*>(base + L.l2);
   const int Np = (N + BB - 1) / BB * BB, nb = Np / BB;
   const dim3 pg(nb, BH);
   const uint8_t* qcb = reinterpret_cast<const uint8_t*>(qc);
@@ -542,22 +600,22 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
   const f16* doh = reinterpret_cast<const f16*>(dout);
   if (stages & BWD_PREP) {
     if (mx) {
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr, nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr, nullptr);
     } else {
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr);
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr, nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr, nullptr);
     }
-    bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, dl);
+    bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, lse, l2, dl);
   }
-  const int grid = BH * nb;
+  const int grid = BH * ((N + WB - 1) / WB);
 #define SAGE_BWD_LAUNCH(CZ, F32)                                                                          \
   do {                                                                                                    \
     if (stages & BWD_DKDV)                                                                                \
-      bwd_dkdv_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, lse, dl, N, Np, \
-                                                        BH, c, dk, dv);                                   \
+      bwd_dkdv_kernel<D, CZ, F32><<<grid, 64 * NWAVE, 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, dl, N, \
+                                                               Np, BH, c, dk, dv);                        \
     if (stages & BWD_DQ)                                                                                  \
-      bwd_dq_kernel<D, CZ, F32><<<grid, 256, 0, st>>>(qh, kh, vh, doh, k8, k8s, lse, dl, N, Np, BH, c, dq); \
+      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * NWAVE, 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, dq); \
   } while (0)
   if (causal) {
     if (out_f32) SAGE_BWD_LAUNCH(true, true);

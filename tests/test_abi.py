@@ -127,7 +127,7 @@ def test_bwd_workspace_and_validation():
     B, H, N, D = 2, 3, 300, 128
     np64, nb = 320, 5
     want = (2 * a256(B * H * N * D * 2) + 3 * a256(B * H * D * np64) + 3 * a256(B * H * D * nb * 4)
-            + a256(B * H * N * 4))
+            + 2 * a256(B * H * np64 * 4))
     assert bnd.sage_fp4_attn_bwd_workspace_bytes(B, H, N, D) == want
     assert bnd.sage_fp4_attn_bwd_workspace_bytes(B, H, N, 96) == 0
     assert bnd.sage_fp4_attn_bwd_workspace_bytes(1, 1024, 1 << 20, 64) == 0

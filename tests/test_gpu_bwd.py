@@ -77,14 +77,15 @@ def _ws_views(ws, B, H, N, D):
         return (x + 255) // 256 * 256
     BH, Np = B * H, -(-N // 64) * 64
     nb = Np // 64
-    sizes = [BH * N * D * 2] * 2 + [BH * D * Np] * 3 + [BH * D * nb * 4] * 3 + [BH * N * 4]
+    sizes = [BH * N * D * 2] * 2 + [BH * D * Np] * 3 + [BH * D * nb * 4] * 3 + [BH * Np * 4] * 2
     offs = np.cumsum([0] + [a256(s) for s in sizes])
     raw = [ws[offs[i]:offs[i] + sizes[i]] for i in range(len(sizes))]
     bf = [(r.view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(B, H, N, D) for r in raw[:2]]
     i8 = [r.view(np.int8).reshape(B, H, D, Np) for r in raw[2:5]]
-    sc = [r.view(np.float32).reshape(B, H, D, nb) for r in raw[5:8]]
-    dl = raw[8].view(np.float32).reshape(B, H, N)
-    return bf, i8, sc, dl
+    sc = [r.view(np.float32).reshape(B, H, nb, D).transpose(0, 1, 3, 2) for r in raw[5:8]]
+    dl = raw[8].view(np.float32).reshape(B, H, Np)
+    l2 = raw[9].view(np.float32).reshape(B, H, Np)
+    return bf, i8, sc, dl, l2
 
 
 CASES = [
@@ -111,7 +112,7 @@ def test_bwd_matches_oracle(fmt, B, H, N, D, causal):
 
     # the workspace: bf16 Q^, K^; INT8 codes and scales of Q^, K^, dO; D
     fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
-    bf, i8, sc, dl = _ws_views(ws, B, H, N, D)
+    bf, i8, sc, dl, l2 = _ws_views(ws, B, H, N, D)
     xs = (orc.dequant(fq, *Q), orc.dequant(fq, *K), do.astype(np.float64))
     for t in range(2):
         assert np.array_equal(bf[t], xs[t].astype(np.float32))
@@ -127,7 +128,9 @@ def test_bwd_matches_oracle(fmt, B, H, N, D, causal):
                 assert np.array_equal(sc[t][b, h].astype(np.float64), scales_o), (t, b, h)
     dref = np.sum(do.astype(np.float64) * o.astype(np.float64), axis=3)
     gsum = D * 2.0 ** -24 * np.sum(np.abs(do.astype(np.float64) * o.astype(np.float64)), axis=3)
-    assert np.all(np.abs(dl - dref) <= gsum + 1e-30)
+    assert np.all(np.abs(dl[..., :N] - dref) <= gsum + 1e-30)
+    assert not dl[..., N:].any() and not l2[..., N:].any()
+    assert np.array_equal(l2[..., :N], (lse * np.float32(1.4426950408889634)).astype(np.float32))
 
 
 def test_bwd_fp16_outputs_and_determinism():
