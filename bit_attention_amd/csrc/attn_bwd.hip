@@ -19,7 +19,7 @@
 //     from FP4 to bf16 (exact: a code times its scale has at most 6 significant bits and lies
 //     in bf16's exponent range), and Q^, K^ and dO are encoded to INT8 per (channel, block),
 //     stored channel-major in the token order below; the dO prep also forms D_i in fp32.
-//   - dK/dV kernel, one workgroup of 8 waves per (batch*head, 128-key block): each wave owns 16
+//   - dK/dV kernel, one workgroup of 12 waves per (batch*head, 192-key block): each wave owns 16
 //     keys and keeps their K^ (bf16) and V (fp16) rows as MFMA B operands in registers while
 //     64-query tiles stream into LDS by asynchronous global-to-LDS copies (global_load_lds),
 //     double-buffered, one barrier per tile. S = Q^ K^T and dP = dO V^T take 16x16x32
@@ -27,7 +27,8 @@
 //     (subtile s, lane group g, element i). P and dS are therefore lane-local, a key's block
 //     maximum takes two cross-lane swaps, and a lane's 16 codes are directly the A operand of a
 //     16x16x64 INT8 MFMA whose K slots 16g + 4s + i hold those queries; the INT8 dO and Q^ are
-//     stored in that slot order. One workgroup per CU (two 49 KB tile buffers at D = 128).
+//     stored in that slot order. One workgroup per CU (two 49 KB tile buffers at D = 128), three
+//     waves per SIMD (at most 168 VGPRs).
 //   - dQ kernel: the mirror image, one wave per 16 queries looping over 64-key tiles. dQ gets
 //     a kernel of its own instead of atomic adds, so every result is deterministic.
 #include <type_traits>
@@ -181,7 +182,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
 // ---------------------------------------------------------------------------------------------
 // Shared pieces of the two gradient kernels.
 // ---------------------------------------------------------------------------------------------
-constexpr int NWAVE = 8;        // waves per workgroup: two per SIMD, one workgroup per CU
+constexpr int NWAVE = 12;       // waves per workgroup: three per SIMD (at most 168 VGPRs), one
+                                // workgroup per CU (LDS)
 constexpr int WB = 16 * NWAVE;  // keys (dK/dV) or queries (dQ) per workgroup
 
 template <int D>
@@ -271,7 +273,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK and dV: one workgroup of 8 waves per (batch*head, 128-key block); 64-query tiles arrive in
+// dK and dV: one workgroup of 12 waves per (batch*head, 192-key block); 64-query tiles arrive in
 // LDS through asynchronous copies, double-buffered: tile t + 1 is copied while tile t is used.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
@@ -316,7 +318,11 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
   // causal: query tiles from the one holding the block's first key; non-causal: every tile,
   // starting at the block's own position and wrapping, so the blocks of a head spread out
   const int qt0 = CAUSAL ? kb * (WB / BB) : 0, nit = nq - qt0;
-  auto tile_of = [&](int it) { return CAUSAL ? qt0 + it : (kb * (WB / BB) + it) % nq; };
+  const int st0 = CAUSAL ? qt0 : __builtin_amdgcn_readfirstlane((kb * (WB / BB)) % nq);
+  auto tile_of = [&](int it) {
+    const int t = st0 + it;
+    return CAUSAL ? t : (t >= nq ? t - nq : t);
+  };
   auto issue = [&](int it, uint8_t* buf) {
     const int qt = tile_of(it), t0 = qt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup of 8 waves per (batch*head, 128-query block); 64-key tiles double-buffered
+// dQ: one workgroup of 12 waves per (batch*head, 192-query block); 64-key tiles double-buffered
 // through asynchronous copies as in the dK/dV kernel.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
@@ -461,7 +467,11 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
 
   // causal: key tiles up to the one holding the block's last query
   const int nit = CAUSAL ? min(nk, (qb * WB + WB - 1) / BB + 1) : nk;
-  auto tile_of = [&](int it) { return CAUSAL ? it : (qb * (WB / BB) + it) % nk; };
+  const int st0 = CAUSAL ? 0 : __builtin_amdgcn_readfirstlane((qb * (WB / BB)) % nk);
+  auto tile_of = [&](int it) {
+    const int t = st0 + it;
+    return CAUSAL ? t : (t >= nk ? t - nk : t);
+  };
   auto issue = [&](int it, uint8_t* buf) {
     const int kt = tile_of(it), t0 = kt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
