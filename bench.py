@@ -477,6 +477,12 @@ def bench_backward(args, shape, fmt, torch, bnd, synth):
         a = g.view(B * H, N, D)[h0].double().cpu().numpy().reshape(-1)
         b = r.numpy().reshape(-1)
         res[f"cos_sim_{name}_vs_fp64"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 256 << 20
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_bwd(q_np, k_np, v_np, do_np, shape, fmt, causal)
     else:

@@ -43,6 +43,9 @@ typedef _Float16 f16;
 
 constexpr int BB = 64;                          // token block of the INT8 operands and tile size
 constexpr float LOG2E = 1.4426950408889634f;
+// lse * log2(e) stored for token positions past N: exp2(x - PAD_L2) is exactly 0 for any finite
+// score x, so such a query's P and dS vanish without a per-element mask
+constexpr float PAD_L2 = 1.0e30f;
 
 // Token held by slot p of a 64-token block: slot 16g + 4s + i holds token 16s + 4g + i (an
 // involution). A wave's 16x16 MFMA results for four 16-token subtiles put token 16s + 4g + i in
@@ -54,6 +57,14 @@ __host__ __device__ inline int slot_token64(int p) { return 16 * ((p >> 2) & 3) 
 // equals the correctly rounded fp32 quotient (53 >= 2 * 24 + 2).
 __device__ __forceinline__ float div_rn(float a, float b) { return (float)((double)a / (double)b); }
 
+// The scale and reciprocal of a block of P or dS inside the gradient kernels: a * fl32(1/127) and
+// 127 * rcp(a) (v_rcp_f32, 1 ulp), 0 for a = 0. They differ from fl32(a / 127) and fl32(127 / a)
+// by at most about an ulp, which moves a result far less than its float32 tolerance and a code
+// only where x * r lies within a few ulp of a half-integer, where either rounding is allowed.
+// The operand preparation uses the exact quotients (its codes are compared bit for bit).
+constexpr float INV127 = 1.0f / 127.0f;
+__device__ __forceinline__ float recip127(float a) { return a > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(a) : 0.0f; }
+
 // Four integers in [-127, 127] -> one dword, the first in the low byte.
 __device__ __forceinline__ int pack4(int a, int b, int c, int d) {
   return (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((d & 0xFF) << 24);
@@ -62,7 +73,7 @@ __device__ __forceinline__ int pack4(int a, int b, int c, int d) {
 // ---------------------------------------------------------------------------------------------
 // Prep: one workgroup per (block of 64 tokens, batch*head). SRC 0: NVFP4 codes, 1: MXFP4 codes
 // (both also write the bf16 values), 2: fp16 dO (also writes D_i from dO and O, and lse * log2 e;
-// both [.., Np], zero past N). INT8 scales are stored block-major, [.., Np / 64, D].
+// both [.., Np], past N 0 and PAD_L2). INT8 scales are stored block-major, [.., Np / 64, D].
 // ---------------------------------------------------------------------------------------------
 template <int D, int SRC>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ codes,
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
       if constexpr (SRC == 2) {
         if (ch == 0 && tok < Np) {
           dl[bh * Np + tok] = 0.0f;
-          l2[bh * Np + tok] = 0.0f;
+          l2[bh * Np + tok] = PAD_L2;
         }
       }
     }
@@ -315,14 +326,11 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
   for (int n = 0; n < T::NN; ++n) accK[n] = accV[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  // causal: query tiles from the one holding the block's first key; non-causal: every tile,
-  // starting at the block's own position and wrapping, so the blocks of a head spread out
+  // causal: query tiles from the one holding the block's first key; non-causal: every tile. The
+  // workgroups of a head run side by side on one XCD and walk the tiles in the same order, so
+  // each tile comes from HBM once and from that XCD's L2 for the others.
   const int qt0 = CAUSAL ? kb * (WB / BB) : 0, nit = nq - qt0;
-  const int st0 = CAUSAL ? qt0 : __builtin_amdgcn_readfirstlane((kb * (WB / BB)) % nq);
-  auto tile_of = [&](int it) {
-    const int t = st0 + it;
-    return CAUSAL ? t : (t >= nq ? t - nq : t);
-  };
+  auto tile_of = [&](int it) { return qt0 + it; };
   auto issue = [&](int it, uint8_t* buf) {
     const int qt = tile_of(it), t0 = qt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
@@ -366,12 +374,13 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
       }
       const v4f L4 = *reinterpret_cast<const v4f*>(buf + O_L + 4 * (16 * s + 4 * g));
       const v4f D4 = *reinterpret_cast<const v4f*>(buf + O_D + 4 * (16 * s + 4 * g));
+      // queries past N have L = PAD_L2 (P = 0); keys past N only reach their own dK and dV rows,
+      // which are not stored: only the causal test remains
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qi = q0 + 16 * s + 4 * g + i;
-        const bool ok = qi < N && key < N && (!CAUSAL || key <= qi);
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -L4[i]));
-        const float p = ok ? e : 0.0f;
+        const float p = (!CAUSAL || key <= qi) ? e : 0.0f;
         P[s][i] = p;
         dS[s][i] = p * (dp[i] - D4[i]);
         pmax = fmaxf(pmax, p);
@@ -380,10 +389,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
     }
     pmax = xg_max(pmax);
     smax = xg_max(smax);
-    const v4i aP = codes16(P, pmax > 0.0f ? div_rn(127.0f, pmax) : 0.0f);
-    const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
-    const float sP = pmax > 0.0f ? div_rn(pmax, 127.0f) : 0.0f;
-    const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
+    const v4i aP = codes16(P, recip127(pmax));
+    const v4i aS = codes16(dS, recip127(smax));
+    const float sP = pmax * INV127, sS = smax * INV127;
     // the accumulator rows are keys 16 * wave + 4g + i; lane 4g + i holds their scales
     float rP[4], rS[4];
 #pragma unroll
@@ -465,13 +473,10 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
   for (int n = 0; n < T::NN; ++n) acc[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  // causal: key tiles up to the one holding the block's last query
+  // causal: key tiles up to the one holding the block's last query; all blocks walk the tiles
+  // in the same order (L2 reuse, as in the dK/dV kernel)
   const int nit = CAUSAL ? min(nk, (qb * WB + WB - 1) / BB + 1) : nk;
-  const int st0 = CAUSAL ? 0 : __builtin_amdgcn_readfirstlane((qb * (WB / BB)) % nk);
-  auto tile_of = [&](int it) {
-    const int t = st0 + it;
-    return CAUSAL ? t : (t >= nk ? t - nk : t);
-  };
+  auto tile_of = [&](int it) { return it; };
   auto issue = [&](int it, uint8_t* buf) {
     const int kt = tile_of(it), t0 = kt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
@@ -519,8 +524,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
         }
       }
       smax = xg_max(smax);
-      const v4i aS = codes16(dS, smax > 0.0f ? div_rn(127.0f, smax) : 0.0f);
-      const float sS = smax > 0.0f ? div_rn(smax, 127.0f) : 0.0f;
+      const v4i aS = codes16(dS, recip127(smax));
+      const float sS = smax * INV127;
       float rS[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rS[i] = __shfl(sS, 4 * g + i);

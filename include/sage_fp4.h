@@ -173,7 +173,7 @@ size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D);
  *                        Q^, K^ and dO, each [B,H,D,Np64] with the tokens of every 64-token
  *                        block in slot order (slot 16g + 4s + i holds token 16s + 4g + i, zero
  *                        past N); their scales, fp32 [B,H,Np64/64,D] each; D and lse*log2(e),
- *                        fp32 [B,H,Np64] each (zero past N).
+ *                        fp32 [B,H,Np64] each (past N: 0 and 1e30).
  *                        Calls that share a workspace must not overlap.
  * Errors as for the forward; a workspace below the needed size is SAGE_ERR_WORKSPACE. Five
  * kernel launches on `stream` (three operand preparations, dK/dV, dQ); no atomics, so results
