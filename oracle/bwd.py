@@ -102,7 +102,54 @@ def _near_half(u: np.ndarray, e: np.ndarray) -> np.ndarray:
     return np.abs(np.abs(u - np.floor(u)) - 0.5) <= e
 
 
-def _head(Qh, Kh, V, O, dO, lse, N, D, c, causal, quantize, want_bounds):
+def _ambiguous(eX, u, sc):
+    """Codes whose scaled value u lies within its float32 error of a half-integer. eX: the
+    error bound of each encoded value; sc: the per-(row, block) scales."""
+    R, C = eX.shape
+    a = 127.0 * np.repeat(sc, QB, axis=1)            # block maximum of each element
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ra = np.where(a > 0, 127.0 / a, 0.0)
+        emax = np.repeat(np.max(eX.reshape(R, C // QB, QB), axis=2), QB, axis=1)
+        e = eX * ra + np.abs(u) * emax * ra / 127.0 + 2.0 ** -21 * np.abs(u)
+    return _near_half(u.astype(np.float64), e) & (a > 0)
+
+
+def _el(sc):
+    return np.repeat(sc, QB, axis=1)
+
+
+def _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, I, J, want_bounds):
+    """S, P, dP, dS of query rows I and key columns J (index arrays over the padded tokens), and
+    with want_bounds the float32 error bounds of P and dS: dot products of D exact terms
+    (error <= D 2^-24 sum|terms|), exp of an argument near |c S| + |lse|, a factor 4 of margin."""
+    i = I[:, None]
+    j = J[None, :]
+    vis = (i < N) & (j < N)
+    if causal:
+        vis &= j <= i
+    S = Qp[I] @ Kp[J].T
+    with np.errstate(over="ignore"):
+        P = np.where(vis, np.exp(np.where(vis, c * S - lsep[I][:, None], -np.inf)), 0.0)
+    dP = dOp[I] @ Vp[J].T
+    Dl = np.sum(dOp[I] * Op[I], axis=1)
+    dS = P * (dP - Dl[:, None])
+    if not want_bounds:
+        return P, dS, None, None
+    g = D * 2.0 ** -24
+    aQ, aK, aV, aO, adO = np.abs(Qp[I]), np.abs(Kp[J]), np.abs(Vp[J]), np.abs(Op[I]), np.abs(dOp[I])
+    relP = 4.0 * (c * g * (aQ @ aK.T) + 2.0 ** -22 * (np.abs(c * S) + np.abs(lsep[I][:, None]) + 1.0) + 2.0 ** -21)
+    eP = np.where(vis, P * relP, 0.0)
+    edS = 4.0 * (P * (g * (adO @ aV.T) + g * np.sum(adO * aO, axis=1)[:, None]) + np.abs(dS) * relP)
+    edS = np.where(vis, edS + 2.0 ** -22 * np.abs(dS), 0.0)
+    return P, dS, eP, edS
+
+
+def _head(Qh, Kh, V, O, dO, lse, N, D, c, causal, quantize, want_bounds, keys=None, queries=None):
+    """One head. keys / queries: None for all, else the token indices whose dK, dV (keys) and dQ
+    (queries) are wanted. A key's gradients need only its column of S (over all queries) and a
+    query's only its row, and every INT8 scale of P and dS belongs to one row of its operand, so
+    selected gradients come out exactly as in the full computation (their slack and mag up to
+    float64 summation order)."""
     Np = -(-N // QB) * QB
     pad = Np - N
 
@@ -111,73 +158,50 @@ def _head(Qh, Kh, V, O, dO, lse, N, D, c, causal, quantize, want_bounds):
 
     Qp, Kp, Vp, Op, dOp = (padr(X) for X in (Qh, Kh, V, O, dO))
     lsep = np.pad(lse, (0, pad))
-    i = np.arange(Np)[:, None]
-    j = np.arange(Np)[None, :]
-    vis = (i < N) & (j < N)
-    if causal:
-        vis &= j <= i
-    S = Qp @ Kp.T
-    with np.errstate(over="ignore"):
-        P = np.where(vis, np.exp(np.where(vis, c * S - lsep[:, None], -np.inf)), 0.0)
-    dP = dOp @ Vp.T
-    Dl = np.sum(dOp * Op, axis=1)
-    dS = P * (dP - Dl[:, None])
+    every = np.arange(Np)
+    J = every if keys is None else np.asarray(keys, np.int64)
+    I = every if queries is None else np.asarray(queries, np.int64)
     if not quantize:
-        dV = P.T @ dOp
-        dK = c * (dS.T @ Qp)
-        dQ = c * (dS @ Kp)
-        return dQ[:N], dK[:N], dV[:N], None
+        Pc, dSc, _, _ = _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, every, J, False)
+        _, dSr, _, _ = _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, I, every, False)
+        dV = Pc.T @ dOp
+        dK = c * (dSc.T @ Qp)
+        dQ = c * (dSr @ Kp)
+        if keys is None and queries is None:
+            return dQ[:N], dK[:N], dV[:N], None
+        return dQ, dK, dV, None
 
     Qt, sQ = q8_tokens(Qh)                       # [D, Np], per (channel, query block)
     Kt, sK = q8_tokens(Kh)
     dOt, sdO = q8_tokens(dO)
-    Pk, sPk, uP = q8_rows(P.T)                   # P^T [keys, queries], per (key, query block)
-    dSk, sSk, uk = q8_rows(dS.T)                 # dS^T [keys, queries], per (key, query block)
-    dSq, sSq, uq = q8_rows(dS)                   # dS [queries, keys], per (query, key block)
+    # keys J: columns of S over every query
+    Pc, dSc, ePc, edSc = _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, every, J, want_bounds)
+    Pk, sPk, uP = q8_rows(Pc.T)                  # P^T [keys, queries], per (key, query block)
+    dSk, sSk, uk = q8_rows(dSc.T)                # dS^T [keys, queries], per (key, query block)
     dV = _int8_mm(Pk, sPk, dOt, sdO)
     dK = c * _int8_mm(dSk, sSk, Qt, sQ)
+    # queries I: rows of S over every key
+    _, dSr, _, edSr = _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, I, every, want_bounds)
+    dSq, sSq, uq = q8_rows(dSr)                  # dS [queries, keys], per (query, key block)
     dQ = c * _int8_mm(dSq, sSq, Kt, sK)
     bounds = None
     if want_bounds:
-        # float32 error estimates of the values a kernel rounds: dot products of D exact terms
-        # (error <= D 2^-24 sum|terms|), exp of an argument near |c S| + |lse|, with a factor 4
-        # of margin; the ambiguity test then asks whether a code's scaled value lies within
-        # that error of a rounding boundary
-        g = D * 2.0 ** -24
-        aQ, aK, aV, aO, adO = (np.abs(X) for X in (Qp, Kp, Vp, Op, dOp))
-        relP = 4.0 * (c * g * (aQ @ aK.T) + 2.0 ** -22 * (np.abs(c * S) + np.abs(lsep[:, None]) + 1.0) + 2.0 ** -21)
-        eP = np.where(vis, P * relP, 0.0)
-        edS = 4.0 * (P * (g * (adO @ aV.T) + g * np.sum(adO * aO, axis=1)[:, None]) + np.abs(dS) * relP)
-        edS = np.where(vis, edS + 2.0 ** -22 * np.abs(dS), 0.0)
-
-        def ambiguous(eX, u, sc):
-            R, C = eX.shape
-            a = 127.0 * np.repeat(sc, QB, axis=1)            # block maximum of each element
-            with np.errstate(divide="ignore", invalid="ignore"):
-                ra = np.where(a > 0, 127.0 / a, 0.0)
-                emax = np.repeat(np.max(eX.reshape(R, C // QB, QB), axis=2), QB, axis=1)
-                e = eX * ra + np.abs(u) * emax * ra / 127.0 + 2.0 ** -21 * np.abs(u)
-            return _near_half(u.astype(np.float64), e) & (a > 0)
-
-        def el(sc):
-            return np.repeat(sc, QB, axis=1)
-
-        ambP = ambiguous(eP.T, uP, sPk)                   # [keys, queries]
-        ambK = ambiguous(edS.T, uk, sSk)                  # [keys, queries]
-        ambQ = ambiguous(edS, uq, sSq)                    # [queries, keys]
-        wdO = (np.abs(dOt) * el(sdO)).T                   # [Np, D]
-        wQ = (np.abs(Qt) * el(sQ)).T
-        wK = (np.abs(Kt) * el(sK)).T
-        slack_dV = (ambP * el(sPk)) @ wdO
-        slack_dK = c * ((ambK * el(sSk)) @ wQ)
-        slack_dQ = c * ((ambQ * el(sSq)) @ wK)
-        mag_dV = (np.abs(Pk) * el(sPk)) @ wdO
-        mag_dK = c * ((np.abs(dSk) * el(sSk)) @ wQ)
-        mag_dQ = c * ((np.abs(dSq) * el(sSq)) @ wK)
-        bounds = dict(slack=(slack_dQ[:N], slack_dK[:N], slack_dV[:N]),
-                      mag=(mag_dQ[:N], mag_dK[:N], mag_dV[:N]),
+        ambP = _ambiguous(ePc.T, uP, sPk)                 # [keys, queries]
+        ambK = _ambiguous(edSc.T, uk, sSk)                # [keys, queries]
+        ambQ = _ambiguous(edSr, uq, sSq)                  # [queries, keys]
+        wdO = (np.abs(dOt) * _el(sdO)).T                  # [Np, D]
+        wQ = (np.abs(Qt) * _el(sQ)).T
+        wK = (np.abs(Kt) * _el(sK)).T
+        bounds = dict(slack=[c * ((ambQ * _el(sSq)) @ wK), c * ((ambK * _el(sSk)) @ wQ), (ambP * _el(sPk)) @ wdO],
+                      mag=[c * ((np.abs(dSq) * _el(sSq)) @ wK), c * ((np.abs(dSk) * _el(sSk)) @ wQ),
+                           (np.abs(Pk) * _el(sPk)) @ wdO],
                       n_amb=(int(ambQ.sum()), int(ambK.sum()), int(ambP.sum())))
-    return dQ[:N], dK[:N], dV[:N], bounds
+    if keys is None and queries is None:
+        if bounds is not None:
+            bounds["slack"] = tuple(x[:N] for x in bounds["slack"])
+            bounds["mag"] = tuple(x[:N] for x in bounds["mag"])
+        return dQ[:N], dK[:N], dV[:N], bounds
+    return dQ, dK, dV, bounds
 
 
 def attn_bwd(fmt, q, k, v, o, do, lse, causal=False, sm_scale=0.0, heads=None, quantize=True,
@@ -213,3 +237,22 @@ def attn_bwd(fmt, q, k, v, o, do, lse, causal=False, sm_scale=0.0, heads=None, q
     if want_bounds:
         return tuple(out), dict(slack=tuple(sl), mag=tuple(mg), n_amb=tuple(namb))
     return tuple(out)
+
+
+def attn_bwd_sampled(fmt, q, k, v, o, do, lse, head, keys, queries, causal=False, sm_scale=0.0,
+                     want_bounds=True):
+    """The same gradients for one head (b, h) at selected tokens, without forming N x N arrays:
+    dK and dV of `keys` and dQ of `queries` (token indices < N). Returns (dq [len(queries), D],
+    dk [len(keys), D], dv [len(keys), D]) and, with want_bounds, the matching slack / mag."""
+    fq = MXFP4 if fmt == MX4_PV8 else fmt
+    B, H, N, D = v.shape
+    b, h = head
+    c = float(np.float32(1.0 / np.sqrt(D))) if sm_scale <= 0 else float(np.float32(sm_scale))
+    Qh = dequant(fq, q[0][b, h], q[1][b, h])
+    Kh = dequant(fq, k[0][b, h], k[1][b, h])
+    V, O, dO = (np.asarray(X[b, h], np.float64) for X in (v, o, do))
+    L = np.asarray(lse[b, h], np.float64)
+    r = _head(Qh, Kh, V, O, dO, L, N, D, c, causal, True, want_bounds, keys=keys, queries=queries)
+    if want_bounds:
+        return r[:3], dict(slack=tuple(r[3]["slack"]), mag=tuple(r[3]["mag"]), n_amb=r[3]["n_amb"])
+    return r[:3]

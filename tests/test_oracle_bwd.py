@@ -226,3 +226,23 @@ def test_float32_twin_within_slack(fmt, N, D, causal):
         bound = bd["slack"][t][0, 0] + 1e-4 * bd["mag"][t][0, 0] + 1e-30
         assert np.all(np.abs(got - ref) <= bound), (t, np.max(np.abs(got - ref) / bound))
     assert all(n < 0.1 * N * N for n in bd["n_amb"])
+
+
+@pytest.mark.parametrize("fmt,N,D,causal", [(orc.NVFP4, 200, 64, True), (orc.MXFP4, 130, 128, False)])
+def test_sampled_mode_matches_full(fmt, N, D, causal):
+    """Selected keys and queries (the mode used at sizes where N x N arrays do not fit) give the
+    full computation's gradients bit for bit, and its bounds to float64 summation order."""
+    q, k, v, do, Q, K = _setup(fmt, N, D, causal)
+    o, lse = orc.attn_fwd(fmt, Q, K, orc.quant(orc.ROLE_V, fmt, v), q.shape, causal=causal, want_lse=True)
+    o = o.astype(np.float16)
+    lse = lse.astype(np.float32).reshape(q.shape[:3])
+    full, bd = bwd.attn_bwd(fmt, Q, K, v, o, do, lse, causal=causal, want_bounds=True)
+    keys = np.array([0, 5, 63, 64, N - 1])
+    qs = np.array([1, 64, 100, N - 1])
+    (sq, sk, sv), sb = bwd.attn_bwd_sampled(fmt, Q, K, v, o, do, lse, (0, 1), keys, qs, causal=causal)
+    assert np.array_equal(sq, full[0][0, 1][qs])
+    assert np.array_equal(sk, full[1][0, 1][keys]) and np.array_equal(sv, full[2][0, 1][keys])
+    for t, rows in ((0, qs), (1, keys), (2, keys)):
+        for part in ("slack", "mag"):
+            ref = bd[part][t][0, 1][rows]
+            np.testing.assert_allclose(sb[part][t], ref, rtol=1e-12, atol=1e-15 * max(1.0, np.abs(ref).max()))
