@@ -33,8 +33,9 @@ Everything else is float64: S, P, dP, D and dS from the exact operands, so a cor
 differs only by its float32 rounding, except where a rounding decision (a P or dS code) lies
 within that rounding of its boundary. With ``want_bounds`` the oracle returns, per output
 element, ``slack``: the sum of the largest effect of every such ambiguous decision (the
-kernel may round it either way), and ``mag``: the sum of the magnitudes of the terms of the
-element, on which a float32 tolerance is scaled.
+kernel may round it either way), of the scale's own float32 error, and of whole blocks whose
+maximum is itself at rounding-noise level (``_slack_mag``), and ``mag``: the sum of the
+magnitudes of the terms of the element, on which a float32 tolerance is scaled.
 """
 from __future__ import annotations
 
@@ -118,6 +119,30 @@ def _el(sc):
     return np.repeat(sc, QB, axis=1)
 
 
+def _slack_mag(X, eX, codes, sc, u, wB):
+    """Slack and magnitude of an INT8 matmul's outputs. X [R, C]: the encoded operand's values
+    (rows are the scale owners), eX: their float32 error bounds, codes / sc / u: its encoding,
+    wB [C, D]: |B codes| times B's scales. Per (row, block), with a the block maximum and emax
+    the largest error in the block:
+      - rel = emax / a > 1/254: the kernel's scale may differ enough to move a code by half a
+        step or more (the maximum is near rounding-noise level, e.g. a causal row whose dS
+        cancels to zero), so each element contributes up to 2 (|x| + e + (a + emax) / 127) |B|;
+      - otherwise a code moves by at most |u| rel <= half a step, i.e. only a code within
+        its error (which includes |u| rel) of a half-integer may move, by one step; and the
+        kernel's scale may differ by rel, which moves every term by rel of itself.
+    Returns (slack [R, D], mag [R, D], number of ambiguous codes, number of noise-level blocks)."""
+    R, C = X.shape
+    a = 127.0 * _el(sc)
+    emax = np.repeat(np.max(eX.reshape(R, C // QB, QB), axis=2), QB, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(a > 0, emax / a, np.where(emax > 0, np.inf, 0.0))
+    noisy = rel > 1.0 / 254.0
+    amb = _ambiguous(eX, u, sc) & ~noisy
+    term = np.abs(codes) * _el(sc)
+    w = np.where(noisy, 2.0 * (np.abs(X) + eX + (a + emax) / 127.0), amb * _el(sc) + np.where(noisy, 0.0, rel) * term)
+    return w @ wB, term @ wB, int(amb.sum()), int(noisy.sum()) // QB
+
+
 def _block(Qp, Kp, Vp, Op, dOp, lsep, N, D, c, causal, I, J, want_bounds):
     """S, P, dP, dS of query rows I and key columns J (index arrays over the padded tokens), and
     with want_bounds the float32 error bounds of P and dS: dot products of D exact terms
@@ -186,16 +211,14 @@ def _head(Qh, Kh, V, O, dO, lse, N, D, c, causal, quantize, want_bounds, keys=No
     dQ = c * _int8_mm(dSq, sSq, Kt, sK)
     bounds = None
     if want_bounds:
-        ambP = _ambiguous(ePc.T, uP, sPk)                 # [keys, queries]
-        ambK = _ambiguous(edSc.T, uk, sSk)                # [keys, queries]
-        ambQ = _ambiguous(edSr, uq, sSq)                  # [queries, keys]
         wdO = (np.abs(dOt) * _el(sdO)).T                  # [Np, D]
         wQ = (np.abs(Qt) * _el(sQ)).T
         wK = (np.abs(Kt) * _el(sK)).T
-        bounds = dict(slack=[c * ((ambQ * _el(sSq)) @ wK), c * ((ambK * _el(sSk)) @ wQ), (ambP * _el(sPk)) @ wdO],
-                      mag=[c * ((np.abs(dSq) * _el(sSq)) @ wK), c * ((np.abs(dSk) * _el(sSk)) @ wQ),
-                           (np.abs(Pk) * _el(sPk)) @ wdO],
-                      n_amb=(int(ambQ.sum()), int(ambK.sum()), int(ambP.sum())))
+        sV, mV, aV, nV = _slack_mag(Pc.T, ePc.T, Pk, sPk, uP, wdO)          # rows: keys
+        sK_, mK, aK, nK = _slack_mag(dSc.T, edSc.T, dSk, sSk, uk, wQ)       # rows: keys
+        sQ_, mQ, aQ, nQ = _slack_mag(dSr, edSr, dSq, sSq, uq, wK)           # rows: queries
+        bounds = dict(slack=[c * sQ_, c * sK_, sV], mag=[c * mQ, c * mK, mV],
+                      n_amb=(aQ, aK, aV), n_noisy_blocks=(nQ, nK, nV))
     if keys is None and queries is None:
         if bounds is not None:
             bounds["slack"] = tuple(x[:N] for x in bounds["slack"])
@@ -213,7 +236,8 @@ def attn_bwd(fmt, q, k, v, o, do, lse, causal=False, sm_scale=0.0, heads=None, q
     heads: None for all, or a list of (b, h) to compute (the others are returned as zeros).
     quantize=False: the same gradients with every matmul in float64 (no INT8 step).
     Returns (dq, dk, dv) float64 [B,H,N,D]; with want_bounds also a dict of per-element
-    'slack' and 'mag' tuples (dq, dk, dv) and the number of ambiguous codes 'n_amb'."""
+    'slack' and 'mag' tuples (dq, dk, dv), the number of ambiguous codes 'n_amb' and of
+    (row, block) encodings whose maximum is at rounding-noise level 'n_noisy_blocks'."""
     fq = MXFP4 if fmt == MX4_PV8 else fmt
     B, H, N, D = v.shape
     c = float(np.float32(1.0 / np.sqrt(D))) if sm_scale <= 0 else float(np.float32(sm_scale))
@@ -221,6 +245,7 @@ def attn_bwd(fmt, q, k, v, o, do, lse, causal=False, sm_scale=0.0, heads=None, q
     sl = [np.zeros((B, H, N, D)) for _ in range(3)] if want_bounds else None
     mg = [np.zeros((B, H, N, D)) for _ in range(3)] if want_bounds else None
     namb = [0, 0, 0]
+    nnoisy = [0, 0, 0]
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
         Qh = dequant(fq, q[0][b, h], q[1][b, h])
         Kh = dequant(fq, k[0][b, h], k[1][b, h])
@@ -234,8 +259,9 @@ def attn_bwd(fmt, q, k, v, o, do, lse, causal=False, sm_scale=0.0, heads=None, q
                 sl[t][b, h] = r[3]["slack"][t]
                 mg[t][b, h] = r[3]["mag"][t]
                 namb[t] += r[3]["n_amb"][t]
+                nnoisy[t] += r[3]["n_noisy_blocks"][t]
     if want_bounds:
-        return tuple(out), dict(slack=tuple(sl), mag=tuple(mg), n_amb=tuple(namb))
+        return tuple(out), dict(slack=tuple(sl), mag=tuple(mg), n_amb=tuple(namb), n_noisy_blocks=tuple(nnoisy))
     return tuple(out)
 
 
@@ -254,5 +280,6 @@ def attn_bwd_sampled(fmt, q, k, v, o, do, lse, head, keys, queries, causal=False
     L = np.asarray(lse[b, h], np.float64)
     r = _head(Qh, Kh, V, O, dO, L, N, D, c, causal, True, want_bounds, keys=keys, queries=queries)
     if want_bounds:
-        return r[:3], dict(slack=tuple(r[3]["slack"]), mag=tuple(r[3]["mag"]), n_amb=r[3]["n_amb"])
+        return r[:3], dict(slack=tuple(r[3]["slack"]), mag=tuple(r[3]["mag"]), n_amb=r[3]["n_amb"],
+                           n_noisy_blocks=r[3]["n_noisy_blocks"])
     return r[:3]

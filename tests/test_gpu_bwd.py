@@ -224,3 +224,63 @@ def test_bwd_stages_equal_full_call():
     torch.cuda.synchronize()
     for a, b in zip(full, outs):
         assert np.array_equal(a, b.cpu().numpy().astype(np.float64))
+
+
+def _reference_o_lse(Qh, Kh, V, c, causal, block=2048):
+    """Softmax output and row log-sum-exp of one head in float64 (torch on the CPU), over query
+    blocks so no N x N array is formed: the exact statistic the forward's log-sum-exp defines,
+    used as the backward's O and lse input for both sides."""
+    import torch
+    Q, K, Vt = (torch.from_numpy(np.ascontiguousarray(x, np.float64)) for x in (Qh, Kh, V))
+    N = Q.shape[0]
+    O = torch.empty_like(Q[:, :Vt.shape[1]])
+    L = torch.empty(N, dtype=torch.float64)
+    for i0 in range(0, N, block):
+        S = c * (Q[i0:i0 + block] @ K.T)
+        if causal:
+            rows = torch.arange(i0, min(N, i0 + block))[:, None]
+            S = S.masked_fill(torch.arange(N)[None, :] > rows, float("-inf"))
+        L[i0:i0 + block] = torch.logsumexp(S, dim=1)
+        O[i0:i0 + block] = torch.softmax(S, dim=1) @ Vt
+    return O.numpy(), L.numpy()
+
+
+@pytest.mark.parametrize("wl", [3, 4])
+def test_bwd_large_workloads_sampled(wl):
+    """Workload 3 (B1 H48 N17776 D64, K with channel offsets) and workload 4 (B1 H32 N32768 D128
+    causal, +-20 outliers) at full size: every head runs on the GPU; one head gets a float64
+    reference O and lse, and its dK, dV at 192 keys and dQ at 192 queries (first, middle and
+    last 64 tokens) are checked against the oracle's sampled mode."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    cfg = synth.WORKLOADS[wl]
+    B, H, N, D, causal, fmt = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["causal"], orc.NVFP4
+    h = H - 1
+    say(f"bwd workload {wl} B{B} H{H} N{N} D{D} causal={causal}, oracle head {h}")
+    q, k, v = synth.make_qkv(wl)
+    do = synth.make_do(wl)
+    Qg, Kg, Vg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt), bnd.quant(to_gpu(v), 2, fmt)
+    og = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
+    lg = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    bnd.attn_fwd_into(fmt, Qg, Kg, Vg, (B, H, N, D), og, causal=causal, lse=lg)
+    # the checked head: the oracle's quantisation, a float64 reference O and lse
+    qs, ks, vs, dos = (x[:, h:h + 1] for x in (q, k, v, do))
+    Qs, Ks = orc.quant(0, fmt, qs), orc.quant(1, fmt, ks)
+    c = float(np.float32(1.0 / np.sqrt(D)))
+    O, L = _reference_o_lse(orc.dequant(fmt, *Qs)[0, 0], orc.dequant(fmt, *Ks)[0, 0],
+                            vs[0, 0].astype(np.float64), c, causal)
+    o_s = O.astype(np.float16)[None, None]
+    l_s = L.astype(np.float32)[None, None]
+    og[0, h] = torch.from_numpy(o_s[0, 0]).cuda()
+    lg[0, h] = torch.from_numpy(l_s[0, 0]).cuda()
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), og, to_gpu(do), lg, *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    for t in outs:
+        assert bool(torch.isfinite(t).all())
+    sel = np.concatenate([np.arange(64), np.arange(N // 2 - 32, N // 2 + 32), np.arange(N - 64, N)])
+    (rq, rk, rv), bd = obwd.attn_bwd_sampled(fmt, Qs, Ks, vs, o_s, dos, l_s, (0, 0), sel, sel, causal=causal)
+    say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
+    got = [outs[t][0, h].cpu().numpy().astype(np.float64)[sel] for t in range(3)]
+    _check_grads(got, (rq, rk, rv), dict(slack=bd["slack"], mag=bd["mag"]))
