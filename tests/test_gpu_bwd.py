@@ -166,17 +166,17 @@ def test_bwd_sm_scale():
     _check_grads([t.cpu().numpy().astype(np.float64) for t in outs], ref, bd)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_bwd_full_size_sampled_heads(causal):
-    """B4 H32 N4096 D128 (NVFP4), the size the benchmark times: every head runs on the GPU with
-    the GPU forward's O and lse, except two heads that get the oracle forward's; those two are
-    checked against the oracle in full."""
+@pytest.mark.parametrize("fmt,causal", [(orc.NVFP4, False), (orc.NVFP4, True), (orc.MXFP4, False)])
+def test_bwd_full_size_sampled_heads(fmt, causal):
+    """B4 H32 N4096 D128, the size the benchmark times: every head runs on the GPU with the GPU
+    forward's O and lse, except two heads that get the oracle forward's; those two are checked
+    against the oracle in full."""
     import torch
     from bit_attention_amd import binding as bnd
-    B, H, N, D, fmt = 4, 32, 4096, 128, orc.NVFP4
+    B, H, N, D = 4, 32, 4096, 128
     heads = [(0, 0), (3, 31)]
     flat = [b * H + h for b, h in heads]
-    say(f"bwd full size B{B} H{H} N{N} D{D} causal={causal}, oracle heads {heads}")
+    say(f"bwd full size B{B} H{H} N{N} D{D} fmt={fmt} causal={causal}, oracle heads {heads}")
     q, k, v = synth.make_qkv(2)
     do = synth.make_do(2)
     Qg = bnd.quant(to_gpu(q), 0, fmt)
