@@ -31,8 +31,6 @@
 //     waves per SIMD (at most 168 VGPRs).
 //   - dQ kernel: the mirror image, one wave per 16 queries looping over 64-key tiles. dQ gets
 //     a kernel of its own instead of atomic adds, so every result is deterministic.
-#include <type_traits>
-
 #include "device.h"
 
 namespace sage {
@@ -468,6 +466,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
     Lq = l2[bh * Np + query];
     Dq = dl[bh * Np + query];
   }
+  // keys visible to this lane's query: kj <= klim. A query past N has zero Q^ and dO rows (so S
+  // and dP are 0 and dS is 0) and its dQ row is not stored.
+  const int klim = CAUSAL ? min(query, N - 1) : N - 1;
   v4f acc[T::NN];
 #pragma unroll
   for (int n = 0; n < T::NN; ++n) acc[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -499,10 +500,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
     if (it + 1 < nit) issue(it + 1, lds[(it + 1) & 1]);
     const uint8_t* buf = lds[it & 1];
     const int k0 = tile_of(it) * BB;
-    // every (query, key) pair of the tile is visible: no per-element mask
-    const bool full = k0 + BB <= N && qb * WB + WB <= N && (!CAUSAL || k0 + BB - 1 <= qb * WB);
-    auto tile = [&](auto full_c) {
-      constexpr bool FULL = decltype(full_c)::value;
+    {
       float dS[4][4];
       float smax = 0.0f;
 #pragma unroll
@@ -516,9 +514,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kj = k0 + 16 * s + 4 * g + i;
-          const bool ok = FULL || (kj < N && query < N && (!CAUSAL || kj <= query));
           const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cl2e, -Lq));
-          const float p = ok ? e : 0.0f;
+          const float p = kj <= klim ? e : 0.0f;
           dS[s][i] = p * (dp[i] - Dq);
           smax = fmaxf(smax, fabsf(dS[s][i]));
         }
@@ -537,9 +534,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_fmaf((float)r[i], rS[i] * ck, acc[n][i]);
       }
-    };
-    if (full) tile(std::true_type{});
-    else tile(std::false_type{});
+    }
   }
 
 #pragma unroll
