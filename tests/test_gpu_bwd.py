@@ -284,3 +284,23 @@ def test_bwd_large_workloads_sampled(wl):
     say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
     got = [outs[t][0, h].cpu().numpy().astype(np.float64)[sel] for t in range(3)]
     _check_grads(got, (rq, rk, rv), dict(slack=bd["slack"], mag=bd["mag"]))
+
+
+def _random_cases(n=10, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.choice([orc.NVFP4, orc.MXFP4, orc.MX4_PV8])), int(rng.integers(1, 3)),
+                    int(rng.integers(1, 4)), int(rng.integers(1, 700)), int(rng.choice([64, 128])),
+                    bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("fmt,B,H,N,D,causal,out_f32", _random_cases())
+def test_bwd_random_shapes(fmt, B, H, N, D, causal, out_f32):
+    """Seeded random shapes, formats, masks and output types; every element checked."""
+    say(f"bwd random fmt={fmt} B={B} H={H} N={N} D={D} causal={causal} f32={out_f32}")
+    q, k, v, do, Q, K, o, lse = _inputs(fmt, B, H, N, D, causal)
+    got, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal, out_f32=out_f32)
+    ref, bd = obwd.attn_bwd(fmt, Q, K, v, o, do, lse, causal=causal, want_bounds=True)
+    _check_grads(got, ref, bd, f16_out=not out_f32)
