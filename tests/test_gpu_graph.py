@@ -1,8 +1,8 @@
 """The entry points inside a HIP graph: one step (three sage_fp4_quant launches and one attention
-launch) captured with torch.cuda.CUDAGraph and replayed several times, with eager work and
-synchronisations between the replays that change the inputs, must give exactly the eager results
-every time. The library allocates nothing, synchronises nothing and issues no memset, so each
-call is one kernel node."""
+launch, and in the training form also the backward's five launches) captured with
+torch.cuda.CUDAGraph and replayed several times, with eager work and synchronisations between the
+replays that change the inputs, must give exactly the eager results every time. The library
+allocates nothing, synchronises nothing and issues no memset, so each launch is one kernel node."""
 import numpy as np
 import pytest
 import torch
@@ -55,3 +55,52 @@ def test_graph_replays_match_eager(fmt, direct_p, causal):
         assert torch.equal(got_out, out), f"replay {r}: output differs from eager"
         assert torch.equal(got_lse, lse), f"replay {r}: lse differs from eager"
         assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("fmt,causal", [(bnd.NVFP4, True), (bnd.MXFP4, False)])
+def test_graph_training_step_replays_match_eager(fmt, causal):
+    """Forward with the row log-sum-exp and the 8-bit backward (three quantisations, one
+    attention launch, five backward launches) captured as one graph: every replay, with new
+    inputs and output gradients written between replays, equals the eager run bit for bit."""
+    B, H, N, D = 1, 4, 700, 128
+    shape = (B, H, N, D)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    q, k, v, do = (torch.randn(shape, generator=g, device="cuda").half() for _ in range(4))
+    Q, K, V = (bnd.alloc_quant(r, fmt, *shape) for r in (bnd.ROLE_Q, bnd.ROLE_K, bnd.ROLE_V))
+    out = torch.empty(shape, dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    grads = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+
+    def step():
+        bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
+        bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
+        bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
+        bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, lse=lse)
+        bnd.attn_bwd_into(fmt, Q, K, v, out, do, lse, *grads, ws, causal=causal)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for x in (q, k, v, do):
+            x.copy_(torch.randn(shape, generator=g, device="cuda").half())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in grads]
+        for t in grads:
+            t.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        say(f"  training-step replay {r}: fmt={fmt} causal={causal}")
+        for a, b in zip(got, grads):
+            assert torch.equal(a, b), f"replay {r}: gradients differ from eager"
+            assert bool(torch.isfinite(b).all())
