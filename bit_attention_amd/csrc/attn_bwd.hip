@@ -19,7 +19,8 @@
 //     from FP4 to bf16 (exact: a code times its scale has at most 6 significant bits and lies
 //     in bf16's exponent range), and Q^, K^ and dO are encoded to INT8 per (channel, block),
 //     stored channel-major in the token order below; the dO prep also forms D_i in fp32.
-//   - dK/dV kernel, one workgroup of 12 waves per (batch*head, 192-key block): each wave owns 16
+//   - dK/dV kernel, one workgroup of 12 (D = 128) or 16 (D = 64) waves per (batch*head, block of
+//     192 or 256 keys): each wave owns 16
 //     keys and keeps their K^ (bf16) and V (fp16) rows as MFMA B operands in registers while
 //     64-query tiles stream into LDS by asynchronous global-to-LDS copies (global_load_lds),
 //     double-buffered, one barrier per tile. S = Q^ K^T and dP = dO V^T take 16x16x32
@@ -28,7 +29,7 @@
 //     maximum takes two cross-lane swaps, and a lane's 16 codes are directly the A operand of a
 //     16x16x64 INT8 MFMA whose K slots 16g + 4s + i hold those queries; the INT8 dO and Q^ are
 //     stored in that slot order. One workgroup per CU (two 49 KB tile buffers at D = 128), three
-//     waves per SIMD (at most 168 VGPRs).
+//     waves per SIMD at D = 128 (at most 168 VGPRs), four at D = 64.
 //   - dQ kernel: the mirror image, one wave per 16 queries looping over 64-key tiles. dQ gets
 //     a kernel of its own instead of atomic adds, so every result is deterministic.
 #include "device.h"
@@ -191,9 +192,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
 // ---------------------------------------------------------------------------------------------
 // Shared pieces of the two gradient kernels.
 // ---------------------------------------------------------------------------------------------
-constexpr int NWAVE = 12;       // waves per workgroup: three per SIMD (at most 168 VGPRs), one
-                                // workgroup per CU (LDS)
-constexpr int WB = 16 * NWAVE;  // keys (dK/dV) or queries (dQ) per workgroup
+// Waves per workgroup, one workgroup per CU (LDS): three per SIMD at D = 128 (at most 168 VGPRs),
+// four at D = 64 (at most 128 VGPRs).
+template <int D>
+constexpr int nwave() { return D == 64 ? 16 : 12; }
+template <int D>
+constexpr int wblock() { return 16 * nwave<D>(); }  // keys (dK/dV) or queries (dQ) per workgroup
 
 template <int D>
 struct BwdTile {
@@ -282,16 +286,17 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK and dV: one workgroup of 12 waves per (batch*head, 192-key block); 64-query tiles arrive in
+// dK and dV: one workgroup of nwave<D>() waves per (batch*head, 16 nwave<D>()-key block); 64-query tiles arrive in
 // LDS through asynchronous copies, double-buffered: tile t + 1 is copied while tile t is used.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ q8, const float* __restrict__ q8s,
     const int8_t* __restrict__ do8, const float* __restrict__ do8s, const float* __restrict__ l2,
     const float* __restrict__ dl, int N, int Np, int BH, float c, void* __restrict__ dk, void* __restrict__ dv) {
   using T = BwdTile<D>;
+  constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
   constexpr int O_DO = T::T16, O_Q8 = 2 * T::T16, O_DO8 = O_Q8 + T::T8, O_QS = O_DO8 + T::T8;
   constexpr int O_DOS = O_QS + 4 * D, O_L = O_DOS + 4 * D, O_D = O_L + 4 * BB, BUF = O_D + 4 * BB;
   constexpr int NJ = 2 * T::W16 + 2 * T::W8 + 4;
@@ -426,16 +431,18 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup of 12 waves per (batch*head, 192-query block); 64-key tiles double-buffered
+// dQ: one workgroup of nwave<D>() waves per (batch*head, 16 nwave<D>()-query block); 64-key tiles
+// double-buffered
 // through asynchronous copies as in the dK/dV kernel.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(64 * NWAVE, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ k8, const float* __restrict__ k8s,
     const float* __restrict__ l2, const float* __restrict__ dl, int N, int Np, int BH, float c,
     void* __restrict__ dq) {
   using T = BwdTile<D>;
+  constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
   constexpr int O_V = T::T16, O_K8 = 2 * T::T16, O_KS = O_K8 + T::T8, BUF = O_KS + 4 * D;
   constexpr int NJ = 2 * T::W16 + T::W8 + 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
@@ -618,14 +625,15 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
     }
     bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, lse, l2, dl);
   }
+  constexpr int WB = wblock<D>();
   const int grid = BH * ((N + WB - 1) / WB);
 #define SAGE_BWD_LAUNCH(CZ, F32)                                                                          \
   do {                                                                                                    \
     if (stages & BWD_DKDV)                                                                                \
-      bwd_dkdv_kernel<D, CZ, F32><<<grid, 64 * NWAVE, 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, dl, N, \
+      bwd_dkdv_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, dl, N, \
                                                                Np, BH, c, dk, dv);                        \
     if (stages & BWD_DQ)                                                                                  \
-      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * NWAVE, 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, dq); \
+      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, dq); \
   } while (0)
   if (causal) {
     if (out_f32) SAGE_BWD_LAUNCH(true, true);
