@@ -329,11 +329,12 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   for (int n = 0; n < T::NN; ++n) accK[n] = accV[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const float cl2e = c * LOG2E;
 
-  // causal: query tiles from the one holding the block's first key; non-causal: every tile. The
-  // workgroups of a head run side by side on one XCD and walk the tiles in the same order, so
-  // each tile comes from HBM once and from that XCD's L2 for the others.
+  // causal: query tiles from the last down to the one holding the block's first key; non-causal:
+  // every tile. The workgroups of a head run side by side on one XCD and walk the tiles in the
+  // same order (causal blocks all start at the last tile), so each tile comes from HBM once and
+  // from that XCD's L2 for the others.
   const int qt0 = CAUSAL ? kb * (WB / BB) : 0, nit = nq - qt0;
-  auto tile_of = [&](int it) { return qt0 + it; };
+  auto tile_of = [&](int it) { return CAUSAL ? nq - 1 - it : it; };
   auto issue = [&](int it, uint8_t* buf) {
     const int qt = tile_of(it), t0 = qt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
