@@ -12,7 +12,8 @@
 // not contracted) and per 64-wide block of the contraction: P^T and dS^T per (key, 64-query
 // block), dS per (query, 64-key block), dO, Q^ and K^ per (channel, 64-token block). The 64
 // values x of one block, with a = max|x|, get the scale fl32(a / 127) and the codes
-// rne(fl32(x * fl32(127 / a))).
+// rne(fl32(x * fl32(127 / a))); the gradient kernels form P's and dS's within an ulp of these
+// (recip127, codes16).
 //
 // CDNA4 design.
 //   - prep kernels, one workgroup per (batch*head, 64-token block): Q^ and K^ are dequantised
@@ -20,11 +21,11 @@
 //     in bf16's exponent range), and Q^, K^ and dO are encoded to INT8 per (channel, block),
 //     stored channel-major in the token order below; the dO prep also forms D_i in fp32.
 //   - dK/dV kernel, one workgroup of 12 (D = 128) or 16 (D = 64) waves per (batch*head, block of
-//     192 or 256 keys): each wave owns 16
-//     keys and keeps their K^ (bf16) and V (fp16) rows as MFMA B operands in registers while
-//     64-query tiles stream into LDS by asynchronous global-to-LDS copies (global_load_lds),
-//     double-buffered, one barrier per tile. S = Q^ K^T and dP = dO V^T take 16x16x32
-//     MFMAs; a lane then holds 16 (query, key) values of one key, at queries 16s + 4g + i
+//     192 or 256 keys): each wave owns 16 keys and keeps their K^ (bf16) and V (fp16) rows as
+//     MFMA B operands in registers while 64-query tiles stream into LDS by asynchronous
+//     global-to-LDS copies (global_load_lds), double-buffered, one barrier per tile. S = Q^ K^T
+//     and dP = dO V^T take 16x16x32 MFMAs; a lane then holds 16 (query, key) values of one key,
+//     at queries 16s + 4g + i
 //     (subtile s, lane group g, element i). P and dS are therefore lane-local, a key's block
 //     maximum takes two cross-lane swaps, and a lane's 16 codes are directly the A operand of a
 //     16x16x64 INT8 MFMA whose K slots 16g + 4s + i hold those queries; the INT8 dO and Q^ are
@@ -182,7 +183,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
     for (int u = 0; u < PP / 16; ++u) {
       v4i wv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wv[e] = pack4(cq[16 * u + 4 * e], cq[16 * u + 4 * e + 1], cq[16 * u + 4 * e + 2], cq[16 * u + 4 * e + 3]);
+      for (int e = 0; e < 4; ++e) {
+        const int* c4 = cq + 16 * u + 4 * e;
+        wv[e] = pack4(c4[0], c4[1], c4[2], c4[3]);
+      }
       *reinterpret_cast<v4i*>(dst + 16 * u) = wv;
     }
     if (h == 0) q8s[(bh * nb + blk) * D + d] = a > 0.0f ? div_rn(a, 127.0f) : 0.0f;
@@ -262,7 +266,8 @@ __device__ __forceinline__ v4i read8(const uint8_t* tile, int d, int g, int sw8)
 // in the low mantissa bits; the low byte of the result's bits is the two's complement byte of
 // that integer. This is rne(fl32(x * r)) except when x * r lies within half an fp32 ulp of a
 // half-integer, where either rounding is within the contract. |x| <= the block maximum a and
-// r = fl32(127 / a) keep |x * r| below 127.5, so the code lies in [-127, 127] without a clamp.
+// r = recip127(a) (within a few ulp of 127 / a) keep |x * r| below 127.5, so the code lies in
+// [-127, 127] without a clamp.
 // v_perm_b32 gathers four bytes into one dword.
 __device__ __forceinline__ v4i codes16(const float (&x)[4][4], float r) {
   constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
@@ -286,8 +291,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK and dV: one workgroup of nwave<D>() waves per (batch*head, 16 nwave<D>()-key block); 64-query tiles arrive in
-// LDS through asynchronous copies, double-buffered: tile t + 1 is copied while tile t is used.
+// dK and dV: one workgroup of nwave<D>() waves per (batch*head, block of 16 nwave<D>() keys);
+// 64-query tiles arrive in LDS through asynchronous copies, double-buffered: tile t + 1 is copied
+// while tile t is used.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
@@ -308,7 +314,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   const int64_t bh = w / nkb;
   const int kb = w % nkb;  // causal: the heaviest key blocks (most query tiles) of a head first
   // the wave index is uniform across a wave: readfirstlane lets the copy schedule branch on scalars
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, col = l & 15;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 4, col = l & 15;
   const int key = kb * WB + wave * 16 + col;
   const int sw = swz16<D>(col), sw8 = swz8(col);
 
@@ -373,8 +380,10 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
       v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), kreg[kk], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_DO, 16 * s + col, kk, g, sw), vreg[kk], dp, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), kreg[kk], sc,
+                                                     0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_DO, 16 * s + col, kk, g, sw), vreg[kk],
+                                                    dp, 0, 0, 0);
       }
       const v4f L4 = *reinterpret_cast<const v4f*>(buf + O_L + 4 * (16 * s + 4 * g));
       const v4f D4 = *reinterpret_cast<const v4f*>(buf + O_D + 4 * (16 * s + 4 * g));
@@ -407,8 +416,10 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
     const float* os = reinterpret_cast<const float*>(buf + O_DOS);
 #pragma unroll
     for (int n = 0; n < T::NN; ++n) {
-      const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, read8(buf + O_DO8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
-      const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_Q8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
+      const v4i rv = __builtin_amdgcn_mfma_i32_16x16x64_i8(aP, read8(buf + O_DO8, 16 * n + col, g, sw8),
+                                                           v4i{0, 0, 0, 0}, 0, 0, 0);
+      const v4i rk = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_Q8, 16 * n + col, g, sw8),
+                                                           v4i{0, 0, 0, 0}, 0, 0, 0);
       const float co = os[16 * n + col], cq = qs[16 * n + col];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -432,9 +443,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup of nwave<D>() waves per (batch*head, 16 nwave<D>()-query block); 64-key tiles
-// double-buffered
-// through asynchronous copies as in the dK/dV kernel.
+// dQ: one workgroup of nwave<D>() waves per (batch*head, block of 16 nwave<D>() queries); 64-key
+// tiles double-buffered through asynchronous copies as in the dK/dV kernel.
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
@@ -453,7 +463,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
   const int w = xcd_work(blockIdx.x, BH * nqb);
   const int64_t bh = w / nqb;
   const int qb = CAUSAL ? nqb - 1 - w % nqb : w % nqb;  // causal: the heaviest query blocks first
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, col = l & 15;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 4, col = l & 15;
   const int query = qb * WB + wave * 16 + col;
   const int sw = swz16<D>(col), sw8 = swz8(col);
 
@@ -516,8 +527,10 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
         v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk) {
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), qreg[kk], sc, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_V, 16 * s + col, kk, g, sw), oreg[kk], dp, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), qreg[kk],
+                                                       sc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_V, 16 * s + col, kk, g, sw), oreg[kk],
+                                                      dp, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -537,7 +550,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
       const float* ks = reinterpret_cast<const float*>(buf + O_KS);
 #pragma unroll
       for (int n = 0; n < T::NN; ++n) {
-        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_K8, 16 * n + col, g, sw8), v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i r = __builtin_amdgcn_mfma_i32_16x16x64_i8(aS, read8(buf + O_K8, 16 * n + col, g, sw8),
+                                                            v4i{0, 0, 0, 0}, 0, 0, 0);
         const float ck = ks[16 * n + col];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[n][i] = __builtin_fmaf((float)r[i], rS[i] * ck, acc[n][i]);
@@ -618,11 +632,15 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
   const f16* doh = reinterpret_cast<const f16*>(dout);
   if (stages & BWD_PREP) {
     if (mx) {
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr, nullptr);
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr, nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr,
+                                                nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr,
+                                                nullptr);
     } else {
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr, nullptr);
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr, nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr,
+                                                nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr,
+                                                nullptr);
     }
     bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, lse, l2, dl);
   }
@@ -634,7 +652,8 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
       bwd_dkdv_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, dl, N, \
                                                                Np, BH, c, dk, dv);                        \
     if (stages & BWD_DQ)                                                                                  \
-      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, dq); \
+      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, \
+                                                                  dq);                                    \
   } while (0)
   if (causal) {
     if (out_f32) SAGE_BWD_LAUNCH(true, true);
@@ -654,8 +673,10 @@ hipError_t launch_attn_bwd(int stages, bool mx, const void* qc, const void* qs, 
                            bool causal, float c, void* dq, void* dk, void* dv, bool out_f32, void* ws,
                            hipStream_t st) {
   if (D == 64)
-    return launch_bwd_d<64>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
-  return launch_bwd_d<128>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws, st);
+    return launch_bwd_d<64>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws,
+                            st);
+  return launch_bwd_d<128>(stages, mx, qc, qs, kc, ks, v, o, dout, lse, BH, N, causal, c, dq, dk, dv, out_f32, ws,
+                           st);
 }
 
 }  // namespace sage
