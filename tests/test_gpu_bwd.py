@@ -304,3 +304,67 @@ def test_bwd_random_shapes(fmt, B, H, N, D, causal, out_f32):
     got, _, _ = _gpu_bwd(fmt, q, k, v, o, do, lse, causal, out_f32=out_f32)
     ref, bd = obwd.attn_bwd(fmt, Q, K, v, o, do, lse, causal=causal, want_bounds=True)
     _check_grads(got, ref, bd, f16_out=not out_f32)
+
+
+def test_bwd_most_heads():
+    """B*H = 65535 (the most the C ABI accepts) with a ragged N = 65: two heads, the first and the
+    last, get the oracle forward's O and lse and are checked in full."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    B, H, N, D, fmt = 1, 65535, 65, 64, orc.NVFP4
+    heads = [0, H - 1]
+    say(f"bwd limits: B*H={H} N={N} D={D}")
+    rng = np.random.default_rng(960)
+    q, k, v, do = (rng.standard_normal((B, H, N, D), dtype=np.float32).astype(np.float16) for _ in range(4))
+    Qg, Kg, Vg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt), bnd.quant(to_gpu(v), 2, fmt)
+    og = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
+    lg = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    bnd.attn_fwd_into(fmt, Qg, Kg, Vg, (B, H, N, D), og, lse=lg)
+    qs, ks, vs, dos = (x[:, heads] for x in (q, k, v, do))
+    Qs, Ks, Vs = orc.quant(0, fmt, qs), orc.quant(1, fmt, ks), orc.quant(2, fmt, vs)
+    o_s, l_s = orc.attn_fwd(fmt, Qs, Ks, Vs, qs.shape, want_lse=True)
+    o_s = o_s.astype(np.float16)
+    l_s = l_s.astype(np.float32).reshape(1, len(heads), N)
+    for u, h in enumerate(heads):
+        og[0, h] = torch.from_numpy(o_s[0, u]).cuda()
+        lg[0, h] = torch.from_numpy(l_s[0, u]).cuda()
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(B, H, N, D)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), og, to_gpu(do), lg, *outs, ws)
+    torch.cuda.synchronize()
+    for t in outs:
+        assert bool(torch.isfinite(t).all())
+    got = [t[:, heads].cpu().numpy().astype(np.float64) for t in outs]
+    ref, bd = obwd.attn_bwd(fmt, Qs, Ks, vs, o_s, dos, l_s, want_bounds=True)
+    _check_grads(got, ref, bd)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_longest_sequence(causal):
+    """N = 2^20 (the longest the C ABI accepts), one head, D = 64. The backward is defined for any
+    O and lse; at this size both sides get O = V and, per query, the Cauchy-Schwarz bound
+    c |Q^_i| max_j |K^_j| + ln N >= the true log-sum-exp (its exact value would take 2^40 dot
+    products). dK, dV at 64 keys and dQ at 64 queries (the first and last 32) are checked against
+    the oracle's sampled mode; every output must be finite."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    N, D, fmt = 1 << 20, 64, orc.NVFP4
+    say(f"bwd limits: N={N} D={D} causal={causal}")
+    rng = np.random.default_rng(970)
+    q, k, v, do = (rng.standard_normal((1, 1, N, D), dtype=np.float32).astype(np.float16) for _ in range(4))
+    Q, K = orc.quant(0, fmt, q), orc.quant(1, fmt, k)
+    Qh, Kh = orc.dequant(fmt, *Q)[0, 0], orc.dequant(fmt, *K)[0, 0]
+    c = float(np.float32(1.0 / np.sqrt(D)))
+    lse = (c * np.linalg.norm(Qh, axis=1) * np.linalg.norm(Kh, axis=1).max() + np.log(N)).astype(np.float32)
+    lse = lse.reshape(1, 1, N)
+    Qg, Kg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt)
+    outs = [torch.full((1, 1, N, D), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = bnd.alloc_bwd_workspace(1, 1, N, D)
+    bnd.attn_bwd_into(fmt, Qg, Kg, to_gpu(v), to_gpu(v), to_gpu(do), to_gpu(lse), *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    for t in outs:
+        assert bool(torch.isfinite(t).all())
+    sel = np.concatenate([np.arange(32), np.arange(N - 32, N)])
+    (rq, rk, rv), bd = obwd.attn_bwd_sampled(fmt, Q, K, v, v, do, lse, (0, 0), sel, sel, causal=causal)
+    got = [outs[t][0, 0].cpu().numpy().astype(np.float64)[sel] for t in range(3)]
+    _check_grads(got, (rq, rk, rv), dict(slack=bd["slack"], mag=bd["mag"]))
