@@ -9,6 +9,10 @@ Prints one JSON line. `value` = 4*B*H*N^2*D / (step time) in TOPS (whole step, q
 included); the attention kernel alone is reported in `attn_*` fields and `roofline`, timed with
 HIP events on the stream the kernels are launched on. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
+
+`--backward` times the 8-bit backward instead (sage_fp4_attn_bwd as its three stages, on the
+forward's FP4 Q/K, output and log-sum-exp): `value` = 10*B*H*N^2*D / (backward time), the
+roofline is that of its dK/dV kernel, and the CPU baseline is the backward oracle on one head.
 """
 from __future__ import annotations
 
@@ -441,7 +445,7 @@ def bench_backward(args, shape, fmt, torch, bnd, synth):
     st_ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(3)]
 
     pairs = B * H * N * N / (2 if causal else 1)                 # visible (query, key) pairs, tile-level
-    flops = 10.0 * B * H * N * N * D / (2 if causal else 1)      # dS-side: S, dP, dV, dK, dQ
+    flops = 10.0 * B * H * N * N * D / (2 if causal else 1)      # five matmuls (S, dP, dV, dK, dQ), 2D each
     value = flops / (ms_step * 1e-3) / 1e12
     # the dK/dV kernel: per pair S and dP at 16 bits (4D flops) and dV, dK on INT8 (4D ops)
     dkdv_ops = 8.0 * D * pairs
@@ -464,15 +468,18 @@ def bench_backward(args, shape, fmt, torch, bnd, synth):
         "flops_counted": flops, "roofline": roof,
     }
     torch.cuda.synchronize()
-    # accuracy: gradients of one head against float64 autograd of unquantised attention
+    # accuracy: gradients of one head against float64 autograd (CPU) of unquantised attention
     h0 = B * H - 1
-    import torch as T
-    qh, kh, vh, doh = (T.from_numpy(x.reshape(B * H, N, D)[h0].astype(np.float64)).requires_grad_(x is not do_np)
-                       for x in (q_np, k_np, v_np, do_np))
+
+    def head(x):
+        return torch.from_numpy(x.reshape(B * H, N, D)[h0].astype(np.float64))
+
+    qh, kh, vh = (head(x).requires_grad_(True) for x in (q_np, k_np, v_np))
+    doh = head(do_np)
     sc = (qh @ kh.T) / np.sqrt(D)
     if causal:
-        sc = sc.masked_fill(T.ones(N, N, dtype=T.bool).triu(1), float("-inf"))
-    (T.softmax(sc, -1) @ vh * doh).sum().backward()
+        sc = sc.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    (torch.softmax(sc, -1) @ vh * doh).sum().backward()
     for name, g, r in (("dq", grads[0], qh.grad), ("dk", grads[1], kh.grad), ("dv", grads[2], vh.grad)):
         a = g.view(B * H, N, D)[h0].double().cpu().numpy().reshape(-1)
         b = r.numpy().reshape(-1)
