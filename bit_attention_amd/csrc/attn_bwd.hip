@@ -71,15 +71,17 @@ __device__ __forceinline__ int pack4(int a, int b, int c, int d) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prep: one workgroup per (block of 64 tokens, batch*head). SRC 0: NVFP4 codes, 1: MXFP4 codes
-// (both also write the bf16 values), 2: fp16 dO (also writes D_i from dO and O, and lse * log2 e;
-// both [.., Np], past N 0 and PAD_L2). INT8 scales are stored block-major, [.., Np / 64, D].
+// Prep: one workgroup per (block of 64 tokens, batch*head). SRC 0: NVFP4 codes (also writes the
+// bf16 values), 1: MXFP4 codes (also writes the block's E8M0 scale table), 2: fp16 dO (also writes
+// D_i from dO and O, and lse * log2 e; both [.., Np], past N 0 and PAD_L2). INT8 scales are
+// stored block-major, [.., Np / 64, D].
 // ---------------------------------------------------------------------------------------------
 template <int D, int SRC>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const f16* __restrict__ x, const f16* __restrict__ o,
                                                        int N, int Np, __bf16* __restrict__ xh,
+                                                       uint8_t* __restrict__ tab,
                                                        int8_t* __restrict__ q8, float* __restrict__ q8s,
                                                        const float* __restrict__ lse, float* __restrict__ l2,
                                                        float* __restrict__ dl) {
@@ -139,13 +141,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
             v[8 * u + 2 * e + 1] = (float)h[e][1] * s;
           }
         }
-        __bf16* dst = xh + row * D + ch * VPT;
+        if constexpr (SRC == 0) {
+          __bf16* dst = xh + row * D + ch * VPT;
 #pragma unroll
-        for (int u = 0; u < VPT / 8; ++u) {
-          v8bf b;
+          for (int u = 0; u < VPT / 8; ++u) {
+            v8bf b;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = (__bf16)v[8 * u + e];
-          *reinterpret_cast<v8bf*>(dst + 8 * u) = b;
+            for (int e = 0; e < 8; ++e) b[e] = (__bf16)v[8 * u + e];
+            *reinterpret_cast<v8bf*>(dst + 8 * u) = b;
+          }
         }
       }
     } else {
@@ -162,6 +166,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict
     for (int u = 0; u < VPT; ++u) sx[n][ch * VPT + u] = v[u];
   }
   __syncthreads();
+
+  // MXFP4: the E8M0 scales of the block's 64 tokens in the order the gradient kernels read them
+  // (mx_tab_index), rows past N repeating row N - 1
+  if constexpr (SRC == 1) {
+    constexpr int NBD = D / 32;
+    if (tid < BB * NBD) {
+      const int gg = tid >> 6, cc = (tid >> 2) & 15, ss = tid & 3;
+      const int tok = min(blk * BB + 16 * ss + cc, N - 1);
+      tab[(bh * nb + blk) * (BB * NBD) + tid] = scales[(bh * N + tok) * NBD + gg];
+    }
+  }
 
   // channel phase: channel d, slots [h * PP, (h + 1) * PP)
   {
@@ -211,6 +226,9 @@ struct BwdTile {
   static constexpr int W8 = T8 / 1024;    // ... per INT8 tile
   static constexpr int KK = D / 32;       // k steps of the 16x16x32 MFMAs
   static constexpr int NN = D / 16;       // 16-channel output subtiles
+  static constexpr int T4 = BB * D / 2;   // bytes of an FP4 code tile (64 tokens x D / 2)
+  static constexpr int W4 = T4 / 1024;    // ... its wave-wide copies
+  static constexpr int TS = BB * D / 32;  // bytes of an MXFP4 scale table (64 tokens x D / 32)
 };
 
 // LDS tiles carry no padding. An MFMA operand read has 16 lanes fetch one 16-byte chunk from
@@ -260,6 +278,70 @@ __device__ __forceinline__ v4i read8(const uint8_t* tile, int d, int g, int sw8)
   return *reinterpret_cast<const v4i*>(tile + d * BB + 16 * (g ^ sw8));
 }
 
+// MXFP4 operands of the S recompute (MXFP4 Q and K): S = Q^ K^T runs on the block-scaled FP4
+// MFMA, whose lane (row c, group g) supplies the 32 E2M1 values of K block g of row c (16 bytes)
+// and their E8M0 scale. A 64-token tile keeps the codes, D / 2 bytes per row, with chunk c of
+// row r at slot c ^ swz4(r), which spreads the 16 rows a lane group reads over distinct bank
+// groups. The tile's scales come from the prep's table: byte 4 (16 g + c) + s holds the scale of
+// token 16 s + c, block g, so a lane's scales for the four subtiles are one dword, and the
+// instruction's op_sel picks byte s.
+struct Fp4Ops {
+  const uint8_t* qc;  // Q codes [BH, N, D/2] and E8M0 scales [BH, N, D/32]
+  const uint8_t* qs;
+  const uint8_t* kc;  // K codes and scales
+  const uint8_t* ks;
+  const uint8_t* qt;  // scale tables of Q and K [BH, Np/64, 64 D/32]
+  const uint8_t* kt;
+};
+template <int D>
+__device__ __forceinline__ int swz4(int r) { return D == 128 ? (r >> 2) & 3 : (r >> 3) & 1; }
+
+// Copy j of an FP4 code tile: rows [t0, t0 + 64) of one head of a [.., N, D/2] code array; a row
+// past N reads row N - 1.
+template <int D>
+__device__ __forceinline__ void copy4_job(int j, int lane, const uint8_t* head, int t0, int N, uint8_t* tile) {
+  constexpr int RB = D / 2, CPR = RB / 16, RPJ = 64 / CPR;  // row bytes, chunks per row, rows per copy
+  const int r = RPJ * j + lane / CPR, cs = lane % CPR;
+  const int row = min(t0 + r, N - 1);
+  lds_copy16(head + (int64_t)row * RB + 16 * (cs ^ swz4<D>(r)), tile + 1024 * j);
+}
+
+// FP4 MFMA A operand: the 16 code bytes of tile row r, K block g. At D = 64 the lane groups
+// g = 2, 3 repeat blocks 0, 1; the B operand is zero there, so their products vanish.
+template <int D>
+__device__ __forceinline__ v8i read4(const uint8_t* tile, int r, int g, int sw4) {
+  const v4i u = *reinterpret_cast<const v4i*>(tile + r * (D / 2) + 16 * ((g % (D / 32)) ^ sw4));
+  v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+  a[0] = u[0]; a[1] = u[1]; a[2] = u[2]; a[3] = u[3];
+  return a;
+}
+
+// S subtile s: A = FP4 tile rows with scale byte s of sa, B = the wave's own FP4 rows with scale
+// byte 0 of sb (s is a constant after unrolling).
+__device__ __forceinline__ v4f mfma_fp4(const v8i& a, const v8i& b, int s, int sa, int sb) {
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  switch (s) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 4, 1, sa, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 4, 2, sa, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 4, 3, sa, 0, sb);
+  }
+}
+
+// The B operand and scale of row `row` (< N) of an FP4 code array: 16 bytes of block g and its
+// E8M0 byte; zero codes (scale 1) for g >= D / 32.
+template <int D>
+__device__ __forceinline__ void own_fp4(const uint8_t* codes, const uint8_t* scales, int64_t row, int g, v8i& b,
+                                        int& sb) {
+  b = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  sb = 0x7F;
+  if (g < D / 32) {
+    const v4i u = *reinterpret_cast<const v4i*>(codes + row * (D / 2) + 16 * g);
+    b[0] = u[0]; b[1] = u[1]; b[2] = u[2]; b[3] = u[3];
+    sb = scales[row * (D / 32) + g];
+  }
+}
+
 // Codes of 16 values held by a lane (four subtiles s of four elements i) with a common
 // reciprocal scale r; byte 4s + i of the result is the code of value [s][i]. One fma adds
 // 1.5 * 2^23 to the exact product x * r, which rounds it to the nearest integer (ties to even)
@@ -295,17 +377,20 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // 64-query tiles arrive in LDS through asynchronous copies, double-buffered: tile t + 1 is copied
 // while tile t is used.
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MXS>
 __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ q8, const float* __restrict__ q8s,
     const int8_t* __restrict__ do8, const float* __restrict__ do8s, const float* __restrict__ l2,
-    const float* __restrict__ dl, int N, int Np, int BH, float c, void* __restrict__ dk, void* __restrict__ dv) {
+    const float* __restrict__ dl, int N, int Np, int BH, float c, void* __restrict__ dk, void* __restrict__ dv,
+    Fp4Ops f) {
   using T = BwdTile<D>;
   constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
   constexpr int O_DO = T::T16, O_Q8 = 2 * T::T16, O_DO8 = O_Q8 + T::T8, O_QS = O_DO8 + T::T8;
   constexpr int O_DOS = O_QS + 4 * D, O_L = O_DOS + 4 * D, O_D = O_L + 4 * BB, BUF = O_D + 4 * BB;
-  constexpr int NJ = 2 * T::W16 + 2 * T::W8 + 4;
+  // copies of the Q tile: bf16 rows, or (MXS) FP4 codes and one copy of the scale table
+  constexpr int JQ = MXS ? T::W4 + 1 : T::W16;
+  constexpr int NJ = JQ + T::W16 + 2 * T::W8 + 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
 
   const int nq = Np / BB;
@@ -317,17 +402,22 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 4, col = l & 15;
   const int key = kb * WB + wave * 16 + col;
-  const int sw = swz16<D>(col), sw8 = swz8(col);
+  const int sw = swz16<D>(col), sw8 = swz8(col), sw4 = swz4<D>(col);
 
-  v8bf kreg[T::KK];
+  v8bf kreg[MXS ? 1 : T::KK];
   v8h vreg[T::KK];
+  v8i kf = {0, 0, 0, 0, 0, 0, 0, 0};
+  int ksc = 0x7F;
+  if constexpr (MXS) {
+    if (key < N) own_fp4<D>(f.kc + bh * N * (D / 2), f.ks + bh * N * (D / 32), key, g, kf, ksc);
+  }
 #pragma unroll
   for (int kk = 0; kk < T::KK; ++kk) {
     if (key < N) {
-      kreg[kk] = *reinterpret_cast<const v8bf*>(kh + (bh * N + key) * D + 32 * kk + 8 * g);
+      if constexpr (!MXS) kreg[kk] = *reinterpret_cast<const v8bf*>(kh + (bh * N + key) * D + 32 * kk + 8 * g);
       vreg[kk] = *reinterpret_cast<const v8h*>(v + (bh * N + key) * D + 32 * kk + 8 * g);
     } else {
-      kreg[kk] = v8bf{};
+      if constexpr (!MXS) kreg[kk] = v8bf{};
       vreg[kk] = v8h{};
     }
   }
@@ -345,16 +435,21 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   auto issue = [&](int it, uint8_t* buf) {
     const int qt = tile_of(it), t0 = qt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
-      if (j < T::W16) {
-        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(qh + bh * N * D), t0, N, buf);
-      } else if (j < 2 * T::W16) {
-        copy16_job<D>(j - T::W16, l, reinterpret_cast<const uint8_t*>(dout + bh * N * D), t0, N, buf + O_DO);
-      } else if (j < 2 * T::W16 + T::W8) {
-        copy8_job(j - 2 * T::W16, l, q8 + bh * D * Np + t0, Np, buf + O_Q8);
-      } else if (j < 2 * T::W16 + 2 * T::W8) {
-        copy8_job(j - 2 * T::W16 - T::W8, l, do8 + bh * D * Np + t0, Np, buf + O_DO8);
+      if (j < JQ) {
+        if constexpr (MXS) {
+          if (j < T::W4) copy4_job<D>(j, l, f.qc + bh * N * (D / 2), t0, N, buf);
+          else if (l < T::TS / 16) lds_copy16(f.qt + (bh * nq + qt) * T::TS + 16 * l, buf + T::T4);
+        } else {
+          copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(qh + bh * N * D), t0, N, buf);
+        }
+      } else if (j < JQ + T::W16) {
+        copy16_job<D>(j - JQ, l, reinterpret_cast<const uint8_t*>(dout + bh * N * D), t0, N, buf + O_DO);
+      } else if (j < JQ + T::W16 + T::W8) {
+        copy8_job(j - JQ - T::W16, l, q8 + bh * D * Np + t0, Np, buf + O_Q8);
+      } else if (j < JQ + T::W16 + 2 * T::W8) {
+        copy8_job(j - JQ - T::W16 - T::W8, l, do8 + bh * D * Np + t0, Np, buf + O_DO8);
       } else {
-        const int k = j - 2 * T::W16 - 2 * T::W8;  // scales of Q8, of dO8; lse * log2(e); D
+        const int k = j - JQ - T::W16 - 2 * T::W8;  // scales of Q8, of dO8; lse * log2(e); D
         const float* src = k == 0 ? q8s + (bh * nq + qt) * D
                            : k == 1 ? do8s + (bh * nq + qt) * D
                            : k == 2 ? l2 + bh * Np + t0
@@ -375,13 +470,17 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
 
     float P[4][4], dS[4][4];
     float pmax = 0.0f, smax = 0.0f;
+    int qsc = 0;
+    if constexpr (MXS) qsc = *reinterpret_cast<const int*>(buf + T::T4 + 4 * (16 * (g % (D / 32)) + col));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (MXS) sc = mfma_fp4(read4<D>(buf, 16 * s + col, g, sw4), kf, s, qsc, ksc);
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), kreg[kk], sc,
-                                                     0, 0, 0);
+        if constexpr (!MXS)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), kreg[kk],
+                                                       sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_DO, 16 * s + col, kk, g, sw), vreg[kk],
                                                     dp, 0, 0, 0);
       }
@@ -446,16 +545,17 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
 // dQ: one workgroup of nwave<D>() waves per (batch*head, block of 16 nwave<D>() queries); 64-key
 // tiles double-buffered through asynchronous copies as in the dK/dV kernel.
 // ---------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MXS>
 __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
     const __bf16* __restrict__ qh, const __bf16* __restrict__ kh, const f16* __restrict__ v,
     const f16* __restrict__ dout, const int8_t* __restrict__ k8, const float* __restrict__ k8s,
     const float* __restrict__ l2, const float* __restrict__ dl, int N, int Np, int BH, float c,
-    void* __restrict__ dq) {
+    void* __restrict__ dq, Fp4Ops f) {
   using T = BwdTile<D>;
   constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
   constexpr int O_V = T::T16, O_K8 = 2 * T::T16, O_KS = O_K8 + T::T8, BUF = O_KS + 4 * D;
-  constexpr int NJ = 2 * T::W16 + T::W8 + 1;
+  constexpr int JK = MXS ? T::W4 + 1 : T::W16;  // copies of the K tile (as in the dK/dV kernel)
+  constexpr int NJ = JK + T::W16 + T::W8 + 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
 
   const int nk = Np / BB;
@@ -466,18 +566,23 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 4, col = l & 15;
   const int query = qb * WB + wave * 16 + col;
-  const int sw = swz16<D>(col), sw8 = swz8(col);
+  const int sw = swz16<D>(col), sw8 = swz8(col), sw4 = swz4<D>(col);
 
-  v8bf qreg[T::KK];
+  v8bf qreg[MXS ? 1 : T::KK];
   v8h oreg[T::KK];
+  v8i qf = {0, 0, 0, 0, 0, 0, 0, 0};
+  int qsc = 0x7F;
   float Lq = 0.0f, Dq = 0.0f;
+  if constexpr (MXS) {
+    if (query < N) own_fp4<D>(f.qc + bh * N * (D / 2), f.qs + bh * N * (D / 32), query, g, qf, qsc);
+  }
 #pragma unroll
   for (int kk = 0; kk < T::KK; ++kk) {
     if (query < N) {
-      qreg[kk] = *reinterpret_cast<const v8bf*>(qh + (bh * N + query) * D + 32 * kk + 8 * g);
+      if constexpr (!MXS) qreg[kk] = *reinterpret_cast<const v8bf*>(qh + (bh * N + query) * D + 32 * kk + 8 * g);
       oreg[kk] = *reinterpret_cast<const v8h*>(dout + (bh * N + query) * D + 32 * kk + 8 * g);
     } else {
-      qreg[kk] = v8bf{};
+      if constexpr (!MXS) qreg[kk] = v8bf{};
       oreg[kk] = v8h{};
     }
   }
@@ -500,12 +605,17 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
   auto issue = [&](int it, uint8_t* buf) {
     const int kt = tile_of(it), t0 = kt * BB;
     for (int j = wave; j < NJ; j += NWAVE) {
-      if (j < T::W16) {
-        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(kh + bh * N * D), t0, N, buf);
-      } else if (j < 2 * T::W16) {
-        copy16_job<D>(j - T::W16, l, reinterpret_cast<const uint8_t*>(v + bh * N * D), t0, N, buf + O_V);
-      } else if (j < 2 * T::W16 + T::W8) {
-        copy8_job(j - 2 * T::W16, l, k8 + bh * D * Np + t0, Np, buf + O_K8);
+      if (j < JK) {
+        if constexpr (MXS) {
+          if (j < T::W4) copy4_job<D>(j, l, f.kc + bh * N * (D / 2), t0, N, buf);
+          else if (l < T::TS / 16) lds_copy16(f.kt + (bh * nk + kt) * T::TS + 16 * l, buf + T::T4);
+        } else {
+          copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(kh + bh * N * D), t0, N, buf);
+        }
+      } else if (j < JK + T::W16) {
+        copy16_job<D>(j - JK, l, reinterpret_cast<const uint8_t*>(v + bh * N * D), t0, N, buf + O_V);
+      } else if (j < JK + T::W16 + T::W8) {
+        copy8_job(j - JK - T::W16, l, k8 + bh * D * Np + t0, Np, buf + O_K8);
       } else if (l < D / 4) {
         lds_copy16(k8s + (bh * nk + kt) * D + 4 * l, buf + O_KS);
       }
@@ -522,13 +632,17 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
     {
       float dS[4][4];
       float smax = 0.0f;
+      int ksc = 0;
+      if constexpr (MXS) ksc = *reinterpret_cast<const int*>(buf + T::T4 + 4 * (16 * (g % (D / 32)) + col));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         v4f sc = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (MXS) sc = mfma_fp4(read4<D>(buf, 16 * s + col, g, sw4), qf, s, ksc, qsc);
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk) {
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw), qreg[kk],
-                                                       sc, 0, 0, 0);
+          if constexpr (!MXS)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read16<D, v8bf>(buf, 16 * s + col, kk, g, sw),
+                                                         qreg[kk], sc, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_16x16x32_f16(read16<D, v8h>(buf + O_V, 16 * s + col, kk, g, sw), oreg[kk],
                                                       dp, 0, 0, 0);
         }
@@ -580,6 +694,8 @@ enum { BWD_PREP = 1, BWD_DKDV = 2, BWD_DQ = 4 };
 // Workspace layout (offsets in bytes, each 256-aligned; Np = ceil(N/64)*64, nb = Np/64):
 //   Q^ bf16 [BH,N,D] | K^ bf16 [BH,N,D] | Q8, K8, dO8 int8 [BH,D,Np] each |
 //   Q8, K8, dO8 scales fp32 [BH,nb,D] each | D fp32 [BH,Np] | lse * log2(e) fp32 [BH,Np]
+// With MXFP4 Q and K the first two regions start with their E8M0 scale tables instead,
+// [BH,nb,D/32,16,4] bytes each (byte [b][g][c][s]: token 64 b + 16 s + c, block g).
 struct BwdWs {
   int64_t qh, kh, q8, k8, do8, q8s, k8s, do8s, dl, l2, total;
 };
@@ -630,38 +746,49 @@ static hipError_t launch_bwd_d(int stages, bool mx, const void* qc, const void* 
   const f16* vh = reinterpret_cast<const f16*>(v);
   const f16* oh = reinterpret_cast<const f16*>(o);
   const f16* doh = reinterpret_cast<const f16*>(dout);
+  // MXFP4 Q and K: the first two regions hold their scale tables instead of bf16 values
+  uint8_t* qt = base + L.qh;
+  uint8_t* kt = base + L.kh;
+  const Fp4Ops f = {qcb, qsb, kcb, ksb, qt, kt};
   if (stages & BWD_PREP) {
     if (mx) {
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr,
-                                                nullptr);
-      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr,
-                                                nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, nullptr, qt, q8, q8s, nullptr,
+                                                nullptr, nullptr);
+      bwd_prep_kernel<D, 1><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, nullptr, kt, k8, k8s, nullptr,
+                                                nullptr, nullptr);
     } else {
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, q8, q8s, nullptr, nullptr,
-                                                nullptr);
-      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, k8, k8s, nullptr, nullptr,
-                                                nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(qcb, qsb, nullptr, nullptr, N, Np, qh, nullptr, q8, q8s, nullptr,
+                                                nullptr, nullptr);
+      bwd_prep_kernel<D, 0><<<pg, 256, 0, st>>>(kcb, ksb, nullptr, nullptr, N, Np, kh, nullptr, k8, k8s, nullptr,
+                                                nullptr, nullptr);
     }
-    bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, do8, do8s, lse, l2, dl);
+    bwd_prep_kernel<D, 2><<<pg, 256, 0, st>>>(nullptr, nullptr, doh, oh, N, Np, nullptr, nullptr, do8, do8s, lse,
+                                              l2, dl);
   }
   constexpr int WB = wblock<D>();
   const int grid = BH * ((N + WB - 1) / WB);
-#define SAGE_BWD_LAUNCH(CZ, F32)                                                                          \
-  do {                                                                                                    \
-    if (stages & BWD_DKDV)                                                                                \
-      bwd_dkdv_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, dl, N, \
-                                                               Np, BH, c, dk, dv);                        \
-    if (stages & BWD_DQ)                                                                                  \
-      bwd_dq_kernel<D, CZ, F32><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, BH, c, \
-                                                                  dq);                                    \
+#define SAGE_BWD_LAUNCH(CZ, F32, MXS)                                                                    \
+  do {                                                                                                   \
+    if (stages & BWD_DKDV)                                                                               \
+      bwd_dkdv_kernel<D, CZ, F32, MXS><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, q8, q8s, do8, do8s, l2, \
+                                                                         dl, N, Np, BH, c, dk, dv, f);   \
+    if (stages & BWD_DQ)                                                                                 \
+      bwd_dq_kernel<D, CZ, F32, MXS><<<grid, 64 * nwave<D>(), 0, st>>>(qh, kh, vh, doh, k8, k8s, l2, dl, N, Np, \
+                                                                       BH, c, dq, f);                    \
+  } while (0)
+#define SAGE_BWD_FMT(CZ, F32)               \
+  do {                                      \
+    if (mx) SAGE_BWD_LAUNCH(CZ, F32, true); \
+    else SAGE_BWD_LAUNCH(CZ, F32, false);   \
   } while (0)
   if (causal) {
-    if (out_f32) SAGE_BWD_LAUNCH(true, true);
-    else SAGE_BWD_LAUNCH(true, false);
+    if (out_f32) SAGE_BWD_FMT(true, true);
+    else SAGE_BWD_FMT(true, false);
   } else {
-    if (out_f32) SAGE_BWD_LAUNCH(false, true);
-    else SAGE_BWD_LAUNCH(false, false);
+    if (out_f32) SAGE_BWD_FMT(false, true);
+    else SAGE_BWD_FMT(false, false);
   }
+#undef SAGE_BWD_FMT
 #undef SAGE_BWD_LAUNCH
   return hipGetLastError();
 }

@@ -169,7 +169,10 @@ size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D);
  *   workspace            device memory of at least sage_fp4_attn_bwd_workspace_bytes(B,H,N,D)
  *                        bytes (workspace_bytes), 16-byte aligned, caller-owned; its contents
  *                        on entry are ignored, and on return it holds, at 256-byte aligned
- *                        offsets in this order: Q^ and K^ as bf16 [B,H,N,D]; the INT8 codes of
+ *                        offsets in this order: Q^ and K^ as bf16 [B,H,N,D] (with MXFP4 Q and
+ *                        K, these two regions begin instead with their E8M0 scales as
+ *                        [B,H,Np64/64,D/32,16,4] bytes, byte [b][g][c][s] belonging to token
+ *                        min(64b + 16s + c, N - 1), block g); the INT8 codes of
  *                        Q^, K^ and dO, each [B,H,D,Np64] with the tokens of every 64-token
  *                        block in slot order (slot 16g + 4s + i holds token 16s + 4g + i, zero
  *                        past N); their scales, fp32 [B,H,Np64/64,D] each; D and lse*log2(e),

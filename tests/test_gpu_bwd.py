@@ -88,6 +88,25 @@ def _ws_views(ws, B, H, N, D):
     return bf, i8, sc, dl, l2
 
 
+def _mx_table(ws, t, B, H, N, D):
+    """The MXFP4 scale table in workspace region t (0: Q, 1: K), [B, H, Np/64, D/32, 16, 4]."""
+    Np = -(-N // 64) * 64
+    off = 0 if t == 0 else (B * H * N * D * 2 + 255) // 256 * 256
+    n = B * H * Np * (D // 32)
+    return ws[off:off + n].view(np.uint8).reshape(B, H, Np // 64, D // 32, 16, 4)
+
+
+def _mx_table_expected(scales, N, D):
+    """Byte [b][g][c][s] is the E8M0 scale of token min(64 b + 16 s + c, N - 1), block g."""
+    sc = np.asarray(scales).view(np.uint8)
+    B, H = sc.shape[:2]
+    Np = -(-N // 64) * 64
+    tok = np.minimum(np.arange(Np), N - 1)
+    t = sc.reshape(B, H, N, D // 32)[:, :, tok, :]                  # [B, H, Np, D/32]
+    t = t.reshape(B, H, Np // 64, 4, 16, D // 32)                   # token 64 b + 16 s + c
+    return t.transpose(0, 1, 2, 5, 4, 3)                            # [b][g][c][s]
+
+
 CASES = [
     (orc.NVFP4, 1, 2, 256, 64, False),
     (orc.NVFP4, 2, 2, 200, 128, True),
@@ -110,12 +129,16 @@ def test_bwd_matches_oracle(fmt, B, H, N, D, causal):
     say(f"  ambiguous codes (dq, dk, dv): {bd['n_amb']}")
     _check_grads(got, ref, bd)
 
-    # the workspace: bf16 Q^, K^; INT8 codes and scales of Q^, K^, dO; D
+    # the workspace: bf16 Q^, K^ (NVFP4) or the E8M0 scale tables of Q, K (MXFP4); INT8 codes
+    # and scales of Q^, K^, dO; D
     fq = orc.MXFP4 if fmt == orc.MX4_PV8 else fmt
     bf, i8, sc, dl, l2 = _ws_views(ws, B, H, N, D)
     xs = (orc.dequant(fq, *Q), orc.dequant(fq, *K), do.astype(np.float64))
     for t in range(2):
-        assert np.array_equal(bf[t], xs[t].astype(np.float32))
+        if fq == orc.NVFP4:
+            assert np.array_equal(bf[t], xs[t].astype(np.float32))
+        else:
+            assert np.array_equal(_mx_table(ws, t, B, H, N, D), _mx_table_expected((Q, K)[t][1], N, D))
     for t in range(3):
         for b in range(B):
             for h in range(H):
