@@ -447,15 +447,19 @@ def bench_backward(args, shape, fmt, torch, bnd, synth):
     pairs = B * H * N * N / (2 if causal else 1)                 # visible (query, key) pairs, tile-level
     flops = 10.0 * B * H * N * N * D / (2 if causal else 1)      # five matmuls (S, dP, dV, dK, dQ), 2D each
     value = flops / (ms_step * 1e-3) / 1e12
-    # the dK/dV kernel: per pair S and dP at 16 bits (4D flops) and dV, dK on INT8 (4D ops)
+    # the dK/dV kernel, per pair: S (2D flops; bf16 MFMA for NVFP4 Q/K, the block-scaled FP4 MFMA
+    # for MXFP4 Q/K), dP at fp16 (2D) and dV, dK on INT8 (4D ops); the peak is the rate at which
+    # that mix would run with every unit at its dense peak
+    mx = args.fmt != "nvfp4"
     dkdv_ops = 8.0 * D * pairs
     dkdv_tops = dkdv_ops / (st_ms[1] * 1e-3) / 1e12
-    mixed = 2.0 / (1.0 / FP16_PEAK_TFLOPS + 1.0 / INT8_PEAK_TOPS)
-    kname = f"attn_bwd_dkdv_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
+    s_peak = FP4_PEAK_TOPS if mx else FP16_PEAK_TFLOPS
+    mixed = 8.0 / (2.0 / s_peak + 2.0 / FP16_PEAK_TFLOPS + 4.0 / INT8_PEAK_TOPS)
+    kname = f"attn_bwd_dkdv_{'mxfp4_' if mx else ''}b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
     roof = {"bound": "mfma", "achieved": dkdv_tops, "peak": mixed, "unit": "TFLOP/s",
             "frac": dkdv_tops / mixed, "traffic": load_traffic("attn_bwd.hip", kname),
-            "kernel": "bwd_dkdv_kernel (bf16/fp16 MFMA for S and dP, INT8 MFMA for dV and dK; peak "
-                      "= harmonic mean of the 16-bit and INT8 dense peaks, equal op counts)"}
+            "kernel": f"bwd_dkdv_kernel (S on the {'FP4' if mx else 'bf16'} MFMA, dP on fp16, dV and dK "
+                      "on INT8; peak = the op-weighted harmonic mean of those dense peaks)"}
     res = {
         "metric": BWD_METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
