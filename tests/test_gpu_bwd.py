@@ -329,14 +329,15 @@ def test_bwd_random_shapes(fmt, B, H, N, D, causal, out_f32):
     _check_grads(got, ref, bd, f16_out=not out_f32)
 
 
-def test_bwd_most_heads():
+@pytest.mark.parametrize("fmt", [orc.NVFP4, orc.MXFP4])
+def test_bwd_most_heads(fmt):
     """B*H = 65535 (the most the C ABI accepts) with a ragged N = 65: two heads, the first and the
     last, get the oracle forward's O and lse and are checked in full."""
     import torch
     from bit_attention_amd import binding as bnd
-    B, H, N, D, fmt = 1, 65535, 65, 64, orc.NVFP4
+    B, H, N, D = 1, 65535, 65, 64
     heads = [0, H - 1]
-    say(f"bwd limits: B*H={H} N={N} D={D}")
+    say(f"bwd limits: fmt={fmt} B*H={H} N={N} D={D}")
     rng = np.random.default_rng(960)
     q, k, v, do = (rng.standard_normal((B, H, N, D), dtype=np.float32).astype(np.float16) for _ in range(4))
     Qg, Kg, Vg = bnd.quant(to_gpu(q), 0, fmt), bnd.quant(to_gpu(k), 1, fmt), bnd.quant(to_gpu(v), 2, fmt)
@@ -362,8 +363,8 @@ def test_bwd_most_heads():
     _check_grads(got, ref, bd)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_bwd_longest_sequence(causal):
+@pytest.mark.parametrize("causal,fmt", [(False, orc.NVFP4), (True, orc.NVFP4), (True, orc.MXFP4)])
+def test_bwd_longest_sequence(causal, fmt):
     """N = 2^20 (the longest the C ABI accepts), one head, D = 64. The backward is defined for any
     O and lse; at this size both sides get O = V and, per query, the Cauchy-Schwarz bound
     c |Q^_i| max_j |K^_j| + ln N >= the true log-sum-exp (its exact value would take 2^40 dot
@@ -371,8 +372,8 @@ def test_bwd_longest_sequence(causal):
     the oracle's sampled mode; every output must be finite."""
     import torch
     from bit_attention_amd import binding as bnd
-    N, D, fmt = 1 << 20, 64, orc.NVFP4
-    say(f"bwd limits: N={N} D={D} causal={causal}")
+    N, D = 1 << 20, 64
+    say(f"bwd limits: fmt={fmt} N={N} D={D} causal={causal}")
     rng = np.random.default_rng(970)
     q, k, v, do = (rng.standard_normal((1, 1, N, D), dtype=np.float32).astype(np.float16) for _ in range(4))
     Q, K = orc.quant(0, fmt, q), orc.quant(1, fmt, k)
