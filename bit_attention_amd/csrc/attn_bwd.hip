@@ -16,16 +16,18 @@
 // (recip127, codes16).
 //
 // CDNA4 design.
-//   - prep kernels, one workgroup per (batch*head, 64-token block): Q^ and K^ are dequantised
-//     from FP4 to bf16 (exact: a code times its scale has at most 6 significant bits and lies
-//     in bf16's exponent range), and Q^, K^ and dO are encoded to INT8 per (channel, block),
-//     stored channel-major in the token order below; the dO prep also forms D_i in fp32.
+//   - prep kernels, one workgroup per (batch*head, 64-token block): NVFP4 Q^ and K^ are
+//     dequantised from FP4 to bf16 (exact: a code times its scale has at most 6 significant bits
+//     and lies in bf16's exponent range); for MXFP4 Q and K the prep instead lays out their E8M0
+//     scales per 64-token block for the FP4 MFMA. Q^, K^ and dO are encoded to INT8 per (channel,
+//     block), stored channel-major in the token order below; the dO prep also forms D_i in fp32.
 //   - dK/dV kernel, one workgroup of 12 (D = 128) or 16 (D = 64) waves per (batch*head, block of
-//     192 or 256 keys): each wave owns 16 keys and keeps their K^ (bf16) and V (fp16) rows as
-//     MFMA B operands in registers while 64-query tiles stream into LDS by asynchronous
-//     global-to-LDS copies (global_load_lds), double-buffered, one barrier per tile. S = Q^ K^T
-//     and dP = dO V^T take 16x16x32 MFMAs; a lane then holds 16 (query, key) values of one key,
-//     at queries 16s + 4g + i
+//     192 or 256 keys): each wave owns 16 keys and keeps their K^ (bf16, or MXFP4 codes) and
+//     V (fp16) rows as MFMA B operands in registers while 64-query tiles stream into LDS by
+//     asynchronous global-to-LDS copies (global_load_lds), double-buffered, one barrier per
+//     tile. S = Q^ K^T and dP = dO V^T take 16x16x32 MFMAs (with MXFP4 Q and K, S takes one
+//     block-scaled FP4 16x16x128 MFMA per subtile on the codes themselves); a lane then holds 16
+//     (query, key) values of one key, at queries 16s + 4g + i
 //     (subtile s, lane group g, element i). P and dS are therefore lane-local, a key's block
 //     maximum takes two cross-lane swaps, and a lane's 16 codes are directly the A operand of a
 //     16x16x64 INT8 MFMA whose K slots 16g + 4s + i hold those queries; the INT8 dO and Q^ are
