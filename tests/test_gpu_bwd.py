@@ -189,7 +189,8 @@ def test_bwd_sm_scale():
     _check_grads([t.cpu().numpy().astype(np.float64) for t in outs], ref, bd)
 
 
-@pytest.mark.parametrize("fmt,causal", [(orc.NVFP4, False), (orc.NVFP4, True), (orc.MXFP4, False)])
+@pytest.mark.parametrize("fmt,causal", [(orc.NVFP4, False), (orc.NVFP4, True), (orc.MXFP4, False),
+                                        (orc.MXFP4, True)])
 def test_bwd_full_size_sampled_heads(fmt, causal):
     """B4 H32 N4096 D128, the size the benchmark times: every head runs on the GPU with the GPU
     forward's O and lse, except two heads that get the oracle forward's; those two are checked
