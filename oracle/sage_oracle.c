@@ -56,9 +56,13 @@
  *     R9, P2 = E with tile weight beta, and the normaliser sums E (R8).
  *
  * Slack (test aid, not part of the method): a P rounding decision whose input lies within
- * relative delta of its boundary may legitimately go either way in an implementation whose
- * exp or FP32 summation order differs by a few ulp. For each such decision the oracle adds
- * the largest change of the row's output that the other choice could cause.
+ * its window of its boundary may legitimately go either way in an implementation whose exp or
+ * FP32 summation order differs by a few ulp. For each such decision the oracle adds the largest
+ * change of the row's output that the other choice could cause. The window of element j of a
+ * (row, tile) is relative, delta + ORC_SCORE_EPS * (|x_j| + |t|): delta covers exp (a few ulp)
+ * and the FP32 sums of P; the second term covers the scores themselves, since S is summed in an
+ * implementation-defined order (R12) and x = fl32(c S) is rounded, so x_j - t carries an
+ * absolute error of a few ulp of |x_j| + |t|, which is E_j's relative error.
  */
 #include "sage_oracle.h"
 
@@ -70,6 +74,10 @@
 #endif
 
 static const float E2M1_MAG[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* 2^-20, i.e. 16 units of 2^-24: D/16 block partials summed in FP32 (at most 8 roundings), the
+ * scale product and the scaling by c, each at most half an ulp of the score's magnitude */
+#define ORC_SCORE_EPS (1.0 / 1048576.0)
 
 int orc_max_threads(void) {
 #ifdef _OPENMP
@@ -312,15 +320,20 @@ int orc_p_tile(int fmt, const float* x, const uint8_t* vis, float* E, uint8_t* c
 static float scale_val(int fmt, unsigned b) { return fmt == ORC_NVFP4 ? orc_e4m3_decode(b) : orc_e8m0_decode(b); }
 
 /* Largest |change| of the dequantised P block (weighted by vmax) that a different rounding
- * decision within relative delta could cause. */
+ * decision within its relative window could cause: element u's window is dlt[u], the block
+ * scale's the largest window of the block. */
 static double block_ambiguity(int fmt, const float* P2, const uint8_t* codes, unsigned sbyte,
-                              const double* vmax, const uint8_t* exact, double delta) {
+                              const double* vmax, const uint8_t* exact, const double* dlt) {
   const int blk = blk_of(fmt);
   const float s = scale_val(fmt, sbyte);
-  double worst_scale = 0.0;
+  double worst_scale = 0.0, delta = 0.0;
   float amax = 0.0f;
   int has_exact = 0;
-  for (int u = 0; u < blk; ++u) { amax = fmaxf(amax, P2[u]); has_exact |= exact[u]; }
+  for (int u = 0; u < blk; ++u) {
+    amax = fmaxf(amax, P2[u]);
+    has_exact |= exact[u];
+    if (dlt[u] > delta) delta = dlt[u];
+  }
   /* a block holding the exact tile maximum has its amax fixed (E = exp(0) = 1) */
   for (int k = -1; k <= 1 && !has_exact; k += 2) {
     unsigned alt;
@@ -342,7 +355,7 @@ static double block_ambiguity(int fmt, const float* P2, const uint8_t* codes, un
     if (P2[u] == 0.0f || exact[u]) continue;
     double worst = 0.0;
     for (int k = -1; k <= 1; k += 2) {
-      unsigned c2 = pv_quant(fmt, (float)((double)P2[u] * (1.0 + k * delta)), s);
+      unsigned c2 = pv_quant(fmt, (float)((double)P2[u] * (1.0 + k * dlt[u])), s);
       double dv = fabs((double)pv_val(fmt, c2) - (double)pv_val(fmt, codes[u])) * s;
       if (dv > worst) worst = dv;
     }
@@ -473,8 +486,12 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
           vmax[s] = mv + vhead;
           P2[s] = fmt == ORC_NVFP4 ? 2688.0f * E[s] : E[s];
         }
+        /* each element's decision window (header: delta plus the scores' own FP32 error) */
+        double dlt[ORC_KV_TILE];
+        for (int s = 0; s < ORC_KV_TILE; ++s)
+          dlt[s] = delta + ORC_SCORE_EPS * (fabs((double)x[s]) + fabs((double)t));
         /* The tile maximum has E = exp(0) = 1 exactly in any implementation, unless another
-         * visible key is within delta of it (or tied), in which case either may be the top. */
+         * visible key is within the window of it (or tied), in which case either may be the top. */
         uint8_t exact[ORC_KV_TILE];
         int top = -1;
         float second = 0.0f;
@@ -484,14 +501,16 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
           if (top < 0 && x[s] == t) top = s;
           else second = fmaxf(second, E[s]);
         }
-        if (top >= 0 && (double)second < 1.0 - delta) exact[top] = 1;
+        if (top >= 0 && (double)second < 1.0 - dlt[top]) exact[top] = 1;
         double amb = 0.0, pamb = 0.0;
         double ones[ORC_KV_TILE];
         for (int s = 0; s < ORC_KV_TILE; ++s) ones[s] = 1.0;
         for (int b = 0; b < ORC_KV_TILE / blk; ++b) {
-          amb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], vmax + b * blk, exact + b * blk, delta);
+          amb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], vmax + b * blk, exact + b * blk,
+                                 dlt + b * blk);
           /* with unit weights: how far the tile's sum of dequantised P can move (Direct-P lse) */
-          if (direct_p) pamb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], ones, exact + b * blk, delta);
+          if (direct_p)
+            pamb += block_ambiguity(fmt, P2 + b * blk, pc + b * blk, ps[b], ones, exact + b * blk, dlt + b * blk);
         }
         tile_t[ntile_used] = t;
         tile_amb[ntile_used] = amb;

@@ -86,8 +86,9 @@ int orc_p_tile(int fmt, const float* x, const uint8_t* vis, float* E, uint8_t* c
  * rows == NULL: all B*H*N rows, out is [B,H,N,D]; else rows[r] = (b*H + h)*N + i and out is
  * [n_rows, D]. sm_scale <= 0 selects fl32(1/sqrt(D)).
  * slack (may be NULL): per output row, an upper bound on how far a correct implementation may
- * move that row (max over d) because a P rounding decision lies within relative `delta` of its
- * boundary (see sage_oracle.c). nthreads <= 0: OpenMP default. */
+ * move that row (max over d) because a P rounding decision lies within its window of its
+ * boundary: relative delta + 2^-20 (|x_j| + |t|) for element j of a tile with maximum t (see
+ * sage_oracle.c). nthreads <= 0: OpenMP default. */
 int orc_attn_fwd(int fmt, const uint8_t* q_codes, const uint8_t* q_scales,
                  const uint8_t* k_codes, const uint8_t* k_scales,
                  const uint8_t* v_codes, const uint8_t* v_scales,
@@ -109,7 +110,7 @@ int orc_attn_fwd_direct_p(const uint8_t* q_codes, const uint8_t* q_scales,
  * the row's maximum scaled score and l the normaliser the output row is divided by (the sum of
  * E = exp(x - m), or with Direct-P of the dequantised P, each tile weighted by exp(t - m)).
  * lse_slack (may be NULL): per row, a bound on how far lse may move because a P rounding
- * decision lies within delta of its boundary (0 except with Direct-P). ---- */
+ * decision lies within its window of its boundary (0 except with Direct-P). ---- */
 int orc_attn_fwd_lse(int fmt, int direct_p, const uint8_t* q_codes, const uint8_t* q_scales,
                      const uint8_t* k_codes, const uint8_t* k_scales,
                      const uint8_t* v_codes, const uint8_t* v_scales,

@@ -86,14 +86,19 @@ def sample_rows(N, n_each=8, seed=0):
 TOL = 2e-3  # max-abs output tolerance against the oracle
 
 
-def compare(gpu_rows, orc_rows, slack, what):
-    """|gpu - oracle| <= TOL + slack (per row). Returns stats."""
+def compare(gpu_rows, orc_rows, slack, what, use_slack=False, extra=None):
+    """Every row: |gpu - oracle| <= TOL (plus `extra`, a per-row bound the caller documents, such
+    as the rounding of an fp16 output). With use_slack, also plus the oracle's per-row slack: only
+    the tests whose inputs push P decisions onto their boundaries (scores far outside the
+    workloads' range) use it, and each says why. The slack is always reported."""
     err = np.abs(gpu_rows.astype(np.float64) - orc_rows.astype(np.float64)).max(axis=-1)
-    bound = TOL + slack
+    bound = TOL + (extra if extra is not None else 0.0) + (slack if use_slack else 0.0)
     bad = np.nonzero(~(err <= bound))[0]
     clean = slack == 0
     stats = dict(max_err=float(err.max()), max_err_clean=float(err[clean].max()) if clean.any() else 0.0,
-                 rows=int(err.size), rows_with_slack=int((~clean).sum()))
+                 rows=int(err.size), rows_with_slack=int((~clean).sum()), max_slack=float(slack.max()),
+                 bar="2e-3 + slack" if use_slack else "2e-3")
     say(f"  [{what}] {stats}")
-    assert bad.size == 0, f"{what}: {bad.size} rows beyond tolerance, worst row {bad[np.argmax(err[bad])]} err {err[bad].max()} slack {slack[bad].max()}"
+    assert bad.size == 0, (f"{what}: {bad.size} rows beyond the bar, worst row {bad[np.argmax(err[bad])]} "
+                           f"err {err[bad].max()} slack {slack[bad].max()}")
     return stats

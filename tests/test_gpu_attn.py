@@ -1,10 +1,9 @@
 """GPU parity of the full hot path (sage_fp4_quant x3 + sage_fp4_attn_fwd) against the oracle.
 
-Bar: max-abs <= 2e-3 per output element, plus, for the rare rows where a probability rounding
-decision lies within 2^-14 relative of its boundary (where exp and FP32 summation order, which
-legitimately differ, may tip it), the oracle's bound on the effect of the other choice.
-Small shapes are compared on every row; the full-size workloads, in the configuration bench.py
-times, on sampled rows the oracle computes one by one."""
+Bar: max-abs <= 2e-3 on every compared row. Small shapes are compared on every row; the full-size
+workloads, in the configuration bench.py times, on sampled rows the oracle computes one by one.
+The oracle's slack (its bound on P decisions within FP32 resolution of a boundary) is reported,
+not added: on these inputs no such decision moves a row by more than a few 1e-4."""
 import numpy as np
 import pytest
 

@@ -1,10 +1,15 @@
-"""GPU parity on edge cases of the attention entry points, against the oracle (same bar as the
-other attention tests: max-abs 2e-3 plus the oracle's per-row slack):
+"""GPU parity on edge cases of the attention entry points, against the oracle:
   - explicit sm_scale values (the boundary's sm_scale argument; sm_scale <= 0 selects 1/sqrt(D));
   - score gaps so large that whole key tiles fall more than 2^64 below the running maximum (the
     kernels drop them) and whole P blocks underflow;
   - inputs large enough to saturate the E4M3 scales, and inputs so small that the block scales
-    underflow to zero."""
+    underflow to zero;
+  - scores of order 1e5.
+Bar: max-abs 2e-3 plus the oracle's per-row slack. These inputs make attention sharp (a row's
+weight sits on a few keys, so one P code moves the output by far more than 2e-3) or make the
+scores large (FP32 resolves x - t only to about 2^-20 (|x| + |t|)), so a P decision that lies
+within that resolution of its boundary may go either way in a correct implementation; the slack
+is the oracle's bound on the effect of each such decision (pinned in test_oracle_slack.py)."""
 import numpy as np
 import pytest
 
@@ -44,7 +49,8 @@ def test_explicit_sm_scale(fmt, direct_p, sm_scale, causal):
     say(f"sm_scale {sm_scale} fmt={fmt} dp={direct_p} causal={causal}")
     g = gpu_attn_scaled(fmt, q, k, v, causal, sm_scale, direct_p)
     o, sl = oracle_scaled(fmt, q, k, v, causal, sm_scale, direct_p)
-    compare(g.reshape(-1, 64), o.reshape(-1, 64), sl, f"sm_scale {sm_scale} fmt{fmt} dp{direct_p} c{causal}")
+    compare(g.reshape(-1, 64), o.reshape(-1, 64), sl, f"sm_scale {sm_scale} fmt{fmt} dp{direct_p} c{causal}",
+            use_slack=True)
 
 
 @pytest.mark.parametrize("fmt,direct_p", FMTS)
@@ -60,7 +66,8 @@ def test_rejected_tiles_and_underflowing_blocks(fmt, direct_p, causal):
     g = gpu_attn(fmt, q, k, v, causal, direct_p=direct_p)
     assert np.all(np.isfinite(g))
     o, sl = oracle_attn(fmt, q, k, v, causal, direct_p=direct_p)
-    compare(g.reshape(-1, D), o.reshape(-1, D), sl, f"rejected tiles fmt{fmt} dp{direct_p} c{causal}")
+    compare(g.reshape(-1, D), o.reshape(-1, D), sl, f"rejected tiles fmt{fmt} dp{direct_p} c{causal}",
+            use_slack=True)
 
 
 @pytest.mark.parametrize("fmt,direct_p", FMTS)
@@ -83,23 +90,19 @@ def test_extreme_input_magnitudes(fmt, direct_p, case):
     g = gpu_attn(fmt, q, k, v, False, direct_p=direct_p)
     assert np.all(np.isfinite(g))
     o, sl = oracle_attn(fmt, q, k, v, False, direct_p=direct_p)
-    compare(g.reshape(-1, 128), o.reshape(-1, 128), sl, f"{case} fmt{fmt} dp{direct_p}")
+    compare(g.reshape(-1, 128), o.reshape(-1, 128), sl, f"{case} fmt{fmt} dp{direct_p}", use_slack=True)
 
 
 @pytest.mark.parametrize("fmt,direct_p", FMTS)
-def test_huge_scores_stay_finite(fmt, direct_p):
-    """Q and K both at 300 * N(0,1): scaled scores reach ~1e5, where FP32 cannot resolve their
-    differences to better than ~1e-2 (in the exponent), so two correct FP32 evaluation orders
-    (the kernels' fma in log2 units, the oracle's fl32(c S) then exp(x - t)) may differ by
-    about a percent. Outside the parity bar; checked: finite outputs within 3% of the largest
-    |V-hat| of the oracle's."""
+def test_huge_scores(fmt, direct_p):
+    """Q and K both at 300 * N(0,1): scaled scores reach ~1e5. Rows are nearly one-hot, and the
+    tile maximum must still get E = 1 exactly (it sets the normaliser); the other decisions carry
+    the oracle's magnitude-scaled slack."""
     rng = np.random.default_rng(61 + fmt)
     shape = (1, 2, 200, 128)
     q, k = ((rng.standard_normal(shape) * 300.0).astype(np.float16) for _ in range(2))
     v = rng.standard_normal(shape).astype(np.float16)
     g = gpu_attn(fmt, q, k, v, False, direct_p=direct_p)
     assert np.all(np.isfinite(g))
-    o, _ = oracle_attn(fmt, q, k, v, False, direct_p=direct_p)
-    err = np.abs(g.astype(np.float64) - o).max()
-    say(f"  [huge scores fmt{fmt} dp{direct_p}] max err {err:.3g}")
-    assert err <= 0.03 * np.abs(v.astype(np.float64)).max()
+    o, sl = oracle_attn(fmt, q, k, v, False, direct_p=direct_p)
+    compare(g.reshape(-1, 128), o.reshape(-1, 128), sl, f"huge scores fmt{fmt} dp{direct_p}", use_slack=True)

@@ -1,5 +1,5 @@
-"""GPU parity on seeded random shapes (every row compared with the oracle, same bar as the other
-attention tests): B in 1..3, H in 1..5, N in 1..700, D in {64, 128}, every format, Direct-P,
+"""GPU parity on seeded random shapes (every row compared with the oracle at max-abs 2e-3, plus
+half an fp16 ulp of the value for fp16 outputs): B in 1..3, H in 1..5, N in 1..700, D in {64, 128}, every format, Direct-P,
 causal or not, fp32 or fp16 output. Catches indexing mistakes at unusual sizes (tails, one
 token, odd head counts) that the fixed shape lists might miss."""
 import numpy as np
@@ -39,6 +39,6 @@ def test_random_shape(i):
     g = out.float().cpu().numpy()
     assert np.all(np.isfinite(g)), "unwritten outputs"
     o, sl = oracle_attn(fmt, q, k, v, causal, direct_p=dp)
-    if f16_out:  # the fp16 store rounds once more: half an fp16 ulp of each value
-        sl = sl + np.abs(o).reshape(-1, D).max(axis=1) * 2.0 ** -11
-    compare(g.reshape(-1, D), o.reshape(-1, D), sl, f"case {i}")
+    # the fp16 store rounds once more: half an fp16 ulp of each value
+    extra = np.abs(o).reshape(-1, D).max(axis=1) * 2.0 ** -11 if f16_out else None
+    compare(g.reshape(-1, D), o.reshape(-1, D), sl, f"case {i}", extra=extra)
