@@ -6,6 +6,7 @@ The functions named like the C entry points take raw pointers/ints; the convenie
 from __future__ import annotations
 
 import ctypes as C
+import functools
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +77,12 @@ def sage_fp4_slot_token(slot: int) -> int:
     return lib().sage_fp4_slot_token(slot)
 
 
+@functools.lru_cache(maxsize=256)
+def _sizes(role, fmt, B, H, N, D):
+    """(codes, scales) bytes for one operand, cached: the wrappers check sizes on every call."""
+    return sage_fp4_codes_bytes(role, fmt, B, H, N, D), sage_fp4_scales_bytes(role, fmt, B, H, N, D)
+
+
 def sage_fp4_codes_bytes(role, fmt, B, H, N, D) -> int:
     return lib().sage_fp4_codes_bytes(role, fmt, B, H, N, D)
 
@@ -135,12 +142,38 @@ def _stream_ptr(stream):
     return C.c_void_p(s.cuda_stream)
 
 
-def _check(t, dtype, what):
+def _on_gpu(t) -> bool:
+    return t.is_cuda
+
+
+def _check(t, dtype, what, device=None, min_numel=None, numel=None):
+    """t must be a contiguous CUDA (ROCm) tensor of `dtype`, on `device` when given, with at least
+    `min_numel` (or exactly `numel`) elements: the C ABI cannot see buffer sizes, so an undersized
+    buffer would otherwise be read or written out of bounds by the kernels."""
     import torch
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not _on_gpu(t):
         raise TypeError(f"{what} must be a CUDA (ROCm) tensor")
     if t.dtype != dtype or not t.is_contiguous():
         raise TypeError(f"{what} must be a contiguous {dtype} tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the other operands on {device}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call needs {min_numel}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call needs exactly {numel}")
+
+
+def _check_codes(pair, role, fmt, shape, device, what):
+    """A (codes, scales) pair of `role` in format `fmt` for shape (B, H, N, D)."""
+    import torch
+    if not isinstance(pair, (tuple, list)) or len(pair) != 2:
+        raise TypeError(f"{what} must be a (codes, scales) pair")
+    B, H, N, D = shape
+    nc, ns = _sizes(role, fmt, B, H, N, D)
+    if nc == 0 or ns == 0:
+        raise SageError(-2, f"{what}: shape {shape}")
+    _check(pair[0], torch.uint8, f"{what} codes", device, min_numel=nc)
+    _check(pair[1], torch.uint8, f"{what} scales", device, min_numel=ns)
 
 
 def alloc_quant(role, fmt, B, H, N, D, device="cuda"):
@@ -156,7 +189,10 @@ def alloc_quant(role, fmt, B, H, N, D, device="cuda"):
 def quant_into(x, role, fmt, codes, scales, stream=None):
     import torch
     _check(x, torch.float16, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [B,H,N,D]")
     B, H, N, D = x.shape
+    _check_codes((codes, scales), role, fmt, (B, H, N, D), x.device, "output")
     rc = sage_fp4_quant(role, fmt, C.c_void_p(x.data_ptr()), B, H, N, D, C.c_void_p(codes.data_ptr()),
                         C.c_void_p(scales.data_ptr()), _stream_ptr(stream))
     if rc != 0:
@@ -187,11 +223,13 @@ def attn_fwd_into(fmt, q, k, v, shape, out, causal=False, sm_scale=0.0, stream=N
     import torch
     B, H, N, D = shape
     od = _out_code(out)
+    dev = q[0].device if isinstance(q, (tuple, list)) and len(q) == 2 else None
+    for pair, role, name in ((q, ROLE_Q, "q"), (k, ROLE_K, "k"), (v, ROLE_V, "v")):
+        _check_codes(pair, role, fmt, shape, dev, name)
+    _check(out, out.dtype, "out", dev, numel=B * H * N * D)
     ptrs = [C.c_void_p(t.data_ptr()) for pair in (q, k, v) for t in pair]
     if lse is not None:
-        _check(lse, torch.float32, "lse")
-        if lse.numel() != B * H * N:
-            raise ValueError("lse must hold B*H*N elements")
+        _check(lse, torch.float32, "lse", dev, numel=B * H * N)
         rc = sage_fp4_attn_fwd_lse(fmt, direct_p, *ptrs, B, H, N, D, causal, sm_scale, C.c_void_p(out.data_ptr()),
                                    od, C.c_void_p(lse.data_ptr()), _stream_ptr(stream))
         what = "sage_fp4_attn_fwd_lse"
@@ -226,6 +264,33 @@ def alloc_bwd_workspace(B, H, N, D, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _bwd_args(fmt, q, k, v, o, do, lse, dq, dk, dv, causal, sm_scale):
+    """Checked raw arguments of the backward entry points, up to out_dtype."""
+    import torch
+    _check(v, torch.float16, "v")
+    if v.dim() != 4:
+        raise ValueError("v must be [B,H,N,D]")
+    B, H, N, D = v.shape
+    dev = v.device
+    for t, n in ((o, "o"), (do, "do")):
+        _check(t, torch.float16, n, dev, numel=v.numel())
+        if t.shape != v.shape:
+            raise ValueError(f"{n} must have v's shape")
+    _check(lse, torch.float32, "lse", dev, numel=B * H * N)
+    for pair, role, name in ((q, ROLE_Q, "q"), (k, ROLE_K, "k")):
+        _check_codes(pair, role, fmt, (B, H, N, D), dev, name)
+    od = _out_code(dq)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, dq.dtype, n, dev, numel=v.numel())
+        if t.shape != v.shape:
+            raise ValueError(f"{n} must have v's shape")
+    args = [C.c_void_p(t.data_ptr()) for pair in (q, k) for t in pair]
+    args += [C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), C.c_void_p(do.data_ptr()),
+             C.c_void_p(lse.data_ptr()), B, H, N, D, causal, sm_scale, C.c_void_p(dq.data_ptr()),
+             C.c_void_p(dk.data_ptr()), C.c_void_p(dv.data_ptr()), od]
+    return args, dev, (B, H, N, D)
+
+
 def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False, sm_scale=0.0, stream=None,
                   stage=None):
     """q, k: (codes, scales) pairs of the forward's Q and K; v, o, do: fp16 [B,H,N,D]; lse: fp32
@@ -233,22 +298,9 @@ def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False,
     least sage_fp4_attn_bwd_workspace_bytes bytes. Calls sage_fp4_attn_bwd, or with `stage`
     (BWD_PREP, BWD_DKDV, BWD_DQ) sage_fp4_attn_bwd_stage."""
     import torch
-    for t, n in ((v, "v"), (o, "o"), (do, "do")):
-        _check(t, torch.float16, n)
-    _check(lse, torch.float32, "lse")
-    B, H, N, D = v.shape
-    if o.shape != v.shape or do.shape != v.shape or lse.numel() != B * H * N:
-        raise ValueError("o and do must match v's shape and lse must hold B*H*N elements")
-    od = _out_code(dq)
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _check(t, dq.dtype, n)
-        if t.shape != v.shape:
-            raise ValueError(f"{n} must have v's shape")
-    args = [C.c_void_p(t.data_ptr()) for pair in (q, k) for t in pair]
-    args += [C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), C.c_void_p(do.data_ptr()),
-             C.c_void_p(lse.data_ptr()), B, H, N, D, causal, sm_scale, C.c_void_p(dq.data_ptr()),
-             C.c_void_p(dk.data_ptr()), C.c_void_p(dv.data_ptr()), od, C.c_void_p(workspace.data_ptr()),
-             workspace.numel(), _stream_ptr(stream)]
+    args, dev, (B, H, N, D) = _bwd_args(fmt, q, k, v, o, do, lse, dq, dk, dv, causal, sm_scale)
+    _check(workspace, torch.uint8, "workspace", dev, min_numel=sage_fp4_attn_bwd_workspace_bytes(B, H, N, D))
+    args += [C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_ptr(stream)]
     if stage is None:
         rc, what = sage_fp4_attn_bwd(fmt, *args), "sage_fp4_attn_bwd"
     else:
@@ -256,3 +308,4 @@ def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False,
     if rc != 0:
         raise SageError(rc, what)
     return dq, dk, dv
+

@@ -158,27 +158,40 @@ size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D) {
   return sage::bwd_workspace_bytes((int64_t)B * H, N, D);
 }
 
+// Validation of the backward's arguments other than the workspace; SAGE_OK when they are valid.
+static int check_bwd(int fmt, const void* const* in, int B, int H, int N, int D, int out_dtype) {
+  if (!valid_fmt(fmt) || (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32)) return SAGE_ERR_ENUM;
+  for (int i = 0; i < 11; ++i)
+    if (!in[i]) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  for (int i = 0; i < 11; ++i)
+    if (!aligned16(in[i])) return SAGE_ERR_ALIGN;
+  return SAGE_OK;
+}
+
+static int launch_bwd(int stages, int fmt, const void* const* in, int B, int H, int N, int D, int causal,
+                      float sm_scale, int out_dtype, void* workspace, void* stream) {
+  const hipError_t e = sage::launch_attn_bwd(stages, fmt != SAGE_FMT_NVFP4, in[0], in[1], in[2], in[3], in[4], in[5],
+                                             in[6], static_cast<const float*>(in[7]), B * H, N, D, causal != 0,
+                                             scale_or_default(sm_scale, D), const_cast<void*>(in[8]),
+                                             const_cast<void*>(in[9]), const_cast<void*>(in[10]),
+                                             out_dtype == SAGE_OUT_F32, workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 // The backward, all stages (mask 7) or one (1 prep, 2 dK/dV, 4 dQ).
 static int attn_bwd_stages(int stages, int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                            const void* k_scales, const void* v, const void* o, const void* dout, const float* lse,
                            int B, int H, int N, int D, int causal, float sm_scale, void* dq, void* dk, void* dv,
                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_fmt(fmt) || (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32)) return SAGE_ERR_ENUM;
   const void* in[11] = {q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, dq, dk, dv};
-  for (const void* p : in)
-    if (!p) return SAGE_ERR_NULL;
+  const int chk = check_bwd(fmt, in, B, H, N, D, out_dtype);
+  if (chk != SAGE_OK) return chk;
   if (!workspace) return SAGE_ERR_NULL;
-  const int sh = check_shape(B, H, N, D);
-  if (sh != SAGE_OK) return sh;
-  for (const void* p : in)
-    if (!aligned16(p)) return SAGE_ERR_ALIGN;
   if (!aligned16(workspace)) return SAGE_ERR_ALIGN;
   if (workspace_bytes < sage::bwd_workspace_bytes((int64_t)B * H, N, D)) return SAGE_ERR_WORKSPACE;
-  const hipError_t e = sage::launch_attn_bwd(stages, fmt != SAGE_FMT_NVFP4, q_codes, q_scales, k_codes, k_scales, v,
-                                             o, dout, lse, B * H, N, D, causal != 0, scale_or_default(sm_scale, D),
-                                             dq, dk, dv, out_dtype == SAGE_OUT_F32, workspace,
-                                             reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+  return launch_bwd(stages, fmt, in, B, H, N, D, causal, sm_scale, out_dtype, workspace, stream);
 }
 
 int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const void* k_codes, const void* k_scales,
@@ -188,6 +201,8 @@ int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const 
   return attn_bwd_stages(7, fmt, q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, B, H, N, D, causal, sm_scale,
                          dq, dk, dv, out_dtype, workspace, workspace_bytes, stream);
 }
+
+
 
 int sage_fp4_attn_bwd_stage(int stage, int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                             const void* k_scales, const void* v, const void* o, const void* dout, const float* lse,
