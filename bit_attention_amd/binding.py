@@ -21,7 +21,8 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
            "sage_fp4_attn_fwd_lse", "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
-           "sage_fp4_attn_bwd_stage", "sage_fp4_status_string"]
+           "sage_fp4_attn_bwd_stage", "sage_fp4_attn_bwd_noalloc", "sage_fp4_status_string"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGE_BWD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -59,6 +60,8 @@ def lib():
         L.sage_fp4_attn_bwd.restype = I
         L.sage_fp4_attn_bwd_stage.argtypes = [I] + L.sage_fp4_attn_bwd.argtypes
         L.sage_fp4_attn_bwd_stage.restype = I
+        L.sage_fp4_attn_bwd_noalloc.argtypes = L.sage_fp4_attn_bwd.argtypes[:19] + [P]
+        L.sage_fp4_attn_bwd_noalloc.restype = I
         L.sage_fp4_status_string.argtypes = [I]; L.sage_fp4_status_string.restype = C.c_char_p
         _lib = L
     return _lib
@@ -129,6 +132,13 @@ def sage_fp4_attn_bwd_stage(stage, fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, ls
     return lib().sage_fp4_attn_bwd_stage(stage, fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D,
                                          int(causal), float(sm_scale), dq_ptr, dk_ptr, dv_ptr, out_dtype, ws_ptr,
                                          ws_bytes, stream_ptr)
+
+
+def sage_fp4_attn_bwd_noalloc(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D, causal, sm_scale,
+                              dq_ptr, dk_ptr, dv_ptr, out_dtype, stream_ptr) -> int:
+    return lib().sage_fp4_attn_bwd_noalloc(fmt, qc, qs, kc, ks, v_ptr, o_ptr, do_ptr, lse_ptr, B, H, N, D,
+                                           int(causal), float(sm_scale), dq_ptr, dk_ptr, dv_ptr, out_dtype,
+                                           stream_ptr)
 
 
 def status_string(status: int) -> str:
@@ -309,3 +319,12 @@ def attn_bwd_into(fmt, q, k, v, o, do, lse, dq, dk, dv, workspace, causal=False,
         raise SageError(rc, what)
     return dq, dk, dv
 
+
+def attn_bwd_noalloc_into(fmt, q, k, v, o, do, lse, dq, dk, dv, causal=False, sm_scale=0.0, stream=None):
+    """As attn_bwd_into without a workspace: calls sage_fp4_attn_bwd_noalloc, whose workspace is
+    the library's device-resident array (SAGE_ERR_WORKSPACE for shapes that do not fit it)."""
+    args, _, _ = _bwd_args(fmt, q, k, v, o, do, lse, dq, dk, dv, causal, sm_scale)
+    rc = sage_fp4_attn_bwd_noalloc(fmt, *args, _stream_ptr(stream))
+    if rc != 0:
+        raise SageError(rc, "sage_fp4_attn_bwd_noalloc")
+    return dq, dk, dv

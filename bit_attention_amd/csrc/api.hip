@@ -2,6 +2,7 @@
 // Host-side argument validation happens before anything is enqueued; each entry point then
 // launches exactly one kernel on the caller's stream and reports launch errors.
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/sage_fp4.h"
 #include "device.h"
@@ -202,7 +203,60 @@ int sage_fp4_attn_bwd(int fmt, const void* q_codes, const void* q_scales, const 
                          dq, dk, dv, out_dtype, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
 
+// ---- the backward without allocation: its workspace is a device-resident array of this file ----
+
+// One copy per GPU, held until the process ends. Host code never uses the name as an address:
+// the kernels get the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[SAGE_BWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device, set on first use
+
+// The address of `scratch` on the device that runs `stream` (the current device for the null
+// stream), looked up once per device with that device current.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = 0, cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int sage_fp4_attn_bwd_noalloc(int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
+                                         const void* k_scales, const void* v, const void* o, const void* dout,
+                                         const float* lse, int B, int H, int N, int D, int causal, float sm_scale,
+                                         void* dq, void* dk, void* dv, int out_dtype, void* stream) {
+  const void* in[11] = {q_codes, q_scales, k_codes, k_scales, v, o, dout, lse, dq, dk, dv};
+  const int chk = check_bwd(fmt, in, B, H, N, D, out_dtype);
+  if (chk != SAGE_OK) return chk;
+  if (sage::bwd_workspace_bytes((int64_t)B * H, N, D) > SAGE_BWD_NOALLOC_SCRATCH_BYTES) return SAGE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(reinterpret_cast<hipStream_t>(stream), &ws) != hipSuccess) return SAGE_ERR_HIP;
+  return launch_bwd(7, fmt, in, B, H, N, D, causal, sm_scale, out_dtype, ws, stream);
+}
+
+extern "C" {
 
 int sage_fp4_attn_bwd_stage(int stage, int fmt, const void* q_codes, const void* q_scales, const void* k_codes,
                             const void* k_scales, const void* v, const void* o, const void* dout, const float* lse,

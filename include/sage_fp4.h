@@ -203,6 +203,27 @@ int sage_fp4_attn_bwd_stage(int stage, int fmt, const void* q_codes, const void*
                             void* dq, void* dk, void* dv, int out_dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device-resident workspace of sage_fp4_attn_bwd_noalloc: 64 MiB, enough for
+ * shapes with about B*H*N*D <= 8M elements (e.g. B=1, H=16, N=4096, D=128). */
+#define SAGE_BWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* sage_fp4_attn_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc. Same arguments,
+ * computation, validation and results (bit for bit) as sage_fp4_attn_bwd, without `workspace`
+ * and `workspace_bytes`: the workspace is an array of SAGE_BWD_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy per GPU (the GPU of `stream`; the current one for the null stream), held
+ * until the process ends. The first call on a GPU looks up that copy's address
+ * (hipGetSymbolAddress); no call allocates, frees or clears memory. Shapes whose workspace
+ * (sage_fp4_attn_bwd_workspace_bytes) exceeds the array return SAGE_ERR_WORKSPACE before any
+ * launch. Every call on one GPU uses the same array and leaves its contents behind (the next
+ * call overwrites what it reads before reading it), so calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. */
+int sage_fp4_attn_bwd_noalloc(int fmt, const void* q_codes, const void* q_scales,
+                              const void* k_codes, const void* k_scales,
+                              const void* v, const void* o, const void* dout, const float* lse,
+                              int B, int H, int N, int D, int causal, float sm_scale,
+                              void* dq, void* dk, void* dv, int out_dtype, void* stream);
+
 /* Static description of a status code. */
 const char* sage_fp4_status_string(int status);
 
