@@ -75,13 +75,13 @@ __device__ __forceinline__ int lds_v(int row, int ch) {
 // Online-softmax state of one 16-query group (per lane: one query, a quarter of its channels).
 template <int D>
 struct RowState {
-  float m_u, R, l2;
-  v4f O[D / 16];
+  float m_u, R, Re, l;  // running maximum and frame R + Re (log2 units), normaliser (sum of E in that frame)
+  v4f O[D / 16];    // sum of P2-hat * V-hat in R's frame (P2 = 2688 E)
 };
 
 // One tile of the online softmax with the two-level P quantisation for one group. S holds the
 // lane's 32 scores (masked ones -infinity); on return Pf holds P2-hat (fp16, code * s_P2) as the
-// four B operands of the PV product, and O, l2 have been rescaled to this tile's reference.
+// four B operands of the PV product, and O, l have been rescaled to this tile's reference.
 template <int D>
 __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, v8h* Pf) {
   float bm[2];  // block maxima: a chain of three-input maxima over the block's 16 scores
@@ -95,19 +95,35 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
   }
   const float tS = xg_max(fmaxf(bm[0], bm[1]));
   const bool vis = tS > -INFINITY;
-  const float t_u = tS * k2;  // tile maximum in log2 units
-  const float m_new = fmaxf(st.m_u, t_u);
-  const bool accept = vis && (t_u >= m_new - 64.0f);
-  const float bias = vis ? LOG2_2688 - t_u : -INFINITY;  // log2(P2) = S*k2 + bias
+  // tile maximum in log2 units, rounded toward -infinity (as in the MXFP4 kernel): T is the
+  // frame of this tile's P and of the accumulator, and S*k2 - T >= 0 only at the maximum
+  const float T0 = tS * k2;
+  const float Tdn = as_f(as_u(T0) - (unsigned)((__float_as_int(T0) >> 31) | 1));
+  float T = __builtin_fmaf(tS, k2, -T0) < 0.0f ? Tdn : T0;
+  T = vis ? T : 0.0f;
+  // the exact tile maximum tau = tS*k2 is T + eT with eT in [0, ulp(T)), exact in FP32; P, the
+  // normaliser and the accumulator all take tau as their frame, so that the maximal key has
+  // E = 1 exactly however large the scores (eT matters only when ulp(T) does)
+  const float eT = vis ? __builtin_fmaf(tS, k2, -T) : 0.0f;
+  const float m_new = fmaxf(st.m_u, T);
+  const bool accept = vis && (T >= m_new - 64.0f);
+  const float bias = LOG2_2688 - T;  // log2(P2) = S*k2 + bias, up to the rounding of bias
 
-  float sP[2], bq[2];
+  float sP[2], bq[2], wl[2];
   v2h sh[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, bias));  // block max of P2
+    // block maximum of P2 = 2688 E with E = clamp01(2^(S*k2 - T)): exactly 2688 for the block of
+    // the tile maximum (its argument lies in [0, ulp)), as the two-level P requires
+    const float pmax = 2688.0f * __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, -T)), 0.0f, 1.0f);
     const unsigned sb = e4m3_encode(pmax * (1.0f / 6.0f));
     sP[h] = e4m3_decode(sb);
     bq[h] = sP[h] > 0.0f ? bias - __builtin_amdgcn_logf(sP[h]) : -INFINITY;  // log2(P2/s)
+    // The quotients q = 2^(S*k2 + bq) carry the rounding of bq (up to an ulp of T, which moves
+    // the code decisions only for huge scores): q = E * 2^(theta + eT) with E = 2^(S*k2 - tau)
+    // and theta = T + bq, exact by Sterbenz. The block's share of the normaliser, sum E, is
+    // therefore 2^-(theta + eT) * sum q, to a few ulp at any score magnitude.
+    wl[h] = sP[h] > 0.0f ? __builtin_amdgcn_exp2f(-((T + bq[h]) + eT)) : 0.0f;
     // a rejected tile contributes nothing: its P blocks get scale 0 (codes are finite)
     const _Float16 s16 = accept ? (_Float16)sP[h] : (_Float16)0.0f;
     sh[h] = v2h{s16, s16};
@@ -124,11 +140,14 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
     }
     Pf[u] = dequant8(pack_fp4_8(q), sh[h]);
   }
-  const float l2t = accept ? sP[0] * qsum[0] + sP[1] * qsum[1] : 0.0f;
-  const float factor = accept ? __builtin_amdgcn_exp2f(st.R - t_u) : 1.0f;
-  st.R = accept ? t_u : st.R;
+  const float lt = accept ? wl[0] * qsum[0] + wl[1] * qsum[1] : 0.0f;  // sum of E in T's frame
+  // frames are (R, Re) pairs: R - T is exact when the two are close, and any tile far below
+  // the running maximum is rejected
+  const float factor = accept ? __builtin_amdgcn_exp2f((st.R - T) + (st.Re - eT)) : 1.0f;
+  st.R = accept ? T : st.R;
+  st.Re = accept ? eT : st.Re;
   st.m_u = m_new;
-  st.l2 = st.l2 * factor + l2t;
+  st.l = st.l * factor + lt;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.O[dt] *= factor;
 }
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   RowState<D> st[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    st[a].m_u = -INFINITY; st[a].R = -INFINITY; st[a].l2 = 0.0f;
+    st[a].m_u = -INFINITY; st[a].R = -INFINITY; st[a].Re = 0.0f; st[a].l = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st[a].O[dt] = v4f{0, 0, 0, 0};
   }
@@ -308,18 +327,16 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     }
   }
 
-  // ---- epilogue: O / l; lane (g, c) holds channels 16dt + 4g + i of its query in each group.
-  // lse (when given): the row's log-sum-exp of the scaled scores, ln(2^R * l2 / 2688), since l2
-  // sums P2 = 2688 E in the frame of the reference R (log2 units)
+  // ---- epilogue: O / (2688 l); lane (g, c) holds channels 16dt + 4g + i of its query in each
+  // group. lse (when given): the row's log-sum-exp of the scaled scores, ln(2^(R + Re) * l)
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const float L = xg_sum(st[a].l2);
+    const float L = xg_sum(st[a].l);
     const int qi = qi0 + 16 * a;
     if (qi < N) {
-      const float inv = 1.0f / L;
+      const float inv = 1.0f / (2688.0f * L);
       const int64_t row = bh * N + qi;
-      if (lse && g == 0)
-        lse[row] = (st[a].R + __builtin_amdgcn_logf(L) - LOG2_2688) * 0.6931471805599453f;
+      if (lse && g == 0) lse[row] = (st[a].R + (st[a].Re + __builtin_amdgcn_logf(L))) * 0.6931471805599453f;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const v4f o = st[a].O[dt] * inv;
