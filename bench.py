@@ -10,6 +10,9 @@ included); the attention kernel alone is reported in `attn_*` fields and `roofli
 HIP events on the stream the kernels are launched on. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.
 
+`--sweep PATH` times the attention alone over the N sweep and workloads 3 and 4, every format and
+mask, appending one JSON line per entry to PATH and skipping entries already there.
+
 `--backward` times the 8-bit backward instead (sage_fp4_attn_bwd as its three stages, on the
 forward's FP4 Q/K, output and log-sum-exp): `value` = 10*B*H*N^2*D / (backward time), the
 roofline is that of its dK/dV kernel, and the CPU baseline is the backward oracle on one head.
@@ -68,8 +71,9 @@ def load_traffic(kernel_file: str, key: str):
     return e.get("bytes_per_launch")
 
 
-def torch_reference_rows(q, k, v, heads, rows, sm_scale):
-    """Plain PyTorch fp32 attention on the GPU for a few (head, row) samples."""
+def torch_reference_rows(q, k, v, heads, rows, sm_scale, causal=False):
+    """Plain PyTorch fp32 attention on the GPU for a few (head, row) samples; with causal, key j
+    is visible to query i iff j <= i."""
     import torch
     outs = []
     for h in heads:
@@ -77,24 +81,43 @@ def torch_reference_rows(q, k, v, heads, rows, sm_scale):
         kh = k.view(-1, k.shape[2], k.shape[3])[h].float().contiguous()
         vh = v.view(-1, v.shape[2], v.shape[3])[h].float().contiguous()
         s = torch.matmul(qh[rows], kh.t().contiguous()) * sm_scale
+        if causal:
+            keys = torch.arange(kh.shape[0], device=s.device)
+            s = s.masked_fill(keys[None, :] > rows[:, None], float("-inf"))
         p = torch.softmax(s, dim=-1)
         outs.append(torch.matmul(p, vh))
     return torch.cat(outs).double().cpu().numpy()
 
 
-def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15.0, gpu_out=None):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15.0, gpu_out=None, gpu_qkv=None):
     """The oracle, as it stands, on a bounded sample of the same workload: head after head, the
     quantisation of the head's Q, K and V and the attention of every 4th query row of it, until
     about `seconds_target` seconds of CPU time; the quantisation is charged pro rata to the rows
     computed. Throughput by the same 4*N*D-per-row count as the GPU figure. If `gpu_out` (the
     non-causal GPU output, [B*H, N, D] on the host) is given, the largest |GPU - oracle| over the
-    sampled rows is returned as well."""
+    sampled rows is returned as well; if `gpu_qkv` (the GPU's Q, K, V codes and scales on the
+    host, in the oracle's array shapes) is given, the number of code and scale bytes of the
+    sampled heads that differ from the oracle's."""
     import oracle as orc
     B, H, N, D = shape
     nthreads = orc.max_threads()
     rows = np.arange(0, N, 4, dtype=np.int64)
     total_t, total_rows, heads = 0.0, 0, 0
     max_abs = 0.0
+    mism = {"code_bytes_compared": 0, "code_bytes_differing": 0, "scale_bytes_compared": 0,
+            "scale_bytes_differing": 0}
     for bh in range(B * H):
         b, h = divmod(bh, H)
         t0 = time.perf_counter()
@@ -102,6 +125,12 @@ def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15
         K = orc.quant(orc.ROLE_K, fmt, k_np[b:b + 1, h:h + 1])
         V = orc.quant(orc.ROLE_V, fmt, v_np[b:b + 1, h:h + 1])
         t_quant = time.perf_counter() - t0
+        if gpu_qkv is not None:
+            for (oc, os_), (gc, gs) in zip((Q, K, V), gpu_qkv):
+                mism["code_bytes_compared"] += oc.size
+                mism["code_bytes_differing"] += int(np.count_nonzero(oc[0, 0] != gc[b, h]))
+                mism["scale_bytes_compared"] += os_.size
+                mism["scale_bytes_differing"] += int(np.count_nonzero(os_[0, 0] != gs[b, h]))
         t0 = time.perf_counter()
         out = orc.attn_fwd(fmt, Q, K, V, (1, 1, N, D), rows=rows, nthreads=nthreads, direct_p=direct_p)
         t_attn = time.perf_counter() - t0
@@ -114,7 +143,8 @@ def cpu_baseline(q_np, k_np, v_np, shape, fmt, direct_p=False, seconds_target=15
         if total_t >= seconds_target:
             break
     tops = 4.0 * N * D * total_rows / total_t / 1e12
-    return {"value": tops, "unit": "TOPS", "cores": nthreads, "kind": "oracle",
+    return {"value": tops, "unit": "TOPS", "cores": nthreads, "kind": "oracle", "cpu_model": cpu_model(),
+            "quant_vs_oracle": mism if gpu_qkv is not None else None,
             "sample": f"{heads} heads x {len(rows)} query rows (every 4th row; non-causal, N={N}, "
                       f"D={D}), format {fmt}{' Direct-P' if direct_p else ''}: per head the quantisation of Q, K, V (charged "
                       f"{len(rows)}/{N}) and the attention rows; {total_t:.1f} s of CPU time",
@@ -135,6 +165,7 @@ def cpu_one_thread_small(fmt, direct_p=False):
     orc.attn_fwd(fmt, Q, K, V, (B, H, N, D), nthreads=1, direct_p=direct_p)
     t = time.perf_counter() - t0
     return {"value": 4.0 * B * H * N * N * D / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"whole B{B} H{H} N{N} D{D} workload, non-causal (quantisation on the oracle's "
                       f"default threads), attention on 1 thread", "seconds": t}
 
@@ -190,6 +221,10 @@ def main():
                     help="also run one plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--backward", action="store_true",
                     help="time the 8-bit backward instead (sage_fp4_attn_bwd, as its three stages)")
+    ap.add_argument("--sweep", metavar="PATH",
+                    help="time the attention alone over the N sweep (B4 H32 D128, N 1024..16384) and "
+                         "workloads 3 and 4, every format and mask; one JSON line per entry appended "
+                         "to PATH, entries already in PATH skipped (the sweep resumes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,6 +237,8 @@ def main():
     from bit_attention_amd import binding as bnd
     from bit_attention_amd import synth
 
+    if args.sweep:
+        return run_sweep(args.sweep, torch, bnd, synth)
     fmt = {"nvfp4": bnd.NVFP4, "mxfp4": bnd.MXFP4, "mx4_pv8": bnd.MX4_PV8}[args.fmt]
     if args.direct_p and fmt != bnd.MXFP4:
         print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
@@ -270,20 +307,19 @@ def main():
     kname += "_direct_p" if args.direct_p else ""
     tkey = f"{kname}_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
     traffic = load_traffic(kfile, tkey)
+    # the metric's denominator is the dense FP4 MFMA peak for every format; the fraction of the
+    # peak of the MFMA the kernel actually runs on is reported beside it
     if fmt == bnd.NVFP4:
-        roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": attn_tops / FP16_PEAK_TFLOPS, "traffic": traffic,
-                "kernel": "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"}
+        own_peak, kdesc = FP16_PEAK_TFLOPS, "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"
     elif fmt == bnd.MXFP4:
-        roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": attn_tops / FP4_PEAK_TOPS, "traffic": traffic,
-                "kernel": "attn_mxfp4_kernel (block-scaled FP4 MFMA"
-                          + (", Direct-P normaliser)" if args.direct_p else ")")}
-    else:
-        mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)  # QK at the FP4 rate, PV at FP8
-        roof = {"bound": "mfma", "achieved": attn_tops, "peak": mixed, "unit": "TFLOP/s",
-                "frac": attn_tops / mixed, "traffic": traffic,
-                "kernel": "attn_mxfp4_kernel, FP8-PV instance (FP4 QK, FP8 PV MFMA)"}
+        own_peak = FP4_PEAK_TOPS
+        kdesc = "attn_mxfp4_kernel (block-scaled FP4 MFMA" + (", Direct-P normaliser)" if args.direct_p else ")")
+    else:  # QK at the FP4 rate, PV at the FP8 rate
+        own_peak = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)
+        kdesc = "attn_mxfp4_kernel, FP8-PV instance (FP4 QK, FP8 PV MFMA)"
+    roof = {"bound": "mfma", "achieved": attn_tops, "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": attn_tops / FP4_PEAK_TOPS, "traffic": traffic, "kernel": kdesc,
+            "own_mfma_peak": own_peak, "frac_own_mfma_peak": attn_tops / own_peak}
     blk = 16 if fmt == bnd.NVFP4 else 32
     v_code_bytes = 1.0 if fmt == bnd.MX4_PV8 else 0.5  # MXFP8 V: one byte per element
     quant_bytes = B * H * N * D * (2 * (2 + 0.5 + 1.0 / blk) + (2 + v_code_bytes + 1.0 / blk))
@@ -307,12 +343,11 @@ def main():
     torch.cuda.synchronize()
     heads = [0, B * H // 2 + 1, B * H - 1]
     rows = torch.arange(0, N, max(1, N // 256), device=dev)
-    ref = torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D))  # non-causal
-    if not causal:
-        got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
-        a, b = got.reshape(-1), ref.reshape(-1)
-        res["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
-        res["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
+    refs = {c: torch_reference_rows(q, k, v, heads, rows, 1.0 / np.sqrt(D), causal=c) for c in (False, True)}
+    got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
+    a, b = got.reshape(-1), refs[causal].reshape(-1)
+    res["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+    res["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -371,11 +406,11 @@ def main():
             fl = flops_formula / 2 if c2 else flops_formula
             t = fl / (ms * 1e-3) / 1e12
             extras[name] = {"attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS}
-            if not c2:  # accuracy against the same fp32 reference rows
-                got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
-                a, b = got.reshape(-1), ref.reshape(-1)
-                extras[name]["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
-                extras[name]["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
+            # accuracy against the same fp32 reference rows (causal mask when causal)
+            got = torch.cat([out.view(-1, N, D)[h][rows] for h in heads]).double().cpu().numpy()
+            a, b = got.reshape(-1), refs[c2].reshape(-1)
+            extras[name]["cos_sim_vs_fp32"] = float(a @ b / np.sqrt((a @ a) * (b @ b)))
+            extras[name]["rel_l1_vs_fp32"] = float(np.abs(a - b).sum() / np.abs(b).sum())
             if f2 == bnd.MX4_PV8:  # half the flops at the FP4 rate (QK), half at the FP8 rate (PV)
                 mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)
                 extras[name]["frac_fp4_fp8_mixed_peak"] = t / mixed
@@ -389,13 +424,77 @@ def main():
             bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=False, direct_p=args.direct_p)
             torch.cuda.synchronize()
             gpu_out = out.view(B * H, N, D).float().cpu().numpy()
-        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p, gpu_out=gpu_out)
+        # the GPU's codes and scales of the last step, in the oracle's array shapes
+        Np = (N + 127) // 128 * 128
+        vb = Np if fmt == bnd.MX4_PV8 else Np // 2
+        gpu_qkv = [(Q[0].cpu().numpy().reshape(B, H, N, D // 2), Q[1].cpu().numpy().reshape(B, H, N, D // blk)),
+                   (K[0].cpu().numpy().reshape(B, H, N, D // 2), K[1].cpu().numpy().reshape(B, H, N, D // blk)),
+                   (V[0].cpu().numpy().reshape(B, H, D, vb), V[1].cpu().numpy().reshape(B, H, D, Np // blk))]
+        res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p, gpu_out=gpu_out,
+                                           gpu_qkv=gpu_qkv)
         # fp16 output: the GPU side is rounded once more (half an fp16 ulp, ~1e-3 at |o| ~ 2)
         res["max_abs_vs_oracle_f16_out"] = res["cpu_baseline"]["max_abs_gpu_vs_oracle"]
         res["cpu_one_thread_small_workload"] = cpu_one_thread_small(ofmt, args.direct_p)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+SWEEP_FORMATS = (("nvfp4", 0, False), ("mxfp4", 1, False), ("mxfp4_direct_p", 1, True), ("mx4_pv8", 2, False))
+
+
+def run_sweep(path, torch, bnd, synth):
+    """The attention kernel alone (warmed up, 10 launches timed with HIP events on the launch
+    stream) for every (shape, format, mask) entry; each entry is appended to `path` as one JSON
+    line as soon as it is measured, and entries already in `path` are skipped."""
+    done = set()
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line:
+                    done.add(json.loads(line)["key"])
+    shapes = [("N%d" % n, 2, (4, 32, n, 128), n) for n in (1024, 2048, 4096, 8192, 16384)]
+    shapes += [("wl3", 3, None, None), ("wl4", 4, None, None)]
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+    for tag, wl, shape, n in shapes:
+        if shape is None:
+            w = synth.WORKLOADS[wl]
+            shape = (w["B"], w["H"], w["N"], w["D"])
+        masks = (True,) if wl == 4 else (False, True)
+        todo = [(f, fv, dp, c) for f, fv, dp in SWEEP_FORMATS for c in masks
+                if f"{tag}_{f}_{'causal' if c else 'noncausal'}" not in done]
+        if not todo:
+            continue
+        log(f"bench sweep: {tag} {shape}, {len(todo)} entries")
+        q_np, k_np, v_np = synth.make_qkv(2, N=n) if wl == 2 else synth.make_qkv(wl)
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (q_np, k_np, v_np))
+        del q_np, k_np, v_np
+        out = torch.empty(shape, dtype=torch.float16, device=dev)
+        B, H, N, D = shape
+        for f, fv, dp, c in todo:
+            Q, K, V = bnd.quant(q, bnd.ROLE_Q, fv), bnd.quant(k, bnd.ROLE_K, fv), bnd.quant(v, bnd.ROLE_V, fv)
+            launch = lambda: bnd.attn_fwd_into(fv, Q, K, V, shape, out, causal=c, direct_p=dp)  # noqa: E731
+            warm(launch, torch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            fl = 4.0 * B * H * N * N * D / (2 if c else 1)
+            entry = {"key": f"{tag}_{f}_{'causal' if c else 'noncausal'}", "B": B, "H": H, "N": N, "D": D,
+                     "format": f, "causal": c, "attn_kernel_ms": ms, "attn_tops": fl / (ms * 1e-3) / 1e12,
+                     "frac_fp4_peak": fl / (ms * 1e-3) / 1e12 / FP4_PEAK_TOPS}
+            with open(path, "a") as fh:
+                fh.write(json.dumps(entry) + "\n")
+            log(f"bench sweep: {entry['key']} {ms:.4f} ms {entry['attn_tops']:.0f} TOPS")
+            del Q, K, V
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": path, "entries_skipped": len(done)}), flush=True)
 
 
 BWD_METRIC = "8-bit attention bwd TOPS (10·B·H·N²·D/t: the five backward matmuls)"

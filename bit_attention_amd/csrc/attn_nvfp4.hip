@@ -75,7 +75,7 @@ __device__ __forceinline__ int lds_v(int row, int ch) {
 // Online-softmax state of one 16-query group (per lane: one query, a quarter of its channels).
 template <int D>
 struct RowState {
-  float m_u, R, Re, l;  // running maximum and frame R + Re (log2 units), normaliser (sum of E in that frame)
+  float m_u, R, l;  // running maximum and frame (log2 units), normaliser (sum of E in the frame)
   v4f O[D / 16];    // sum of P2-hat * V-hat in R's frame (P2 = 2688 E)
 };
 
@@ -95,15 +95,12 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
   }
   const float tS = xg_max(fmaxf(bm[0], bm[1]));
   const bool vis = tS > -INFINITY;
-  // tile maximum in log2 units, rounded toward -infinity (as in the MXFP4 kernel): T is the
-  // frame of this tile's P and of the accumulator, and S*k2 - T >= 0 only at the maximum
-  const float T0 = tS * k2;
-  const float Tdn = as_f(as_u(T0) - (unsigned)((__float_as_int(T0) >> 31) | 1));
-  float T = __builtin_fmaf(tS, k2, -T0) < 0.0f ? Tdn : T0;
-  T = vis ? T : 0.0f;
-  // the exact tile maximum tau = tS*k2 is T + eT with eT in [0, ulp(T)), exact in FP32; P, the
-  // normaliser and the accumulator all take tau as their frame, so that the maximal key has
-  // E = 1 exactly however large the scores (eT matters only when ulp(T) does)
+  // the exact tile maximum in log2 units, tau = tS*k2, is T + eT with T its FP32 rounding and eT
+  // the rounding error (exact, |eT| <= ulp(T)/2). P and this tile's share of the normaliser take
+  // tau as their frame, so that the maximal key has E = 1 exactly however large the scores (eT
+  // matters only when ulp(T) does); between tiles the frames are rescaled by 2^(T_old - T), which
+  // is as exact as the scores themselves are in FP32
+  const float T = vis ? tS * k2 : 0.0f;
   const float eT = vis ? __builtin_fmaf(tS, k2, -T) : 0.0f;
   const float m_new = fmaxf(st.m_u, T);
   const bool accept = vis && (T >= m_new - 64.0f);
@@ -113,9 +110,10 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
   v2h sh[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    // block maximum of P2 = 2688 E with E = clamp01(2^(S*k2 - T)): exactly 2688 for the block of
-    // the tile maximum (its argument lies in [0, ulp)), as the two-level P requires
-    const float pmax = 2688.0f * __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, -T)), 0.0f, 1.0f);
+    // block maximum of P2 = 2688 E with E = 2^(S*k2 - tau): the fma is exact for the block of
+    // the tile maximum, whose argument is then exactly 0, so its P2 is 2688 as the two-level P
+    // requires
+    const float pmax = 2688.0f * __builtin_amdgcn_exp2f(__builtin_fmaf(bm[h], k2, -T) - eT);
     const unsigned sb = e4m3_encode(pmax * (1.0f / 6.0f));
     sP[h] = e4m3_decode(sb);
     bq[h] = sP[h] > 0.0f ? bias - __builtin_amdgcn_logf(sP[h]) : -INFINITY;  // log2(P2/s)
@@ -141,11 +139,8 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
     Pf[u] = dequant8(pack_fp4_8(q), sh[h]);
   }
   const float lt = accept ? wl[0] * qsum[0] + wl[1] * qsum[1] : 0.0f;  // sum of E in T's frame
-  // frames are (R, Re) pairs: R - T is exact when the two are close, and any tile far below
-  // the running maximum is rejected
-  const float factor = accept ? __builtin_amdgcn_exp2f((st.R - T) + (st.Re - eT)) : 1.0f;
+  const float factor = accept ? __builtin_amdgcn_exp2f(st.R - T) : 1.0f;
   st.R = accept ? T : st.R;
-  st.Re = accept ? eT : st.Re;
   st.m_u = m_new;
   st.l = st.l * factor + lt;
 #pragma unroll
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   RowState<D> st[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    st[a].m_u = -INFINITY; st[a].R = -INFINITY; st[a].Re = 0.0f; st[a].l = 0.0f;
+    st[a].m_u = -INFINITY; st[a].R = -INFINITY; st[a].l = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st[a].O[dt] = v4f{0, 0, 0, 0};
   }
@@ -328,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   }
 
   // ---- epilogue: O / (2688 l); lane (g, c) holds channels 16dt + 4g + i of its query in each
-  // group. lse (when given): the row's log-sum-exp of the scaled scores, ln(2^(R + Re) * l)
+  // group. lse (when given): the row's log-sum-exp of the scaled scores, ln(2^R * l)
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const float L = xg_sum(st[a].l);
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     if (qi < N) {
       const float inv = 1.0f / (2688.0f * L);
       const int64_t row = bh * N + qi;
-      if (lse && g == 0) lse[row] = (st[a].R + (st[a].Re + __builtin_amdgcn_logf(L))) * 0.6931471805599453f;
+      if (lse && g == 0) lse[row] = (st[a].R + __builtin_amdgcn_logf(L)) * 0.6931471805599453f;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const v4f o = st[a].O[dt] * inv;

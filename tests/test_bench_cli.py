@@ -39,5 +39,6 @@ def test_sequence_length_must_be_a_multiple_of_256():
 def test_help_lists_the_options():
     r = run("--help")
     assert r.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--causal", "--fmt", "--direct-p", "--seq-len", "--workload"):
+    for opt in ("--gpus", "--steps", "--warmup", "--causal", "--fmt", "--direct-p", "--seq-len", "--workload",
+                "--sweep", "--backward"):
         assert opt in r.stdout
