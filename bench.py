@@ -426,10 +426,10 @@ def main():
             gpu_out = out.view(B * H, N, D).float().cpu().numpy()
         # the GPU's codes and scales of the last step, in the oracle's array shapes
         Np = (N + 127) // 128 * 128
-        vb = Np if fmt == bnd.MX4_PV8 else Np // 2
+        vb = 128 if fmt == bnd.MX4_PV8 else 64
         gpu_qkv = [(Q[0].cpu().numpy().reshape(B, H, N, D // 2), Q[1].cpu().numpy().reshape(B, H, N, D // blk)),
                    (K[0].cpu().numpy().reshape(B, H, N, D // 2), K[1].cpu().numpy().reshape(B, H, N, D // blk)),
-                   (V[0].cpu().numpy().reshape(B, H, D, vb), V[1].cpu().numpy().reshape(B, H, D, Np // blk))]
+                   (V[0].cpu().numpy().reshape(B, H, Np // 128, D, vb), V[1].cpu().numpy().reshape(B, H, Np // 128, D, 128 // blk))]
         res["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, shape, ofmt, args.direct_p, gpu_out=gpu_out,
                                            gpu_qkv=gpu_qkv)
         # fp16 output: the GPU side is rounded once more (half an fp16 ulp, ~1e-3 at |o| ~ 2)

@@ -153,9 +153,12 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
   const uint8_t* kc_h = kc + bh * N * (D / 2);
   const uint8_t* ks_h = ks + bh * N * NBD;
   const int64_t vrow_bytes = PV8 ? Np : Np / 2;
+  // V codes are stored tile by tile ([Np/128][D][VB]): a tile's codes are one contiguous run of
+  // D*VB bytes, piece e of it channel e/VPR, bytes 16*(e%VPR) of the channel's VB
   const uint8_t* vc_h = vc + bh * D * vrow_bytes;   // uniform base; per-thread offsets are 32-bit
   const uint8_t* vs_h = vs + bh * D * (Np / 32);
-  const unsigned vs_off = (unsigned)((tid >> 2) * (Np / 32) + (tid & 3));  // channel tid/4, block tid%4
+  // V scales are stored tile by tile, [Np/128][D][4]: byte tid of a tile is channel tid/4, block tid%4
+  const unsigned vs_off = (unsigned)tid;
   uint4 rk[KPT], rv[VPT];
   unsigned rks = 0, rvs = 0;
 #pragma unroll
@@ -179,10 +182,9 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     for (int i = 0; i < VPT; ++i) {
       const int e = tid + MX_NT * i;
       if (e < VPIECES)
-        rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)((e / VPR) * vrow_bytes + 16 * (e % VPR)) +
-                                                (unsigned)kt * (unsigned)VB);
+        rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)(16 * e) + (unsigned)kt * (unsigned)(VB * D));
     }
-    rvs = vs_h[vs_off + (unsigned)kt * 4u];
+    rvs = vs_h[vs_off + (unsigned)kt * (unsigned)(4 * D)];
   };
   prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {

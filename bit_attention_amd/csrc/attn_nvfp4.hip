@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   const uint8_t* ks_h = ks + bh * N * (D / 16);
   const uint8_t* vc_h = vc + bh * D * (Np / 2);
   const uint8_t* vs_h = vs + bh * D * (Np / 16);
-  const unsigned vc_off = (unsigned)(vd * (Np / 2) + vpart * CB);
-  const unsigned vs_off = (unsigned)(vd * (Np / 16) + vpart * (CB / 8));
+  // V codes and scales are stored tile by tile, [Np/128][D][64] and [Np/128][D][8]
+  const unsigned vc_off = (unsigned)(vd * 64 + vpart * CB);
+  const unsigned vs_off = (unsigned)(vd * 8 + vpart * (CB / 8));
   unsigned kr[CW], vr[CW], ksr = 0, vsr = 0;
 
   auto prefetch = [&](int kt) {
@@ -236,13 +237,13 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
       for (int u = 0; u < CW; ++u) kr[u] = 0;
       ksr = 0;
     }
-    const uint4* vsrc = reinterpret_cast<const uint4*>(vc_h + (vc_off + (unsigned)kt * 64u));
+    const uint4* vsrc = reinterpret_cast<const uint4*>(vc_h + (vc_off + (unsigned)kt * (unsigned)(64 * D)));
 #pragma unroll
     for (int u = 0; u < CW / 4; ++u) {
       const uint4 x = vsrc[u];
       vr[4 * u] = x.x; vr[4 * u + 1] = x.y; vr[4 * u + 2] = x.z; vr[4 * u + 3] = x.w;
     }
-    const uint8_t* vsp = vs_h + (vs_off + (unsigned)kt * 8u);
+    const uint8_t* vsp = vs_h + (vs_off + (unsigned)kt * (unsigned)(8 * D));
     if (CB / 8 == 4) vsr = *reinterpret_cast<const unsigned*>(vsp);
     else vsr = *reinterpret_cast<const unsigned short*>(vsp);
   };

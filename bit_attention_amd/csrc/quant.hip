@@ -13,31 +13,39 @@
 
 namespace sage {
 
-// Codes of n values with block scale s (E4M3 value or power of two): the E2M1 value nearest the
-// exact quotient x/s, ties to even. q = x*r (r = 1/s rounded) is refined by one Newton step on
-// the exact remainder; the refined q equals x/s exactly whenever x/s is a tie point, and is
-// within 2^-45 relative otherwise, while a non-tie fp16 x is at least 2^-12 relative away from
-// any tie, so the hardware's round-to-nearest-even conversion then decides correctly.
-// The sum in the last step turns a -0 quotient into +0, so the input's sign is put back (the
-// code's sign bit is the input's, -0 included).
-__device__ __forceinline__ float refine_quot(float x, float s, float r) {
-  float q = x * r;
-  float rem = __builtin_fmaf(-s, q, x);
-  return __builtin_copysignf(__builtin_fmaf(rem, r, q), x);
-}
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
-template <int BLK>
-__device__ __forceinline__ void encode_block(const float* v, float s, bool pow2_scale, unsigned* out_words) {
-  const float r = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+// Codes of a block of values with scale s (E4M3 value or power of two): the E2M1 value nearest
+// the exact quotient x/s, ties to even, the code's sign the input's (-0 included).
+// Power of two: x * (1/s) is exact. E4M3 s: 1/s is split as r_hi + r_lo, r_hi the hardware
+// reciprocal (within 1 ulp) scaled down by 2^-21, so that the residual e = 1 - s*r_hi is
+// positive and exact in one fma (s has at most 4 significant bits), and r_lo = e*r_hi >= 0;
+// r_hi + r_lo is 1/s within 2^-40 relative. q = fma(x, r_hi, x*r_lo) is then x/s within 2^-40
+// before its one rounding: q equals x/s exactly when x/s is one of the tie points (0.25, 0.75,
+// ..., 5), and otherwise x/s, with x fp16, is at least 2^-12 relative from every tie, so the
+// hardware's round-to-nearest-even conversion of q decides as it would on x/s. For x = -0 both
+// terms are -0 (r_hi, r_lo >= 0) and so is their sum. (An exhaustive check over every finite
+// fp16 x and every positive E4M3 s, with the reciprocal off by one ulp either way, agrees.)
+template <int BLK, typename Get>
+__device__ __forceinline__ void encode_block(Get v, float s, bool pow2_scale, unsigned* out_words) {
+  float rh, rl = 0.0f;
+  if (pow2_scale) {
+    // 1/s by exponent arithmetic: s = 2^X with X >= -26 for fp16 inputs (a normal float)
+    rh = s > 0.0f ? as_f((254u << 23) - as_u(s)) : 0.0f;
+  } else {
+    rh = s > 0.0f ? __builtin_amdgcn_rcpf(s) * (1.0f - 0x1p-21f) : 0.0f;
+    const float e = __builtin_fmaf(-s, rh, 1.0f);
+    rl = s > 0.0f ? e * rh : 0.0f;
+  }
 #pragma unroll
   for (int w = 0; w < BLK / 8; ++w) {
     unsigned word = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float x0 = v[8 * w + 2 * b], x1 = v[8 * w + 2 * b + 1];
+      const float x0 = v(8 * w + 2 * b), x1 = v(8 * w + 2 * b + 1);
       float q0, q1;
-      if (pow2_scale) { q0 = x0 * r; q1 = x1 * r; }  // exact
-      else { q0 = refine_quot(x0, s, r); q1 = refine_quot(x1, s, r); }
+      if (pow2_scale) { q0 = x0 * rh; q1 = x1 * rh; }  // exact
+      else { q0 = __builtin_fmaf(x0, rh, x0 * rl); q1 = __builtin_fmaf(x1, rh, x1 * rl); }
       switch (b) {
         case 0: word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, 0); break;
         case 1: word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, 1); break;
@@ -49,9 +57,15 @@ __device__ __forceinline__ void encode_block(const float* v, float s, bool pow2_
   }
 }
 
-// NVFP4 scale byte and value of a block with absolute maximum amax (exact FP32).
+// NVFP4 scale byte and value of a block with absolute maximum amax (an fp16 magnitude): the
+// E4M3 encoding of fl32(amax/6). The quotient is rounded correctly with one refinement step
+// (Markstein): q0 = amax * fl32(1/6), the remainder amax - 6*q0 is exact in one fma, and
+// q0 + remainder * fl32(1/6) rounds to fl32(amax/6) (checked exhaustively over fp16 amax).
 __device__ __forceinline__ unsigned nv_scale(float amax, float* s) {
-  const unsigned b = e4m3_encode(__fdiv_rn(amax, 6.0f));
+  constexpr float R6 = 1.0f / 6.0f;
+  const float q0 = amax * R6;
+  const float q = __builtin_fmaf(__builtin_fmaf(-6.0f, q0, amax), R6, q0);
+  const unsigned b = e4m3_encode(q);
   *s = e4m3_decode(b);
   return b;
 }
@@ -107,7 +121,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   float s;
   const unsigned sb = MX ? mx_scale(amax, &s) : nv_scale(amax, &s);
   unsigned words[BLK / 8];
-  encode_block<BLK>(v, s, MX, words);
+  encode_block<BLK>([&](int u) { return v[u]; }, s, MX, words);
   if (BLK == 16) {
     reinterpret_cast<uint2*>(codes)[b] = make_uint2(words[0], words[1]);
   } else {
@@ -116,130 +130,158 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
   scales[b] = (uint8_t)sb;
 }
 
-// V: one workgroup per (batch*head, run of `tpw` <= 4 consecutive 128-token tiles). Each tile, a
-// contiguous D*256-byte run of fp16, is loaded into registers with 16-byte loads while the
-// previous tile is encoded, then staged in LDS (row pitch D+8 halves keeps 16-byte alignment).
-// Item (channel d, block) gathers its values in slot order from LDS; the blocks of a channel sit
-// in consecutive lanes, so their code bytes form one contiguous run per channel. Four blocks'
-// scale bytes are gathered into one dword per tile, and after the run the lane of block 0 stores
-// the channel's scale bytes of all the run's tiles together. Token positions >= N are zero.
+// V: one workgroup of 2*D threads per (batch*head, run of `tpw` consecutive 128-token tiles).
+// Each tile, a contiguous D*256-byte run of fp16, is loaded into registers with 16-byte loads,
+// two tiles ahead (two register buffers, each refilled as soon as it is staged), then staged in
+// LDS (row pitch D+8 halves keeps 16-byte alignment). An item is (channel pair dp, block): it
+// reads its block's slots as 32-bit words (channels 2dp and 2dp+1 of one token) and encodes the
+// two channels' blocks. Lane l of wave w takes channel pair 16w + l%16 and block l/16 (NVFP4:
+// blocks 2(l/16) and 2(l/16)+1 in two passes), so the 64 lanes of one LDS read touch 16
+// consecutive words in each of 4 token rows whose word offsets differ by multiples of 16
+// modulo 64: no bank conflicts. Codes and scales are stored tile by tile ([B,H,Np/128,D,64]
+// and [B,H,Np/128,D,128/blk]; MXFP8 codes [B,H,Np/128,D,128]): a lane stores 16 (MXFP8: 32)
+// contiguous code bytes of each of its two channels, which complete whole 128-byte lines
+// within one tile, and lanes gather a channel's scale bytes with shuffles so that each wave
+// stores one contiguous run of them. Token positions >= N are zero.
 // FMT 0: NVFP4 (16-slot blocks, E4M3 scale of amax/6); 1: MXFP4 (32-slot blocks, E8M0 scale;
 // codes are the E2M1 value nearest the exact quotient, ties to even); 2: MXFP8 (32-slot blocks;
 // codes the E4M3 value nearest x / 2^X, ties to even, clamped to +-448; sign the input's).
 template <int D, int FMT>
-__global__ __launch_bounds__(256) void quant_v_tile_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales, int N, int64_t Np, int tpw) {
-  constexpr bool F8 = FMT == 2;
+__global__ __launch_bounds__(2 * D, FMT == 2 ? 2 : 3) void quant_v_tile_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales, int N, int64_t Np, int tpw) {
+  constexpr bool F8 = FMT == 2, NV = FMT == 0;
+  constexpr int NT = 2 * D;     // threads: one channel pair x one block (pair) each
   constexpr int PITCH = D + 8;  // halves
-  constexpr int BLK = FMT == 0 ? 16 : 32, NB = KV_TILE / BLK;
-  constexpr int CPB = F8 ? BLK : BLK / 2;  // code bytes per block
-  constexpr int PPT = KV_TILE * D / 8 / 256;  // 16-byte pieces of a tile per thread
+  constexpr int BLK = NV ? 16 : 32, NB = KV_TILE / BLK;
+  constexpr int PASSES = NV ? 2 : 1;
+  constexpr int LW = F8 ? 8 : 4;             // code dwords per lane, channel and tile (16 or 32 bytes)
+  constexpr int PPT = KV_TILE * D / 8 / NT;  // 16-byte pieces of a tile per thread
+  constexpr int64_t TB = F8 ? KV_TILE : KV_TILE / 2;  // code bytes per channel and tile
+  static_assert(NT % 64 == 0 && D / 32 == NT / 64, "one wave per group of 16 channel pairs");
   __shared__ __attribute__((aligned(16))) __half tile[KV_TILE * PITCH];
   const int64_t bh = blockIdx.y;
   const int ntiles = (int)(Np / KV_TILE);
   const int kt0 = blockIdx.x * tpw, kt1 = min(ntiles, kt0 + tpw);
-  uint4 pre[PPT];
-  // scale dwords of this thread's items, one per tile of the run (tpw <= 4, see v_tiles_per_wg),
-  // stored once at the end so that each channel's scale bytes of the run leave as one burst
-  constexpr int ITEMS = D * NB / 256;
-  unsigned sacc[ITEMS][4] = {};
-  // the tile's fp16 pieces into registers (token positions >= N read as zero)
-  auto load = [&](int kt) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int dp = 16 * (tid >> 6) + (lane & 15), j = lane >> 4;
+  // codes are stored tile by tile ([Np/128][D][TB]): this lane's 16 (MXFP8: 32) bytes of
+  // channel 2dp of tile kt sit at ((bh*ntiles + kt)*D + 2dp)*TB + that width times j
+  uint8_t* cbase = codes + (bh * ntiles * D + 2 * dp) * TB + (F8 ? 32 : 16) * j;
+  auto load = [&](int kt, uint4 (&buf)[PPT]) {
     const int tok0 = kt * KV_TILE, ntok = min(KV_TILE, N - tok0);
     const uint4* xs = reinterpret_cast<const uint4*>(x + (bh * N + tok0) * (int64_t)D);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int e = threadIdx.x + 256 * i, tok = e / (D / 8);
-      pre[i] = tok < ntok ? xs[e] : make_uint4(0, 0, 0, 0);
+      const int e = tid + NT * i, tok = e / (D / 8);
+      buf[i] = tok < ntok ? xs[e] : make_uint4(0, 0, 0, 0);
     }
   };
-  load(kt0);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int tix = kt - kt0;
+  auto store_codes = [&](int kt, const unsigned (&wd)[2][LW]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint4* dst = reinterpret_cast<uint4*>(cbase + ((int64_t)kt * D + c) * TB);
+#pragma unroll
+      for (int q = 0; q < LW / 4; ++q) dst[q] = make_uint4(wd[c][4 * q], wd[c][4 * q + 1], wd[c][4 * q + 2], wd[c][4 * q + 3]);
+    }
+  };
+  // One tile: stage `buf` in LDS, refill `buf` with tile ktn (if it is in the run) while this
+  // tile is encoded, encode into wd and store the tile's scales.
+  auto step = [&](int kt, uint4 (&buf)[PPT], int ktn, unsigned (&wd)[2][LW]) {
     __syncthreads();  // the previous tile's LDS reads are complete
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int e = threadIdx.x + 256 * i, tok = e / (D / 8), c8 = e % (D / 8);
-      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c8]) = pre[i];
+      const int e = tid + NT * i, tok = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<uint4*>(&tile[tok * PITCH + 8 * c8]) = buf[i];
     }
+    if (ktn < kt1) load(ktn, buf);
     __syncthreads();
-    if (kt + 1 < kt1) load(kt + 1);  // in flight while this tile is encoded and stored
-    static_assert((D * NB) % 256 == 0, "every lane of a quad takes part in each pass");
+    unsigned sbp[PASSES];  // scale bytes per pass: channel 2dp in byte 0, 2dp+1 in byte 1
 #pragma unroll
-    for (int ii = 0; ii < ITEMS; ++ii) {
-      const int it = threadIdx.x + 256 * ii;
-      const int d = it / NB, blk = it % NB;
-      float v[BLK];
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int blk = NV ? 2 * j + ps : j;
+      unsigned raw[BLK];
 #pragma unroll
-      for (int u = 0; u < BLK; ++u) v[u] = (float)tile[slot_token(blk * BLK + u) * PITCH + d];
-      float amax = 0.0f;
+      for (int u = 0; u < BLK; ++u)
+        raw[u] = *reinterpret_cast<const unsigned*>(&tile[slot_token(blk * BLK + u) * PITCH + 2 * dp]);
+      // block maxima of both channels at once: fp16 magnitudes order as their 15-bit patterns
+      v2u16 m2 = {0, 0};
 #pragma unroll
-      for (int u = 0; u < BLK; ++u) amax = fmaxf(amax, fabsf(v[u]));
-      float s;
-      const unsigned sb = FMT == 2 ? mx8_scale(amax, &s) : FMT == 1 ? mx_scale(amax, &s) : nv_scale(amax, &s);
-      unsigned words[CPB / 4];
-      if (F8) {
-        const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sb) << 23) : 0.0f;  // 1/s, exact
+      for (int u = 0; u < BLK; ++u) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2u16, raw[u] & 0x7FFF7FFFu));
+      unsigned sbc[2];
 #pragma unroll
-        for (int w = 0; w < CPB / 4; ++w) {
-          float q[4];
+      for (int c = 0; c < 2; ++c) {
+        // element u of channel c, converted where it is used (halves are taken by shifts: a
+        // bit cast of an element of a vector value reads element 0 with this compiler)
+        auto v = [&](int u) { return (float)__ushort_as_half((unsigned short)(c ? raw[u] >> 16 : raw[u] & 0xFFFFu)); };
+        const unsigned mm = __builtin_bit_cast(unsigned, m2);
+        const float amax = (float)__ushort_as_half((unsigned short)(c ? mm >> 16 : mm & 0xFFFFu));
+        float s;
+        sbc[c] = FMT == 2 ? mx8_scale(amax, &s) : FMT == 1 ? mx_scale(amax, &s) : nv_scale(amax, &s);
+        unsigned* out = &wd[c][F8 ? 0 : (BLK / 8) * ps];
+        if (F8) {
+          const float r = s > 0.0f ? as_f((unsigned)(254 - (int)sbc[c]) << 23) : 0.0f;  // 1/s, exact
 #pragma unroll
-          for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[4 * w + k] * r, -448.0f, 448.0f);
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
-          words[w] = (unsigned)word;
+          for (int w = 0; w < BLK / 4; ++w) {
+            float q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v(4 * w + k) * r, -448.0f, 448.0f);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+            out[w] = (unsigned)word;
+          }
+        } else {
+          encode_block<BLK>(v, s, FMT == 1, out);
         }
-      } else {
-        encode_block<BLK>(v, s, FMT == 1, words);
       }
-      uint4* crow = reinterpret_cast<uint4*>(codes + (bh * D + d) * (F8 ? Np : Np / 2) +
-                                             (int64_t)kt * (F8 ? KV_TILE : KV_TILE / 2) + blk * CPB);
-      if (CPB == 8) {
-        *reinterpret_cast<uint2*>(crow) = make_uint2(words[0], words[CPB / 4 > 1 ? 1 : 0]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < CPB / 16; ++q)
-          crow[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
-      }
-      // four consecutive blocks' scale bytes, gathered into the lane of the first
-      const unsigned s1 = __shfl_down(sb, 1, 4), s2 = __shfl_down(sb, 2, 4), s3 = __shfl_down(sb, 3, 4);
-      const unsigned wv = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u == tix) sacc[ii][u] = wv;
+      sbp[ps] = sbc[0] | (sbc[1] << 8);
     }
-  }
-  // the run's scale bytes of each channel are contiguous: NB bytes per tile. NVFP4 (NB = 8):
-  // the lane of blocks 0..3 takes the partner dword (blocks 4..7) from the lane 4 above it.
-  const int nt = kt1 - kt0;
-#pragma unroll
-  for (int ii = 0; ii < ITEMS; ++ii) {
-    const int it = threadIdx.x + 256 * ii;
-    const int d = it / NB, blk = it % NB;
-    unsigned w[8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (NB == 8) {
-        const unsigned hi = __shfl_down(sacc[ii][u], 4, 8);
-        w[2 * u] = sacc[ii][u]; w[2 * u + 1] = hi;
-      } else {
-        w[u] = sacc[ii][u];
+    // scale bytes of channel d sit at tile offset d*NB + block. NVFP4: this lane has blocks
+    // 2j, 2j+1 of both channels; the lane 16 above has 2j+2, 2j+3. MX: blocks j of both
+    // channels; lanes 16, 32, 48 above have blocks 1, 2, 3.
+    uint8_t* srun = scales + (bh * ntiles + kt) * (int64_t)(D * NB);
+    if (NV) {
+      const unsigned mine = (sbp[0] & 0xFFu) | ((sbp[1] & 0xFFu) << 8) | ((sbp[0] & 0xFF00u) << 8) | ((sbp[1] & 0xFF00u) << 16);
+      const unsigned up = __shfl_down(mine, 16, 64);  // blocks 2j+2, 2j+3 (lanes with j even use it)
+      // j even: dword of blocks 4(j/2)..+3 for channel 2dp (lo halves) and 2dp+1 (hi halves)
+      const unsigned ch0 = (mine & 0xFFFFu) | (up << 16), ch1 = (mine >> 16) | (up & 0xFFFF0000u);
+      // lanes j = 0 and j = 2 swap so that each stores 8 contiguous bytes: j = 0 takes channel
+      // 2dp (blocks 0..7), j = 2 channel 2dp+1
+      const unsigned give = j == 0 ? ch1 : ch0;
+      const unsigned got = __shfl_xor(give, 32, 64);
+      if ((j & 1) == 0) {
+        const unsigned lo = j == 0 ? ch0 : got, hi = j == 0 ? got : ch1;
+        *reinterpret_cast<uint2*>(srun + (2 * dp + (j >> 1)) * NB) = make_uint2(lo, hi);
+      }
+    } else {
+      const unsigned s1 = __shfl_down(sbp[0], 16, 64), s2 = __shfl_down(sbp[0], 32, 64), s3 = __shfl_down(sbp[0], 48, 64);
+      if (j == 0) {
+        const unsigned lo01 = (sbp[0] & 0xFFu) | ((s1 & 0xFFu) << 8), lo23 = (s2 & 0xFFu) | ((s3 & 0xFFu) << 8);
+        const unsigned hi01 = ((sbp[0] >> 8) & 0xFFu) | (s1 & 0xFF00u), hi23 = ((s2 >> 8) & 0xFFu) | (s3 & 0xFF00u);
+        *reinterpret_cast<uint2*>(srun + 2 * dp * NB) = make_uint2(lo01 | (lo23 << 16), hi01 | (hi23 << 16));
       }
     }
-    if (blk == 0) {
-      uint8_t* dst = scales + (bh * D + d) * (Np / BLK) + (int64_t)kt0 * NB;
-      const int nw = nt * NB / 4;  // dwords to store
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (q < nw) reinterpret_cast<unsigned*>(dst)[q] = w[q];
+  };
+  // Two register buffers: tiles kt0 and kt0+1 are both in flight from the start, and each
+  // buffer is refilled two tiles ahead as soon as it is staged.
+  uint4 bufa[PPT], bufb[PPT];
+  load(kt0, bufa);
+  if (kt0 + 1 < kt1) load(kt0 + 1, bufb);
+  for (int kp = kt0; kp < kt1; kp += 2) {
+    unsigned wd[2][LW];
+    step(kp, bufa, kp + 2, wd);
+    store_codes(kp, wd);
+    if (kp + 1 < kt1) {
+      step(kp + 1, bufb, kp + 3, wd);
+      store_codes(kp + 1, wd);
     }
   }
 }
 
-// tiles per workgroup of the V quantiser: up to 4, keeping at least 2048 workgroups
+// tiles per workgroup of the V quantiser: 4 or 2 (whole tile pairs), keeping at least 2048
+// workgroups where the shape allows
 inline int v_tiles_per_wg(int64_t ntiles, int BH) {
   int tpw = 4;
-  while (tpw > 1 && ((ntiles + tpw - 1) / tpw) * BH < 2048) tpw /= 2;
+  while (tpw > 2 && ((ntiles + tpw - 1) / tpw) * BH < 2048) tpw /= 2;
   return tpw;
 }
 
@@ -256,7 +298,7 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE, nt = Np / KV_TILE;
   const int tpw = v_tiles_per_wg(nt, BH);
-  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(256);
+  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(2 * D);
   if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
   else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
   return hipGetLastError();
@@ -268,7 +310,7 @@ hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* co
   uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
   const int64_t nt = Np / KV_TILE;
   const int tpw = v_tiles_per_wg(nt, BH);
-  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(256);
+  const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(2 * D);
   if (mx) {
     if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
     else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);

@@ -84,8 +84,11 @@ int sage_fp4_slot_token(int slot);
 
 /* Bytes needed for the codes / scales of one quantised tensor (0 for invalid arguments).
  *   Q, K: codes [B,H,N,D/2], scales [B,H,N,D/16] (NVFP4) or [B,H,N,D/32] (MXFP4);
- *   V:    codes [B,H,D,Np/2], scales [B,H,D,Np/16] or [B,H,D,Np/32], Np = ceil(N/128)*128;
- *         MX4_PV8: codes [B,H,D,Np] (one E4M3 byte per element), scales [B,H,D,Np/32]. */
+ *   V:    codes [B,H,Np/128,D,64], scales [B,H,Np/128,D,8] or [B,H,Np/128,D,4],
+ *         Np = ceil(N/128)*128; MX4_PV8: codes [B,H,Np/128,D,128] (one E4M3 byte per element),
+ *         scales [B,H,Np/128,D,4]. Tile by tile: one 128-token tile's codes, and its scales,
+ *         for every channel are one contiguous run (the quantiser writes, and the attention
+ *         reads, whole runs); inside a tile a channel's 128 slots are in slot order. */
 size_t sage_fp4_codes_bytes(int role, int fmt, int B, int H, int N, int D);
 size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D);
 

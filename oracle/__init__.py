@@ -93,8 +93,8 @@ def quant(role: int, fmt: int, x: np.ndarray):
     b = blk(fmt)
     if role == ROLE_V:
         Np = padded_n(N)
-        codes = np.zeros((B, H, D, Np if fmt == MX4_PV8 else Np // 2), np.uint8)
-        scales = np.zeros((B, H, D, Np // b), np.uint8)
+        codes = np.zeros((B, H, Np // KV_TILE, D, KV_TILE if fmt == MX4_PV8 else KV_TILE // 2), np.uint8)
+        scales = np.zeros((B, H, Np // KV_TILE, D, KV_TILE // b), np.uint8)
     else:
         codes = np.zeros((B, H, N, D // 2), np.uint8)
         scales = np.zeros((B, H, N, D // b), np.uint8)
@@ -222,13 +222,28 @@ def e4m3_table() -> np.ndarray:
 
 def dequant(fmt, codes, scales) -> np.ndarray:
     """Values code*scale (float64) along the last axis. With MX4_PV8 the codes are the FP8 bytes
-    of V (or P); its Q and K codes are MXFP4 and dequantise with fmt = MXFP4."""
+    of V (or P); its Q and K codes are MXFP4 and dequantise with fmt = MXFP4. V's codes and
+    scales go through v_by_channel() first."""
+    if np.ndim(codes) != np.ndim(scales) or np.ndim(codes) > 4:
+        raise ValueError("codes and scales must be [..., rows, cols] alike (V: use v_by_channel first)")
     if fmt == MX4_PV8:
         c = e4m3_table()[codes].astype(np.float64)
     else:
         c = e2m1_table()[unpack(codes)].astype(np.float64)
     s = scale_table(fmt)[scales].astype(np.float64)
     return c * np.repeat(s, blk(fmt), axis=-1)
+
+
+def _tiles_to_rows(a: np.ndarray) -> np.ndarray:
+    B, H, T, D, w = a.shape
+    return np.ascontiguousarray(np.transpose(a, (0, 1, 3, 2, 4))).reshape(B, H, D, T * w)
+
+
+def v_by_channel(codes: np.ndarray, scales: np.ndarray):
+    """V's codes and scales from their stored tile-by-tile layouts ([B,H,Np/128,D,64 or 128] and
+    [B,H,Np/128,D,128/blk]) to one row per channel ([B,H,D,Np/2 or Np] and [B,H,D,Np/blk]),
+    slot positions in order along the row: the form dequant() takes."""
+    return _tiles_to_rows(codes), _tiles_to_rows(scales)
 
 
 def slot_tokens() -> np.ndarray:

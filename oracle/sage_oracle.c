@@ -238,9 +238,20 @@ static unsigned get_code(const uint8_t* packed, int64_t pos) {
   return (pos % 2 == 0) ? (b & 15u) : (b >> 4);
 }
 
-/* V code at slot position pos of one channel row: a nibble, or a byte in the R14 variant */
-static unsigned get_v_code(int fmt, const uint8_t* row, int64_t pos) { return pv8(fmt) ? row[pos] : get_code(row, pos); }
-static int64_t v_row_bytes(int fmt, int64_t Np) { return pv8(fmt) ? Np : Np / 2; }
+/* Index of V's scale byte for channel d at slot position p of head bh: scales are stored tile
+ * by tile, [B*H][Np/128][D][128/blk], so that one tile's scales for all channels are one run. */
+static int64_t v_scale_index(int64_t bh, int d, int64_t p, int D, int64_t Np, int blk) {
+  const int64_t nb = ORC_KV_TILE / blk;
+  return ((bh * (Np / ORC_KV_TILE) + p / ORC_KV_TILE) * D + d) * nb + (p % ORC_KV_TILE) / blk;
+}
+
+/* V codes are stored tile by tile too, [B*H][Np/128][D][128 slots], a nibble per slot (a byte
+ * in the R14 variant), so that one tile's codes for all channels are one run. Code index of
+ * channel d at slot position p of head bh: */
+static int64_t v_code_index(int64_t bh, int d, int64_t p, int D, int64_t Np) {
+  return ((bh * (Np / ORC_KV_TILE) + p / ORC_KV_TILE) * D + d) * ORC_KV_TILE + p % ORC_KV_TILE;
+}
+static unsigned get_v_code(int fmt, const uint8_t* codes, int64_t i) { return pv8(fmt) ? codes[i] : get_code(codes, i); }
 
 int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
               uint8_t* codes, uint8_t* scales) {
@@ -277,8 +288,6 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
     const int64_t bh = row / D;
     const int d = (int)(row % D);
     const uint16_t* xh = x + bh * N * D;
-    uint8_t* crow = codes + (bh * D + d) * v_row_bytes(fmt, Np);
-    uint8_t* srow = scales + (bh * D + d) * (Np / blk);
     float xb[32];
     uint8_t cb[32], sb;
     for (int64_t p0 = 0; p0 < Np; p0 += blk) {
@@ -289,10 +298,11 @@ int orc_quant(int role, int fmt, const uint16_t* x, int B, int H, int N, int D,
       }
       quant_block(fmt, xb, blk, cb, &sb);
       for (int u = 0; u < blk; ++u) {
-        if (pv8(fmt)) crow[p0 + u] = cb[u];
-        else put_code(crow, p0 + u, cb[u]);
+        const int64_t i = v_code_index(bh, d, p0 + u, D, Np);
+        if (pv8(fmt)) codes[i] = cb[u];
+        else put_code(codes, i, cb[u]);
       }
-      srow[p0 / blk] = sb;
+      scales[v_scale_index(bh, d, p0, D, Np, blk)] = sb;
     }
   }
   return ORC_OK;
@@ -408,10 +418,9 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
     double vhead = 0.0;
     if (slack && direct_p) {
       for (int d = 0; d < D; ++d) {
-        const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
-        const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
         for (int64_t p = 0; p < Np; ++p) {
-          double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+          double v = fabs((double)pv_val(fmt, get_v_code(fmt, v_codes, v_code_index(bh, d, p, D, Np))) *
+                          (double)scale_val(fmt, v_scales[v_scale_index(bh, d, p, D, Np, blk)]));
           if (v > vhead) vhead = v;
         }
       }
@@ -456,16 +465,16 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
       l = alpha * l + beta * sumE;
       const float w = beta / Kp;                                          /* R7/R9 */
       for (int d = 0; d < D; ++d) {
-        const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
-        const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
         float acc = 0.0f;
         for (int b = 0; b < ORC_KV_TILE / blk; ++b) {
           float inner = 0.0f;
           for (int u = 0; u < blk; ++u) {
             const int s = b * blk + u;
-            inner += pv_val(fmt, pc[s]) * pv_val(fmt, get_v_code(fmt, vc, (int64_t)kt * ORC_KV_TILE + s));
+            inner += pv_val(fmt, pc[s]) *
+                     pv_val(fmt, get_v_code(fmt, v_codes, v_code_index(bh, d, (int64_t)kt * ORC_KV_TILE + s, D, Np)));
           }
-          const float sc = scale_val(fmt, ps[b]) * scale_val(fmt, vsc[((int64_t)kt * ORC_KV_TILE) / blk + b]);
+          const float sc = scale_val(fmt, ps[b]) *
+                           scale_val(fmt, v_scales[v_scale_index(bh, d, (int64_t)kt * ORC_KV_TILE + b * blk, D, Np, blk)]);
           acc += sc * inner;
         }
         O[d] = alpha * O[d] + w * acc;
@@ -477,10 +486,9 @@ static int attn_fwd_impl(int fmt, int direct_p, const uint8_t* q_codes, const ui
         for (int s = 0; s < ORC_KV_TILE; ++s) {
           double mv = 0.0;
           for (int d = 0; d < D; ++d) {
-            const uint8_t* vc = v_codes + (bh * D + d) * v_row_bytes(fmt, Np);
-            const uint8_t* vsc = v_scales + (bh * D + d) * (Np / blk);
             const int64_t p = (int64_t)kt * ORC_KV_TILE + s;
-            double v = fabs((double)pv_val(fmt, get_v_code(fmt, vc, p)) * (double)scale_val(fmt, vsc[p / blk]));
+            double v = fabs((double)pv_val(fmt, get_v_code(fmt, v_codes, v_code_index(bh, d, p, D, Np))) *
+                            (double)scale_val(fmt, v_scales[v_scale_index(bh, d, p, D, Np, blk)]));
             if (v > mv) mv = v;
           }
           vmax[s] = mv + vhead;

@@ -28,11 +28,14 @@
  *   x (fp16 bits)        [B,H,N,D]
  *   Q/K codes            [B,H,N,D/2]      element 2i in the low nibble of byte i
  *   Q/K scales           [B,H,N,D/16] (E4M3) or [B,H,N,D/32] (E8M0)
- *   V codes              [B,H,D,Np/2]     tokens in slot order inside each 128-token tile
- *   V scales             [B,H,D,Np/16] or [B,H,D,Np/32]
+ *   V codes              [B,H,Np/128,D,64]  tile by tile, tokens in slot order inside each
+ *                        128-token tile (slot 2i in the low nibble of byte i of the channel's 64)
+ *   V scales             [B,H,Np/128,D,8] or [B,H,Np/128,D,4]   tile by tile as well: one
+ *                        128-token tile's codes, and its scales, for every channel are one run
  *   Np = ceil(N/128)*128; token positions >= N are zero.
  * ORC_MX4_PV8 (FP4 QK, FP8 PV; reading R14 in sage_oracle.c): Q/K codes and scales as MXFP4;
- *   V codes [B,H,D,Np] one E4M3 byte per element (slot order), V scales [B,H,D,Np/32] E8M0.
+ *   V codes [B,H,Np/128,D,128] one E4M3 byte per element (slot order), V scales
+ *   [B,H,Np/128,D,4] E8M0.
  * Slot order inside a 128-token tile: slot s = 32g + 4t + i holds token 16t + 4g + i
  * (g in 0..3, t in 0..7, i in 0..3). Blocks of P and of V are consecutive slots.
  */

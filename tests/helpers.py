@@ -39,8 +39,8 @@ def gpu_quant(x, role, fmt):
     blk = 16 if fmt == 0 else 32
     if role == 2:
         Np = orc.padded_n(N)
-        vb = Np if fmt == 2 else Np // 2
-        return c.cpu().numpy().reshape(B, H, D, vb), s.cpu().numpy().reshape(B, H, D, Np // blk)
+        vb = 128 if fmt == 2 else 64
+        return c.cpu().numpy().reshape(B, H, Np // 128, D, vb), s.cpu().numpy().reshape(B, H, Np // 128, D, 128 // blk)
     return c.cpu().numpy().reshape(B, H, N, D // 2), s.cpu().numpy().reshape(B, H, N, D // blk)
 
 

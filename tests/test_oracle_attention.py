@@ -22,7 +22,7 @@ VARIANTS = [(orc.NVFP4, False), (orc.MXFP4, False), (orc.MXFP4, True), (orc.MX4_
 
 def vhat_tokens(fmt, v_codes, v_scales, N):
     """Dequantised V back in token order: [B,H,N,D] (float64)."""
-    vd = orc.dequant(fmt, v_codes, v_scales)  # [B,H,D,Np] in slot order
+    vd = orc.dequant(fmt, *orc.v_by_channel(v_codes, v_scales))  # [B,H,D,Np] in slot order
     B, H, D, Np = vd.shape
     tok = np.empty(Np, np.int64)
     st = orc.slot_tokens()
@@ -62,7 +62,7 @@ def test_v_quant_layout_one_hot(fmt):
         v = np.zeros((1, 1, N, D), np.float16)
         v[0, 0, jstar, dstar] = 6.0
         codes, scales = orc.quant(orc.ROLE_V, fmt, v)
-        vd = orc.dequant(fmt, codes, scales)[0, 0]
+        vd = orc.dequant(fmt, *orc.v_by_channel(codes, scales))[0, 0]
         nz = np.argwhere(vd != 0)
         assert nz.tolist() == [[dstar, (jstar // 128) * 128 + st.index(jstar % 128)]]
         assert vd[dstar, (jstar // 128) * 128 + st.index(jstar % 128)] == 6.0

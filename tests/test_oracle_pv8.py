@@ -26,9 +26,10 @@ def torch_e4m3_code(y):
 
 def vhat_tokens_fp8(v_codes, v_scales, N):
     """V-hat in token order [B,H,N,D] float64, decoded with torch's float8 codecs."""
+    v_codes, v_scales = orc.v_by_channel(v_codes, v_scales)
     B, H, D, Np = v_codes.shape
-    vals = torch.from_numpy(v_codes.copy()).view(torch.float8_e4m3fn).double().numpy()
-    sc = torch.from_numpy(v_scales.copy()).view(torch.float8_e8m0fnu).double().numpy()
+    vals = torch.from_numpy(v_codes).view(torch.float8_e4m3fn).double().numpy()
+    sc = torch.from_numpy(v_scales).view(torch.float8_e8m0fnu).double().numpy()
     vd = vals * np.repeat(sc, 32, axis=-1)
     st = orc.slot_tokens()
     tok = np.array([(p // 128) * 128 + st[p % 128] for p in range(Np)])
@@ -99,13 +100,13 @@ def test_v_lossless_when_representable():
     B, H, N, D = 1, 2, 300, 64
     v = rng.choice(np.array([0.5, -0.75, 1.0, 1.25, -2.0, 3.5, -4.0, 7.0], np.float16), size=(B, H, N, D))
     vc, vs = orc.quant(orc.ROLE_V, PV8, v)
-    assert vc.shape == (B, H, D, 384) and vs.shape == (B, H, D, 12)
+    assert vc.shape == (B, H, 3, D, 128) and vs.shape == (B, H, 3, D, 4)
     vh = vhat_tokens_fp8(vc, vs, N)
     assert np.array_equal(vh, v.astype(np.float64))
     # token positions >= N (the padding of the last tile) are zero codes
     st = orc.slot_tokens()
-    pad = [256 + s for s in range(128) if 256 + st[s] >= N]
-    assert np.all(vc[..., pad] == 0)
+    pad = [s for s in range(128) if 256 + st[s] >= N]
+    assert np.all(vc[:, :, 2][..., pad] == 0)
 
 
 @pytest.mark.parametrize("causal", [False, True])
