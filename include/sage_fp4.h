@@ -32,9 +32,8 @@
  *   - causal: key j is visible to query i iff j <= i. Exact key ties and decisions within a
  *     few ulp of a rounding boundary may round either way (exp and FP32 summation order differ
  *     from the oracle by a few ulp); codes and scales of Q, K, V are bit-exact.
- *   - exponents are formed in FP32: with NVFP4, P carries a relative error of about
- *     2^-24 * |t * log2(e)| (t the tile's largest scaled score), below 1e-4 while scaled scores
- *     stay under about 1e3 and near 1% at 1e5.
+ *   - exponents are formed in FP32 relative to the tile maximum, carried with its exact
+ *     rounding error, so the outputs stay within the same bar at any score magnitude.
  *
  * Conventions for every entry point:
  *   - all tensor pointers are DEVICE pointers owned by the caller; the library allocates
