@@ -1,5 +1,6 @@
 """Shared helpers for the GPU tests: run the HIP path through the C ABI and the oracle on the same
 seeded inputs (each side quantises for itself; nothing flows from one to the other)."""
+import os
 import sys
 
 import numpy as np
@@ -8,6 +9,17 @@ import oracle as orc
 from bit_attention_amd import synth
 
 _CACHE = {}
+
+
+# worst |gpu - oracle| / bound of each test that checks against a bound, by test id; the
+# session's terminal summary prints them (tests/conftest.py)
+BOUND_RATIOS = {}
+
+
+def record_ratio(what, ratio):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    key = f"{test} {what}"
+    BOUND_RATIOS[key] = max(BOUND_RATIOS.get(key, 0.0), float(ratio))
 
 
 def say(*a):

@@ -19,7 +19,7 @@ import pytest
 import oracle as orc
 from oracle import bwd as obwd
 from bit_attention_amd import synth
-from helpers import say, to_gpu
+from helpers import record_ratio, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,7 @@ def _check_grads(got, ref, bd, f16_out=False, heads=None):
         err = np.abs(g - r)
         worst = float(np.max(err / bound))
         say(f"  {names[t]}: max err {err.max():.3e}, max err/bound {worst:.3f}, max |ref| {np.abs(r).max():.3e}")
+        record_ratio(names[t], worst)
         assert worst <= 1.0, names[t]
 
 
