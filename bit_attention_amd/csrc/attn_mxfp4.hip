@@ -13,8 +13,9 @@
 // on gfx950 MFMA and plain VALU instructions do not overlap (measured), so what counts is the
 // number of VALU instructions per score, which the layout keeps at about six. Workgroups are
 // ordered so that each XCD walks through whole heads. The next tile's codes and scales are
-// loaded into registers as soon as the current tile's scores are consumed, so the global loads
-// overlap the PV products and the barrier. Scale bytes sit in LDS so that a lane reads its eight
+// loaded into registers while the current tile is computed (after its QK products, or after its
+// softmax for plain MXFP4 at D = 128), so the global loads overlap the rest of the tile and the
+// barrier. Scale bytes sit in LDS so that a lane reads its eight
 // K (or V) scales of a tile as one 8-byte word; the instruction's op_sel bits pick the byte.
 // Instances: plain MXFP4, Direct-P (normaliser from the rounded P) and FP8-PV (P, V in MXFP8).
 // P has no first level (E8M0 scales cover its range): its codes are E = 2^(x - t) quantised with
@@ -223,6 +224,11 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       // the scale operand's byte t & 3 is selected by the instruction's op_sel bits
       S[t] = mfma_sel<4>(a, qf, v4f{0, 0, 0, 0}, t & 3, (int)(t < 4 ? ksw.x : ksw.y), qsc);
     }
+    // the next tile's loads: issued here, a softmax ahead of their use, for the Direct-P, FP8-PV
+    // and D = 64 instances (1-3% faster each, measured); after the softmax for plain MXFP4 at
+    // D = 128, where the registers they hold through the softmax cost more than the latency
+    constexpr bool EARLY = DIRECT_P || PV8 || D == 64;
+    if (EARLY && kt + 1 < kt_end) prefetch(kt + 1);
     const int kbase = kt * KV_TILE;
     if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
 #pragma unroll
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       }
       psc = keep ? X + 127 : 0;
     }
-    if (kt + 1 < kt_end) prefetch(kt + 1);
+    if (!EARLY && kt + 1 < kt_end) prefetch(kt + 1);
     if (!accept) esum = 0.0f;
     const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
     R = accept ? T : R;
