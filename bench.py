@@ -13,6 +13,9 @@ bounded sample of the same workload.
 `--sweep PATH` times the attention alone over the N sweep and workloads 3 and 4, every format and
 mask, appending one JSON line per entry to PATH and skipping entries already there.
 
+`--kv16` (NVFP4) makes the step quantise, dequantise K and V once to fp16 (sage_fp4_kv16_prep)
+and run sage_fp4_attn_fwd_kv16 on them; the prep is timed apart (`kv16_prep_ms`).
+
 `--backward` times the 8-bit backward instead (sage_fp4_attn_bwd as its three stages, on the
 forward's FP4 Q/K, output and log-sum-exp): `value` = 10*B*H*N^2*D / (backward time), the
 roofline is that of its dK/dV kernel, and the CPU baseline is the backward oracle on one head.
@@ -210,6 +213,9 @@ def main():
     ap.add_argument("--fmt", choices=["nvfp4", "mxfp4", "mx4_pv8"], default="nvfp4",
                     help="mx4_pv8: MXFP4 Q and K, MXFP8 P and V")
     ap.add_argument("--direct-p", action="store_true", help="time sage_fp4_attn_fwd_direct_p (mxfp4 only)")
+    ap.add_argument("--kv16", action="store_true",
+                    help="nvfp4: the step dequantises K and V once (sage_fp4_kv16_prep) and runs "
+                         "sage_fp4_attn_fwd_kv16 on them")
     ap.add_argument("--seq-len", type=int, default=WORKLOAD["N"],
                     help="N of the sweep at B=4 H=32 D=128 (default 4096)")
     ap.add_argument("--workload", type=int, choices=[2, 3, 4], default=2,
@@ -243,6 +249,9 @@ def main():
     if args.direct_p and fmt != bnd.MXFP4:
         print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
         sys.exit(2)
+    if args.kv16 and (fmt != bnd.NVFP4 or args.backward):
+        print("bench.py: --kv16 needs --fmt nvfp4 (forward)", file=sys.stderr)
+        sys.exit(2)
     if args.workload == 2:
         B, H, D = (WORKLOAD[k] for k in "BHD")
         N = args.seq_len
@@ -268,11 +277,17 @@ def main():
     K = bnd.alloc_quant(bnd.ROLE_K, fmt, *shape)
     V = bnd.alloc_quant(bnd.ROLE_V, fmt, *shape)
     out = torch.empty(shape, dtype=torch.float16, device=dev)
+    kv16 = torch.empty(bnd.sage_fp4_kv16_bytes(*shape), dtype=torch.uint8, device=dev) if args.kv16 else None
     stream = torch.cuda.current_stream()
     causal = args.causal
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+
+    def attention():
+        if args.kv16:
+            bnd.attn_fwd_kv16_into(Q, kv16, shape, out, causal=causal)
+        else:
+            bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
 
     def step(i=None):
         if i is not None:
@@ -282,9 +297,13 @@ def main():
         bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
         if i is not None:
             ev[i][1].record(stream)
-        bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
+        if args.kv16:
+            bnd.kv16_prep(K, V, shape, kv16)
         if i is not None:
             ev[i][2].record(stream)
+        attention()
+        if i is not None:
+            ev[i][3].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -295,8 +314,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.kv16 else None
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
 
     flops_formula = 4.0 * B * H * N * N * D
     flops = flops_formula / 2 if causal else flops_formula  # causal: masked work is skipped
@@ -305,11 +325,15 @@ def main():
     kfile = "attn_nvfp4.hip" if fmt == bnd.NVFP4 else "attn_mxfp4.hip"
     kname = {bnd.NVFP4: "attn_nvfp4", bnd.MXFP4: "attn_mxfp4", bnd.MX4_PV8: "attn_mx4pv8"}[fmt]
     kname += "_direct_p" if args.direct_p else ""
+    kname += "_kv16" if args.kv16 else ""
     tkey = f"{kname}_b{B}_h{H}_n{N}_d{D}_{'causal' if causal else 'noncausal'}"
     traffic = load_traffic(kfile, tkey)
     # the metric's denominator is the dense FP4 MFMA peak for every format; the fraction of the
     # peak of the MFMA the kernel actually runs on is reported beside it
-    if fmt == bnd.NVFP4:
+    if fmt == bnd.NVFP4 and args.kv16:
+        own_peak = FP16_PEAK_TFLOPS
+        kdesc = "attn_nvfp4_kernel, KV16 instance (fp16 MFMA; K-hat and V-hat read dequantised from the prep)"
+    elif fmt == bnd.NVFP4:
         own_peak, kdesc = FP16_PEAK_TFLOPS, "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"
     elif fmt == bnd.MXFP4:
         own_peak = FP4_PEAK_TOPS
@@ -328,11 +352,13 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.fmt, "data": DATA_NOTES[args.workload],
         "config": {"workload": f"{WORKLOAD_NAMES[args.workload]} B={B} H={H} N={N} D={D} {args.fmt}"
-                               f"{' direct-p' if args.direct_p else ''} {'causal' if causal else 'non-causal'}",
+                               f"{' direct-p' if args.direct_p else ''}{' kv16' if args.kv16 else ''}"
+                               f" {'causal' if causal else 'non-causal'}",
                    "B": B, "H": H, "N": N, "D": D, "causal": causal, "format": args.fmt,
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
         "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
         "quant_ms_3_tensors": quant_ms, "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+        "kv16_prep_ms": prep_ms,
         # not in counter runs: their one calibration copy must be the only copy kernel
         "copy_ceiling_gbs": None if args.calibrate_copy else copy_ceiling_gbs(torch),
         "flops_counted": flops, "flops_formula_4BHN2D": flops_formula,
@@ -359,11 +385,11 @@ def main():
     if not args.no_extras:
         # the same attention launch alone, back to back (warmed up for 0.15 s, then 10 timed
         # launches): the kernel-benchmark convention, without the quantisation kernels in between
-        warm(lambda: bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p), torch)
+        warm(attention, torch)
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(stream)
         for _ in range(10):
-            bnd.attn_fwd_into(fmt, Q, K, V, shape, out, causal=causal, direct_p=args.direct_p)
+            attention()
         a1.record(stream)
         torch.cuda.synchronize()
         res["attn_alone_ms"] = a0.elapsed_time(a1) / 10
@@ -414,6 +440,31 @@ def main():
             if f2 == bnd.MX4_PV8:  # half the flops at the FP4 rate (QK), half at the FP8 rate (PV)
                 mixed = 2.0 / (1.0 / FP4_PEAK_TOPS + 1.0 / FP8_PEAK_TOPS)
                 extras[name]["frac_fp4_fp8_mixed_peak"] = t / mixed
+        if fmt == bnd.NVFP4 and not args.kv16:
+            # the same NVFP4 operands through sage_fp4_kv16_prep + sage_fp4_attn_fwd_kv16 (outputs
+            # equal bit for bit): the prep once, then the attention alone, both masks
+            kv = torch.empty(bnd.sage_fp4_kv16_bytes(*shape), dtype=torch.uint8, device=dev)
+            warm(lambda: bnd.kv16_prep(K, V, shape, kv), torch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                bnd.kv16_prep(K, V, shape, kv)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            prep = e0.elapsed_time(e1) / 10
+            for c2 in (False, True):
+                warm(lambda: bnd.attn_fwd_kv16_into(Q, kv, shape, out, causal=c2), torch)
+                e0.record(stream)
+                for _ in range(10):
+                    bnd.attn_fwd_kv16_into(Q, kv, shape, out, causal=c2)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / 10
+                t = (flops_formula / 2 if c2 else flops_formula) / (ms * 1e-3) / 1e12
+                extras["nvfp4_kv16_" + ("causal" if c2 else "noncausal")] = {
+                    "attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS,
+                    "kv16_prep_ms": prep, "prep_plus_attn_ms": prep + ms}
+            del kv
         res["extras"] = extras
 
     if not args.no_cpu_baseline:

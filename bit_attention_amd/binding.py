@@ -2,7 +2,8 @@
 of the computation runs in the library's HIP kernels. PyTorch supplies device memory and streams.
 
 The functions named like the C entry points take raw pointers/ints; the convenience wrappers
-(`quant`, `attn_fwd`, `attn_bwd_into`) take torch tensors and pass the current stream."""
+(`quant`, `attn_fwd`, `kv16_prep`, `attn_fwd_kv16_into`, `attn_bwd_into`) take torch tensors and
+pass the current stream."""
 from __future__ import annotations
 
 import ctypes as C
@@ -20,7 +21,8 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP", -7: "SAGE_ERR_WORKSPACE"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
-           "sage_fp4_attn_fwd_lse", "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
+           "sage_fp4_attn_fwd_lse", "sage_fp4_kv16_bytes", "sage_fp4_kv16_prep", "sage_fp4_attn_fwd_kv16",
+           "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
            "sage_fp4_attn_bwd_stage", "sage_fp4_attn_bwd_noalloc", "sage_fp4_status_string"]
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGE_BWD_NOALLOC_SCRATCH_BYTES
 
@@ -54,6 +56,10 @@ def lib():
         L.sage_fp4_attn_fwd_direct_p.restype = I
         L.sage_fp4_attn_fwd_lse.argtypes = [I, I, P, P, P, P, P, P, I, I, I, I, I, F, P, I, P, P]
         L.sage_fp4_attn_fwd_lse.restype = I
+        L.sage_fp4_kv16_bytes.argtypes = [I, I, I, I]; L.sage_fp4_kv16_bytes.restype = S
+        L.sage_fp4_kv16_prep.argtypes = [P, P, P, P, I, I, I, I, P, S, P]; L.sage_fp4_kv16_prep.restype = I
+        L.sage_fp4_attn_fwd_kv16.argtypes = [P, P, P, S, I, I, I, I, I, F, P, I, P, P]
+        L.sage_fp4_attn_fwd_kv16.restype = I
         L.sage_fp4_attn_bwd_workspace_bytes.argtypes = [I, I, I, I]
         L.sage_fp4_attn_bwd_workspace_bytes.restype = S
         L.sage_fp4_attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, P, I, P, S, P]
@@ -114,6 +120,20 @@ def sage_fp4_attn_fwd_lse(fmt, direct_p, qc, qs, kc, ks, vc, vs, B, H, N, D, cau
                           out_dtype, lse_ptr, stream_ptr) -> int:
     return lib().sage_fp4_attn_fwd_lse(fmt, int(direct_p), qc, qs, kc, ks, vc, vs, B, H, N, D, int(causal),
                                        float(sm_scale), out_ptr, out_dtype, lse_ptr, stream_ptr)
+
+
+def sage_fp4_kv16_bytes(B, H, N, D) -> int:
+    return lib().sage_fp4_kv16_bytes(B, H, N, D)
+
+
+def sage_fp4_kv16_prep(kc, ks, vc, vs, B, H, N, D, kv16_ptr, kv16_bytes, stream_ptr) -> int:
+    return lib().sage_fp4_kv16_prep(kc, ks, vc, vs, B, H, N, D, kv16_ptr, kv16_bytes, stream_ptr)
+
+
+def sage_fp4_attn_fwd_kv16(qc, qs, kv16_ptr, kv16_bytes, B, H, N, D, causal, sm_scale, out_ptr, out_dtype,
+                           lse_ptr, stream_ptr) -> int:
+    return lib().sage_fp4_attn_fwd_kv16(qc, qs, kv16_ptr, kv16_bytes, B, H, N, D, int(causal), float(sm_scale),
+                                        out_ptr, out_dtype, lse_ptr, stream_ptr)
 
 
 def sage_fp4_attn_bwd_workspace_bytes(B, H, N, D) -> int:
@@ -264,6 +284,47 @@ def attn_fwd(fmt, q, k, v, shape, causal=False, sm_scale=0.0, out_dtype=None, st
     dt = torch.float32 if out_dtype is None else out_dtype
     out = torch.empty(shape, dtype=dt, device=q[0].device)
     return attn_fwd_into(fmt, q, k, v, shape, out, causal, sm_scale, stream, direct_p)
+
+
+def kv16_prep(k, v, shape, kv16=None, stream=None):
+    """k, v: NVFP4 (codes, scales) pairs from quant(); returns the uint8 buffer (allocated unless
+    `kv16` is given) holding K-hat and V-hat in fp16, as sage_fp4_kv16_prep writes it."""
+    import torch
+    B, H, N, D = shape
+    dev = k[0].device if isinstance(k, (tuple, list)) and len(k) == 2 else None
+    for pair, role, name in ((k, ROLE_K, "k"), (v, ROLE_V, "v")):
+        _check_codes(pair, role, NVFP4, shape, dev, name)
+    need = sage_fp4_kv16_bytes(B, H, N, D)
+    if kv16 is None:
+        kv16 = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(kv16, torch.uint8, "kv16", dev, min_numel=need)
+    ptrs = [C.c_void_p(t.data_ptr()) for pair in (k, v) for t in pair]
+    rc = sage_fp4_kv16_prep(*ptrs, B, H, N, D, C.c_void_p(kv16.data_ptr()), kv16.numel(), _stream_ptr(stream))
+    if rc != 0:
+        raise SageError(rc, "sage_fp4_kv16_prep")
+    return kv16
+
+
+def attn_fwd_kv16_into(q, kv16, shape, out, causal=False, sm_scale=0.0, stream=None, lse=None):
+    """q: NVFP4 (codes, scales) pair; kv16: the buffer from kv16_prep; out [B,H,N,D] fp16 or fp32;
+    lse: None or float32 with B*H*N elements. Calls sage_fp4_attn_fwd_kv16."""
+    import torch
+    B, H, N, D = shape
+    od = _out_code(out)
+    dev = q[0].device if isinstance(q, (tuple, list)) and len(q) == 2 else None
+    _check_codes(q, ROLE_Q, NVFP4, shape, dev, "q")
+    _check(kv16, torch.uint8, "kv16", dev, min_numel=sage_fp4_kv16_bytes(B, H, N, D))
+    _check(out, out.dtype, "out", dev, numel=B * H * N * D)
+    lse_ptr = None
+    if lse is not None:
+        _check(lse, torch.float32, "lse", dev, numel=B * H * N)
+        lse_ptr = C.c_void_p(lse.data_ptr())
+    rc = sage_fp4_attn_fwd_kv16(C.c_void_p(q[0].data_ptr()), C.c_void_p(q[1].data_ptr()),
+                                C.c_void_p(kv16.data_ptr()), kv16.numel(), B, H, N, D, causal, sm_scale,
+                                C.c_void_p(out.data_ptr()), od, lse_ptr, _stream_ptr(stream))
+    if rc != 0:
+        raise SageError(rc, "sage_fp4_attn_fwd_kv16")
+    return out
 
 
 def alloc_bwd_workspace(B, H, N, D, device="cuda"):

@@ -12,8 +12,11 @@ hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* 
 hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
 // lse: NULL, or [B*H*N] fp32 that receives each row's log-sum-exp
+// kv16: ptrs[2] and ptrs[4] are K-hat and V-hat in fp16 (sage_fp4_kv16_prep's layout)
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, float* lse, hipStream_t st);
+                             void* out, bool out_f32, float* lse, bool kv16, hipStream_t st);
+hipError_t launch_kv16_prep(const void* kc, const void* ks, const void* vc, const void* vs, int BH, int N, int D,
+                            void* kv16, hipStream_t st);
 hipError_t launch_attn_mxfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
                              void* out, bool out_f32, float* lse, hipStream_t st);
 hipError_t launch_attn_mxfp4_direct_p(const void* const* ptrs, int BH, int N, int D, bool causal,
@@ -116,7 +119,7 @@ static int attn_any(int fmt, bool direct_p, const void* const* ptrs, int B, int 
   const bool f32 = out_dtype == SAGE_OUT_F32, cz = causal != 0;
   const int BH = B * H;
   const hipError_t e = direct_p                  ? sage::launch_attn_mxfp4_direct_p(ptrs, BH, N, D, cz, c, out, f32, lse, st)
-                       : fmt == SAGE_FMT_NVFP4   ? sage::launch_attn_nvfp4(ptrs, BH, N, D, cz, c, out, f32, lse, st)
+                       : fmt == SAGE_FMT_NVFP4   ? sage::launch_attn_nvfp4(ptrs, BH, N, D, cz, c, out, f32, lse, false, st)
                        : fmt == SAGE_FMT_MXFP4   ? sage::launch_attn_mxfp4(ptrs, BH, N, D, cz, c, out, f32, lse, st)
                                                  : sage::launch_attn_mx4_pv8(ptrs, BH, N, D, cz, c, out, f32, lse, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
@@ -152,6 +155,45 @@ int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void
   if (!lse) return SAGE_ERR_NULL;
   if (!aligned16(lse)) return SAGE_ERR_ALIGN;
   return attn_any(fmt, direct_p != 0, ptrs, B, H, N, D, causal, sm_scale, out, out_dtype, lse, stream);
+}
+
+size_t sage_fp4_kv16_bytes(int B, int H, int N, int D) {
+  if (check_shape(B, H, N, D) != SAGE_OK) return 0;
+  return (size_t)4 * B * H * padded(N) * D;
+}
+
+int sage_fp4_kv16_prep(const void* k_codes, const void* k_scales, const void* v_codes, const void* v_scales, int B,
+                       int H, int N, int D, void* kv16, size_t kv16_bytes, void* stream) {
+  const void* ptrs[5] = {k_codes, k_scales, v_codes, v_scales, kv16};
+  for (int i = 0; i < 5; ++i)
+    if (!ptrs[i]) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  for (int i = 0; i < 5; ++i)
+    if (!aligned16(ptrs[i])) return SAGE_ERR_ALIGN;
+  if (kv16_bytes < sage_fp4_kv16_bytes(B, H, N, D)) return SAGE_ERR_WORKSPACE;
+  const hipError_t e = sage::launch_kv16_prep(k_codes, k_scales, v_codes, v_scales, B * H, N, D, kv16,
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_fp4_attn_fwd_kv16(const void* q_codes, const void* q_scales, const void* kv16, size_t kv16_bytes, int B,
+                           int H, int N, int D, int causal, float sm_scale, void* out, int out_dtype, float* lse,
+                           void* stream) {
+  if (out_dtype != SAGE_OUT_F16 && out_dtype != SAGE_OUT_F32) return SAGE_ERR_ENUM;
+  if (!q_codes || !q_scales || !kv16 || !out) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(kv16) || !aligned16(out) || !aligned16(lse))
+    return SAGE_ERR_ALIGN;
+  if (kv16_bytes < sage_fp4_kv16_bytes(B, H, N, D)) return SAGE_ERR_WORKSPACE;
+  const uint8_t* kh = static_cast<const uint8_t*>(kv16);
+  const uint8_t* vh = kh + (size_t)2 * B * H * padded(N) * D;
+  const void* ptrs[6] = {q_codes, q_scales, kh, nullptr, vh, nullptr};
+  const hipError_t e =
+      sage::launch_attn_nvfp4(ptrs, B * H, N, D, causal != 0, scale_or_default(sm_scale, D), out,
+                              out_dtype == SAGE_OUT_F32, lse, true, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
 size_t sage_fp4_attn_bwd_workspace_bytes(int B, int H, int N, int D) {

@@ -30,6 +30,11 @@
 //     weight relative to the running maximum is below 2^-64 (its maximum more than 64 below it
 //     in log2 units) is dropped for that row.
 //   - workgroups are ordered so that each XCD walks through whole heads (K/V stay in its L2).
+//   - KV16 instance: K-hat and V-hat come already dequantised to fp16 (kv16_prep_kernel, once per
+//     tensor instead of once per query tile) and are copied straight into the swizzled LDS tiles
+//     by buffer loads into LDS (no staging registers, no dequantisation in the loop): K tile
+//     kt + 1 is copied during the PV products of tile kt, V tile kt during its QK products and
+//     softmax. Same arithmetic, same results bit for bit.
 #include "device.h"
 
 namespace sage {
@@ -52,6 +57,13 @@ __device__ __forceinline__ void scales4(unsigned sw, _Float16* h) {
   const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
   const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw >> 16, 1.0f, false);
   h[0] = lo[0]; h[1] = lo[1]; h[2] = hi[0]; h[3] = hi[1];
+}
+
+// Asynchronous copy of 16 bytes per lane into LDS through a buffer resource based at `base`
+// (wave-uniform): lane i reads base + voff and writes lds + 16 i; vmcnt counts completion.
+__device__ __forceinline__ void lds_copy16(const void* base, unsigned voff, void* lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ unsigned pack_fp4_8(const float* q) {
@@ -147,7 +159,9 @@ __device__ __forceinline__ void softmax_tile(v4f* S, float k2, RowState<D>& st, 
   for (int dt = 0; dt < D / 16; ++dt) st.O[dt] *= factor;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// KV16: kc is K-hat fp16 [BH][Np][D] and vc V-hat fp16 [BH][Np/128][D][128] (slot order), both
+// zero past N; ks and vs are unused.
+template <int D, bool CAUSAL, bool OUT_F32, bool KV16>
 __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
@@ -248,24 +262,62 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     else vsr = *reinterpret_cast<const unsigned short*>(vsp);
   };
 
+  // KV16 copies: job j of a wave fills bytes [1024 j, +1024) of the K-hat (V-hat) LDS tile, lane l
+  // the 16 bytes at 1024 j + 16 l, i.e. one swizzled slot of one row, whose source is the row's
+  // logical chunk (slot XOR the row's swizzle). The wave's share of a tile is JOBS copies; the row
+  // part of a source offset is uniform, the rest depends on the job only through j mod 4.
+  constexpr int JOBS = KV_TILE * D * 2 / 1024 / NV_WAVES;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known to be uniform
+  const uint8_t* kh_h = kc + bh * Np * (2 * D);
+  const uint8_t* vh_h = vc + bh * Np * (2 * D);
+  unsigned koff[4], voff[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    koff[m] = D == 128 ? 256 * (lane >> 4) + 16 * ((lane & 15) ^ (4 * m + (lane >> 4)))
+                       : 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+    voff[m] = 256 * (lane >> 4) + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | m));
+  }
+  auto copyK = [&](int kt) {
+    const uint8_t* base = kh_h + (int64_t)kt * (KV_TILE * D * 2);
+#pragma unroll
+    for (int i = 0; i < JOBS; ++i) {
+      const int j = wu * JOBS + i;
+      lds_copy16(base + 1024 * j, koff[i & 3], reinterpret_cast<uint8_t*>(sK) + 1024 * j);
+    }
+  };
+  auto copyV = [&](int kt) {
+    const uint8_t* base = vh_h + (int64_t)kt * (KV_TILE * D * 2);
+#pragma unroll
+    for (int i = 0; i < JOBS; ++i) {
+      const int j = wu * JOBS + i;
+      lds_copy16(base + 1024 * j, voff[i & 3], reinterpret_cast<uint8_t*>(sV) + 1024 * j);
+    }
+  };
+
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + NV_BQ - 1) / KV_TILE + 1) : ntiles;
-  prefetch(0);
+  if constexpr (KV16) copyK(0);
+  else prefetch(0);
   for (int kt = 0; kt < kt_end; ++kt) {
-    __syncthreads();  // the previous tile's LDS reads are complete
-    {
-      _Float16 kh[4], vh[4];
-      scales4(ksr, kh);
-      scales4(vsr, vh);
+    if constexpr (KV16) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of K tile kt have landed
+      __syncthreads();                // every wave's have, and every wave is done with V tile kt - 1
+      copyV(kt);
+    } else {
+      __syncthreads();  // the previous tile's LDS reads are complete
+      {
+        _Float16 kh[4], vh[4];
+        scales4(ksr, kh);
+        scales4(vsr, vh);
 #pragma unroll
-      for (int u = 0; u < CW; ++u) {
-        *reinterpret_cast<v8h*>(sK + lds_k<D>(kkey, CW * kpart + u)) = dequant8(kr[u], v2h{kh[u >> 1], kh[u >> 1]});
-        *reinterpret_cast<v8h*>(sV + lds_v(vd, CW * vpart + u)) = dequant8(vr[u], v2h{vh[u >> 1], vh[u >> 1]});
+        for (int u = 0; u < CW; ++u) {
+          *reinterpret_cast<v8h*>(sK + lds_k<D>(kkey, CW * kpart + u)) = dequant8(kr[u], v2h{kh[u >> 1], kh[u >> 1]});
+          *reinterpret_cast<v8h*>(sV + lds_v(vd, CW * vpart + u)) = dequant8(vr[u], v2h{vh[u >> 1], vh[u >> 1]});
+        }
       }
+      __syncthreads();
+      if (kt + 1 < kt_end) prefetch(kt + 1);
     }
-    __syncthreads();
-    if (kt + 1 < kt_end) prefetch(kt + 1);
-
     // ---- S^T = K-hat Q-hat^T for both groups: subtile t covers keys 16t..16t+15. Operand
     // reads run two MFMA pairs ahead through a ring of three fragments.
     v4f S[2][8];
@@ -303,6 +355,13 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
     v8h Pf[2][4];
     softmax_tile<D>(S[0], k2, st[0], Pf[0]);
     softmax_tile<D>(S[1], k2, st[1], Pf[1]);
+    if constexpr (KV16) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of V tile kt have landed
+      __syncthreads();                // every wave's have, and every wave is done with K tile kt
+      // unconditional, so that no branch splits the loop body (which costs registers): the last
+      // tile copies itself again, into a buffer no wave reads any more
+      copyK(min(kt + 1, kt_end - 1));
+    }
 
     // ---- O^T += V-hat^T P-hat^T: MFMA step u covers slots 32g + 8u .. +8 of every lane group
     {
@@ -322,6 +381,8 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
       }
     }
   }
+
+  if constexpr (KV16) __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the loop
 
   // ---- epilogue: O / (2688 l); lane (g, c) holds channels 16dt + 4g + i of its query in each
   // group. lse (when given): the row's log-sum-exp of the scaled scores, ln(2^R * l)
@@ -348,26 +409,79 @@ __global__ __launch_bounds__(256, 2) void attn_nvfp4_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool F32>
+template <int D, bool CAUSAL, bool F32, bool KV16>
 static void launch_nv(const void* const* p, int BH, int N, float k2, void* out, float* lse, hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const int nqt = (N + NV_BQ - 1) / NV_BQ;
   const int nwork = nqt * BH;
-  const int cgroup = causal_group(BH, Np * D * 9 / 8);  // K and V: codes + E4M3 scales
-  attn_nvfp4_kernel<D, CAUSAL, F32><<<dim3(nwork), dim3(64 * NV_WAVES), 0, st>>>(
+  // K and V bytes per head: codes + E4M3 scales, or fp16
+  const int cgroup = causal_group(BH, KV16 ? Np * D * 4 : Np * D * 9 / 8);
+  attn_nvfp4_kernel<D, CAUSAL, F32, KV16><<<dim3(nwork), dim3(64 * NV_WAVES), 0, st>>>(
       (const uint8_t*)p[0], (const uint8_t*)p[1], (const uint8_t*)p[2], (const uint8_t*)p[3],
       (const uint8_t*)p[4], (const uint8_t*)p[5], N, Np, nqt, nwork, cgroup, k2, out, lse);
 }
 
+// ptrs: Q codes, Q scales, K codes, K scales, V codes, V scales; with kv16, K-hat and V-hat fp16 in
+// the places of the K and V codes (the scale pointers unused).
 hipError_t launch_attn_nvfp4(const void* const* ptrs, int BH, int N, int D, bool causal, float sm_scale,
-                             void* out, bool out_f32, float* lse, hipStream_t st) {
+                             void* out, bool out_f32, float* lse, bool kv16, hipStream_t st) {
   const float k2 = sm_scale * 1.4426950408889634f;  // scores in log2 units
-#define SAGE_NV_CASE(DD, CC, FF) \
-  if (D == DD && causal == CC && out_f32 == FF) launch_nv<DD, CC, FF>(ptrs, BH, N, k2, out, lse, st);
-  SAGE_NV_CASE(64, false, false) SAGE_NV_CASE(64, false, true) SAGE_NV_CASE(64, true, false)
-  SAGE_NV_CASE(64, true, true) SAGE_NV_CASE(128, false, false) SAGE_NV_CASE(128, false, true)
-  SAGE_NV_CASE(128, true, false) SAGE_NV_CASE(128, true, true)
+#define SAGE_NV_CASE(DD, CC, FF, KK) \
+  if (D == DD && causal == CC && out_f32 == FF && kv16 == KK) launch_nv<DD, CC, FF, KK>(ptrs, BH, N, k2, out, lse, st);
+#define SAGE_NV_CASES(KK)                                                                               \
+  SAGE_NV_CASE(64, false, false, KK) SAGE_NV_CASE(64, false, true, KK) SAGE_NV_CASE(64, true, false, KK) \
+  SAGE_NV_CASE(64, true, true, KK) SAGE_NV_CASE(128, false, false, KK) SAGE_NV_CASE(128, false, true, KK) \
+  SAGE_NV_CASE(128, true, false, KK) SAGE_NV_CASE(128, true, true, KK)
+  SAGE_NV_CASES(false)
+  SAGE_NV_CASES(true)
+#undef SAGE_NV_CASES
 #undef SAGE_NV_CASE
+  return hipGetLastError();
+}
+
+// K-hat fp16 [BH][Np][D] (rows past N zero) and V-hat fp16 [BH][Np/128][D][128] (the V codes'
+// tile-major slot order; padding slots hold zero codes, so zero) from NVFP4 codes and scales.
+// Block (x, bh): items x*256 + tid of head bh; item i < Np*D/8 writes eight K-hat values, the
+// next Np*D/8 items eight V-hat values each. Every value is exact (code times E4M3 scale).
+template <int D>
+__global__ __launch_bounds__(256) void kv16_prep_kernel(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
+                                                        const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
+                                                        int N, int64_t Np, _Float16* __restrict__ kh,
+                                                        _Float16* __restrict__ vh) {
+  const int64_t bh = blockIdx.y, n8 = Np * (D / 8);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n8) return;
+  if (i < n8) {
+    const int64_t j = i / (D / 8);
+    const int d = (int)(i % (D / 8)) * 8;
+    v8h val = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+    if (j < N) {
+      const int64_t r = bh * N + j;
+      const unsigned w = *reinterpret_cast<const unsigned*>(kc + r * (D / 2) + d / 2);
+      const _Float16 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ks[r * (D / 16) + d / 16], 1.0f, false)[0];
+      val = dequant8(w, v2h{sc, sc});
+    }
+    *reinterpret_cast<v8h*>(kh + (bh * Np + j) * D + d) = val;
+  } else {
+    const int64_t e = bh * Np * D + 8 * (i - n8);  // element of [BH][Np/128][D][128]
+    const unsigned w = *reinterpret_cast<const unsigned*>(vc + e / 2);
+    const _Float16 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vs[e / 16], 1.0f, false)[0];
+    *reinterpret_cast<v8h*>(vh + e) = dequant8(w, v2h{sc, sc});
+  }
+}
+
+hipError_t launch_kv16_prep(const void* kc, const void* ks, const void* vc, const void* vs, int BH, int N, int D,
+                            void* kv16, hipStream_t st) {
+  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
+  _Float16* kh = static_cast<_Float16*>(kv16);
+  _Float16* vh = kh + (int64_t)BH * Np * D;
+  const dim3 grid((unsigned)((2 * Np * (D / 8) + 255) / 256), (unsigned)BH);
+  if (D == 64)
+    kv16_prep_kernel<64><<<grid, dim3(256), 0, st>>>((const uint8_t*)kc, (const uint8_t*)ks, (const uint8_t*)vc,
+                                                     (const uint8_t*)vs, N, Np, kh, vh);
+  else
+    kv16_prep_kernel<128><<<grid, dim3(256), 0, st>>>((const uint8_t*)kc, (const uint8_t*)ks, (const uint8_t*)vc,
+                                                      (const uint8_t*)vs, N, Np, kh, vh);
   return hipGetLastError();
 }
 

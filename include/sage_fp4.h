@@ -94,10 +94,11 @@ size_t sage_fp4_scales_bytes(int role, int fmt, int B, int H, int N, int D);
 /* Quantise one fp16 tensor x [B,H,N,D] (dense, row-major) for its role in the attention.
  * Q and K: blocks of 16 (32) consecutive channels of each token; codes [B,H,N,D/2] with
  * element 2i in the low nibble of byte i; scales one byte per block.
- * V: blocks along tokens. codes [B,H,D,Np/2] hold, for each channel d, the tokens of each
- * 128-token tile in slot order (two per byte, low nibble first; MX4_PV8: one byte each);
- * token positions >= N hold 0. With MX4_PV8, Q and K are quantised exactly as with MXFP4.
- * scales [B,H,D,Np/blk]. One kernel launch. Inputs must be finite. */
+ * V: blocks along tokens. codes [B,H,Np/128,D,64] hold, for each 128-token tile and channel d,
+ * the tile's tokens in slot order (two per byte, low nibble first; MX4_PV8: [B,H,Np/128,D,128],
+ * one byte each); token positions >= N hold 0. scales [B,H,Np/128,D,128/blk], one per block
+ * of consecutive slots. With MX4_PV8, Q and K are quantised exactly as with MXFP4.
+ * One kernel launch. Inputs must be finite. */
 int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D,
                    void* codes, void* scales, void* stream);
 
@@ -144,6 +145,42 @@ int sage_fp4_attn_fwd_lse(int fmt, int direct_p, const void* q_codes, const void
                           const void* v_codes, const void* v_scales,
                           int B, int H, int N, int D, int causal, float sm_scale,
                           void* out, int out_dtype, float* lse, void* stream);
+
+/* Bytes of the buffer sage_fp4_kv16_prep fills (0 for invalid arguments): 4*B*H*Np*D,
+ * Np = ceil(N/128)*128. */
+size_t sage_fp4_kv16_bytes(int B, int H, int N, int D);
+
+/* NVFP4 K and V dequantised once, exactly, to fp16 (the DeepTech article, section on FP4
+ * inference and its hardware implementation, for the operands; every value is a code times its
+ * E4M3 block scale, at most 6 significant bits in 2^-10 .. 2688, so fp16 holds it exactly).
+ * The attention kernel otherwise dequantises each K and V tile in every query tile that reads
+ * it; sage_fp4_attn_fwd_kv16 reads this buffer instead, and one buffer serves any number of
+ * attention calls over the same K and V.
+ *   k_codes, k_scales, v_codes, v_scales   NVFP4, as from sage_fp4_quant(SAGE_FMT_NVFP4).
+ *   kv16   device buffer of at least sage_fp4_kv16_bytes(B,H,N,D) bytes, caller-owned; it
+ *          receives K-hat fp16 [B,H,Np,D] (rows >= N zero) followed by V-hat fp16
+ *          [B,H,Np/128,D,128] (the V codes' tile-major slot order; positions >= N zero).
+ *          A smaller kv16_bytes is SAGE_ERR_WORKSPACE.
+ * Validation and errors as for sage_fp4_quant. One kernel launch. */
+int sage_fp4_kv16_prep(const void* k_codes, const void* k_scales,
+                       const void* v_codes, const void* v_scales,
+                       int B, int H, int N, int D, void* kv16, size_t kv16_bytes, void* stream);
+
+/* NVFP4 attention forward with K and V from sage_fp4_kv16_prep's buffer: the same operation,
+ * tiles and arithmetic as sage_fp4_attn_fwd(SAGE_FMT_NVFP4, ...) on the codes kv16 was made from,
+ * and the same output bit for bit (and lse as sage_fp4_attn_fwd_lse). It reads 2 bytes per K and
+ * V element instead of 0.56, so it pays where the dequantisation it saves outweighs that:
+ * long sequences, or one kv16 buffer reused by several calls.
+ *   q_codes, q_scales   NVFP4, as from sage_fp4_quant(SAGE_ROLE_Q, SAGE_FMT_NVFP4).
+ *   kv16                the buffer, kv16_bytes >= sage_fp4_kv16_bytes(B,H,N,D), else
+ *                       SAGE_ERR_WORKSPACE.
+ *   lse                 NULL, or fp32 [B,H,N] (16-byte aligned) receiving each row's
+ *                       log-sum-exp as in sage_fp4_attn_fwd_lse.
+ * Other arguments, validation and errors as for sage_fp4_attn_fwd. One kernel launch. */
+int sage_fp4_attn_fwd_kv16(const void* q_codes, const void* q_scales,
+                           const void* kv16, size_t kv16_bytes,
+                           int B, int H, int N, int D, int causal, float sm_scale,
+                           void* out, int out_dtype, float* lse, void* stream);
 
 /* Bytes of device workspace sage_fp4_attn_bwd needs for this shape (0 for invalid arguments).
  * About 4*B*H*N*D + 3*B*H*D*Np64 bytes, Np64 = ceil(N/64)*64. */

@@ -93,6 +93,20 @@ int main(void) {
     CHECK(sage_fp4_attn_bwd(SAGE_FMT_NVFP4, fake, fake, fake, fake, fake, fake, fake, (const float*)fake, 1, 1, 16,
                             80, 0, 0.0f, fake, fake, fake, SAGE_OUT_F32, fake, need, NULL) == SAGE_ERR_HEAD_DIM);
   }
+  /* dequantised K/V: buffer size (Np = 384) and validation */
+  {
+    CHECK(sage_fp4_kv16_bytes(2, 3, 300, 128) == (size_t)4 * 2 * 3 * 384 * 128);
+    CHECK(sage_fp4_kv16_bytes(2, 3, 300, 96) == 0);
+    size_t need = sage_fp4_kv16_bytes(1, 1, 16, 64);
+    CHECK(sage_fp4_kv16_prep(fake, fake, fake, fake, 1, 1, 16, 64, fake, need - 1, NULL) == SAGE_ERR_WORKSPACE);
+    CHECK(sage_fp4_kv16_prep(fake, fake, fake, NULL, 1, 1, 16, 64, fake, need, NULL) == SAGE_ERR_NULL);
+    CHECK(sage_fp4_kv16_prep(fake, fake, fake, fake, 1, 1, 16, 64, mis, need, NULL) == SAGE_ERR_ALIGN);
+    CHECK(sage_fp4_attn_fwd_kv16(fake, fake, fake, need - 1, 1, 1, 16, 64, 0, 0.0f, fake, SAGE_OUT_F32, NULL, NULL) ==
+          SAGE_ERR_WORKSPACE);
+    CHECK(sage_fp4_attn_fwd_kv16(fake, fake, fake, need, 1, 1, 16, 64, 0, 0.0f, fake, 3, NULL, NULL) == SAGE_ERR_ENUM);
+    CHECK(sage_fp4_attn_fwd_kv16(fake, fake, fake, need, 1, 1, 16, 64, 0, 0.0f, fake, SAGE_OUT_F16, (float*)mis,
+                                 NULL) == SAGE_ERR_ALIGN);
+  }
   for (s = -7; s <= 0; ++s) CHECK(sage_fp4_status_string(s) != NULL && strlen(sage_fp4_status_string(s)) > 0);
   CHECK(strcmp(sage_fp4_status_string(SAGE_ERR_WORKSPACE), "unknown status") != 0);
   CHECK(strcmp(sage_fp4_status_string(SAGE_OK), "ok") == 0);

@@ -155,3 +155,37 @@ def test_bwd_workspace_and_validation():
     assert st(-1, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, FAKE, FAKE, 1, FAKE, need, None) == -5
     assert st(1, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, FAKE, FAKE, 1, FAKE, need - 1, None) == -7
     assert st(2, 0, *ok, 1, 1, 16, 64, 0, 0.0, FAKE, None, FAKE, 1, FAKE, need, None) == -1
+
+
+def test_kv16_bytes_and_validation():
+    """Dequantised-K/V entry points: documented buffer size, and every argument check (no launch)."""
+    assert bnd.sage_fp4_kv16_bytes(2, 3, 300, 128) == 4 * 2 * 3 * 384 * 128
+    assert bnd.sage_fp4_kv16_bytes(1, 1, 1, 64) == 4 * 128 * 64
+    assert bnd.sage_fp4_kv16_bytes(2, 3, 300, 96) == 0
+    assert bnd.sage_fp4_kv16_bytes(1, 1024, 1 << 20, 64) == 0
+    need = bnd.sage_fp4_kv16_bytes(1, 1, 16, 64)
+    p = bnd.sage_fp4_kv16_prep
+    ok = [FAKE] * 4
+    assert p(*ok, 1, 1, 16, 64, FAKE, need - 1, None) == -7
+    assert p(*ok, 1, 1, 16, 64, None, need, None) == -1
+    assert p(*ok[:3], None, 1, 1, 16, 64, FAKE, need, None) == -1
+    assert p(*ok[:2], MIS, ok[3], 1, 1, 16, 64, FAKE, need, None) == -4
+    assert p(*ok, 1, 1, 16, 64, MIS, need, None) == -4
+    assert p(*ok, 1, 1, 16, 96, FAKE, need, None) == -3
+    assert p(*ok, 1, 1, 0, 64, FAKE, need, None) == -2
+    a = bnd.sage_fp4_attn_fwd_kv16
+
+    def call(qc=FAKE, qs=FAKE, kv=FAKE, kvb=need, D=64, N=16, out=FAKE, od=1, lse=None):
+        return a(qc, qs, kv, kvb, 1, 1, N, D, 0, 0.0, out, od, lse, None)
+
+    assert call(kvb=need - 1) == -7
+    assert call(kv=None) == -1
+    assert call(qs=None) == -1
+    assert call(out=None) == -1
+    assert call(od=2) == -5
+    assert call(D=96) == -3
+    assert call(N=0) == -2
+    assert call(qc=MIS) == -4
+    assert call(out=MIS) == -4
+    assert call(lse=MIS) == -4
+    assert call(kv=MIS) == -4
