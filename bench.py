@@ -231,6 +231,8 @@ def main():
                     help="time the attention alone over the N sweep (B4 H32 D128, N 1024..16384) and "
                          "workloads 3 and 4, every format and mask; one JSON line per entry appended "
                          "to PATH, entries already in PATH skipped (the sweep resumes)")
+    ap.add_argument("--sweep-formats", default=",".join(f for f, _, _ in SWEEP_FORMATS),
+                    help="comma-separated subset of the sweep's formats (default: all)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -244,7 +246,12 @@ def main():
     from bit_attention_amd import synth
 
     if args.sweep:
-        return run_sweep(args.sweep, torch, bnd, synth)
+        fmts = [f for f in args.sweep_formats.split(",") if f]
+        unknown = sorted(set(fmts) - {f for f, _, _ in SWEEP_FORMATS})
+        if unknown:
+            print(f"bench.py: unknown sweep formats {unknown}", file=sys.stderr)
+            sys.exit(2)
+        return run_sweep(args.sweep, torch, bnd, synth, fmts)
     fmt = {"nvfp4": bnd.NVFP4, "mxfp4": bnd.MXFP4, "mx4_pv8": bnd.MX4_PV8}[args.fmt]
     if args.direct_p and fmt != bnd.MXFP4:
         print("bench.py: --direct-p needs --fmt mxfp4", file=sys.stderr)
@@ -491,13 +498,15 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-SWEEP_FORMATS = (("nvfp4", 0, False), ("mxfp4", 1, False), ("mxfp4_direct_p", 1, True), ("mx4_pv8", 2, False))
+SWEEP_FORMATS = (("nvfp4", 0, False), ("nvfp4_kv16", 0, False), ("mxfp4", 1, False), ("mxfp4_direct_p", 1, True),
+                 ("mx4_pv8", 2, False))
 
 
-def run_sweep(path, torch, bnd, synth):
+def run_sweep(path, torch, bnd, synth, formats):
     """The attention kernel alone (warmed up, 10 launches timed with HIP events on the launch
     stream) for every (shape, format, mask) entry; each entry is appended to `path` as one JSON
-    line as soon as it is measured, and entries already in `path` are skipped."""
+    line as soon as it is measured, and entries already in `path` are skipped. nvfp4_kv16 entries
+    time sage_fp4_attn_fwd_kv16 and, apart, the sage_fp4_kv16_prep it reads."""
     done = set()
     if os.path.exists(path):
         with open(path) as f:
@@ -515,7 +524,7 @@ def run_sweep(path, torch, bnd, synth):
             shape = (w["B"], w["H"], w["N"], w["D"])
         masks = (True,) if wl == 4 else (False, True)
         todo = [(f, fv, dp, c) for f, fv, dp in SWEEP_FORMATS for c in masks
-                if f"{tag}_{f}_{'causal' if c else 'noncausal'}" not in done]
+                if f in formats and f"{tag}_{f}_{'causal' if c else 'noncausal'}" not in done]
         if not todo:
             continue
         log(f"bench sweep: {tag} {shape}, {len(todo)} entries")
@@ -526,9 +535,22 @@ def run_sweep(path, torch, bnd, synth):
         B, H, N, D = shape
         for f, fv, dp, c in todo:
             Q, K, V = bnd.quant(q, bnd.ROLE_Q, fv), bnd.quant(k, bnd.ROLE_K, fv), bnd.quant(v, bnd.ROLE_V, fv)
-            launch = lambda: bnd.attn_fwd_into(fv, Q, K, V, shape, out, causal=c, direct_p=dp)  # noqa: E731
-            warm(launch, torch)
+            kv16 = prep_ms = None
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if f == "nvfp4_kv16":
+                kv16 = torch.empty(bnd.sage_fp4_kv16_bytes(*shape), dtype=torch.uint8, device=dev)
+                prep = lambda: bnd.kv16_prep(K, V, shape, kv16)  # noqa: E731
+                warm(prep, torch)
+                e0.record(stream)
+                for _ in range(10):
+                    prep()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                prep_ms = e0.elapsed_time(e1) / 10
+                launch = lambda: bnd.attn_fwd_kv16_into(Q, kv16, shape, out, causal=c)  # noqa: E731
+            else:
+                launch = lambda: bnd.attn_fwd_into(fv, Q, K, V, shape, out, causal=c, direct_p=dp)  # noqa: E731
+            warm(launch, torch)
             e0.record(stream)
             for _ in range(10):
                 launch()
@@ -539,10 +561,12 @@ def run_sweep(path, torch, bnd, synth):
             entry = {"key": f"{tag}_{f}_{'causal' if c else 'noncausal'}", "B": B, "H": H, "N": N, "D": D,
                      "format": f, "causal": c, "attn_kernel_ms": ms, "attn_tops": fl / (ms * 1e-3) / 1e12,
                      "frac_fp4_peak": fl / (ms * 1e-3) / 1e12 / FP4_PEAK_TOPS}
+            if prep_ms is not None:
+                entry["kv16_prep_ms"] = prep_ms
             with open(path, "a") as fh:
                 fh.write(json.dumps(entry) + "\n")
             log(f"bench sweep: {entry['key']} {ms:.4f} ms {entry['attn_tops']:.0f} TOPS")
-            del Q, K, V
+            del Q, K, V, kv16
         del q, k, v, out
         torch.cuda.empty_cache()
     print(json.dumps({"sweep": path, "entries_skipped": len(done)}), flush=True)
