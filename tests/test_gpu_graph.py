@@ -1,7 +1,8 @@
 """The entry points inside a HIP graph: one step (three sage_fp4_quant launches and one attention
-launch, and in the training form also the backward's five launches) captured with
-torch.cuda.CUDAGraph and replayed several times, with eager work and synchronisations between the
-replays that change the inputs, must give exactly the eager results every time. The library
+launch; with the kv16 path also sage_fp4_kv16_prep; in the training form also the backward's five
+launches) captured with torch.cuda.CUDAGraph and replayed several times, with eager work and
+synchronisations between the replays that change the inputs, must give exactly the eager results
+every time. The library
 allocates nothing, synchronises nothing and issues no memset, so each launch is one kernel node."""
 import numpy as np
 import pytest
@@ -52,6 +53,53 @@ def test_graph_replays_match_eager(fmt, direct_p, causal):
         step()  # eager, same inputs
         torch.cuda.synchronize()
         say(f"  replay {r}: fmt={fmt} dp={direct_p} causal={causal}")
+        assert torch.equal(got_out, out), f"replay {r}: output differs from eager"
+        assert torch.equal(got_lse, lse), f"replay {r}: lse differs from eager"
+        assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_graph_kv16_replays_match_eager(causal):
+    """Three quantisations, sage_fp4_kv16_prep and sage_fp4_attn_fwd_kv16 (with lse) captured as
+    one graph: every replay, with new inputs written between replays, equals the eager run."""
+    B, H, N, D = 2, 3, 500, 64
+    shape = (B, H, N, D)
+    fmt = bnd.NVFP4
+    g = torch.Generator(device="cuda").manual_seed(13)
+    q, k, v = (torch.randn(shape, generator=g, device="cuda").half() for _ in range(3))
+    Q, K, V = (bnd.alloc_quant(r, fmt, *shape) for r in (bnd.ROLE_Q, bnd.ROLE_K, bnd.ROLE_V))
+    kv = torch.empty(bnd.sage_fp4_kv16_bytes(*shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B * H * N, dtype=torch.float32, device="cuda")
+
+    def step():
+        bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
+        bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
+        bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
+        bnd.kv16_prep(K, V, shape, kv)
+        bnd.attn_fwd_kv16_into(Q, kv, shape, out, causal=causal, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for x in (q, k, v):
+            x.copy_(torch.randn(shape, generator=g, device="cuda").half())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_out, got_lse = out.clone(), lse.clone()
+        out.fill_(float("nan")); lse.fill_(float("nan")); kv.fill_(0x7B)
+        step()
+        torch.cuda.synchronize()
+        say(f"  kv16 replay {r}: causal={causal}")
         assert torch.equal(got_out, out), f"replay {r}: output differs from eager"
         assert torch.equal(got_lse, lse), f"replay {r}: lse differs from eager"
         assert bool(torch.isfinite(out).all())

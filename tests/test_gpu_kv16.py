@@ -8,6 +8,7 @@ sage_fp4_attn_fwd_kv16) through the C ABI.
   workload sizes bench.py times.
 - Against the oracle directly, every row of small shapes within 2e-3 (the bar of
   tests/test_gpu_attn.py; the slack is reported, not added).
+- Equal to the codes path at the C ABI's limits too: N = 2^20, and B*H = 65535.
 - A buffer smaller than sage_fp4_kv16_bytes is refused before any launch."""
 import numpy as np
 import pytest
@@ -150,3 +151,16 @@ def test_small_buffer_refused_before_launch():
                                       C.c_void_p(out.data_ptr()), 1, None, None) == -7
     torch.cuda.synchronize()
     assert bool((kv == 0x7B).all()) and bool((out == 5.0).all()), "nothing may be written"
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1 << 20, 64), (1, 65535, 1, 128)])
+def test_limits_equal_to_codes_path(shape):
+    """The longest sequence and the most heads the C ABI accepts (the prep's largest grids in x and
+    in y): equal to the codes path, which tests/test_gpu_limits.py checks against the oracle."""
+    rng = np.random.default_rng(990)
+    q, k, v = (rng.standard_normal(shape).astype(np.float16) for _ in range(3))
+    Q, K, V = _quant_all(q, k, v)
+    for causal in ((False, True) if shape[2] > 1 else (False,)):
+        say(f"kv16 limits shape={shape} causal={causal}")
+        a, b = _both(Q, K, V, shape, causal)
+        _bit_equal(a, b, f"limits {shape} causal {causal}")
