@@ -12,11 +12,11 @@
 // At most 128 VGPRs, so four waves share a SIMD. The softmax's VALU work dominates the time:
 // on gfx950 MFMA and plain VALU instructions do not overlap (measured), so what counts is the
 // number of VALU instructions per score, which the layout keeps at about six. Workgroups are
-// ordered so that each XCD walks through whole heads. The next tile's codes and scales are
-// loaded into registers while the current tile is computed (after its QK products, or after its
-// softmax for plain MXFP4 at D = 128), so the global loads overlap the rest of the tile and the
-// barrier. Scale bytes sit in LDS so that a lane reads its eight
-// K (or V) scales of a tile as one 8-byte word; the instruction's op_sel bits pick the byte.
+// ordered so that each XCD walks through whole heads. The next tile's codes stream straight into
+// a second set of LDS buffers (buffer loads into LDS) during the whole current tile, with one
+// barrier per tile; its scale bytes come through registers. Scale bytes sit in LDS so that a
+// lane reads its eight K (or V) scales of a tile as one 8-byte word; the instruction's op_sel
+// bits pick the byte.
 // Instances: plain MXFP4, Direct-P (normaliser from the rounded P) and FP8-PV (P, V in MXFP8).
 // P has no first level (E8M0 scales cover its range): its codes are E = 2^(x - t) quantised with
 // the lane-local block's power-of-two scale.
@@ -87,6 +87,19 @@ __host__ __device__ constexpr int pv8_rho(int key) {
   return (key & 0x33) | (((key >> 3) & 1) << 6) | (((key >> 2) & 1) << 3) | (((key >> 6) & 1) << 2);
 }
 
+// inverse of pv8_rho: rho moves key bit 6 to 2, 2 to 3 and 3 to 6
+__host__ __device__ constexpr int pv8_rho_inv(int row) {
+  return (row & 0x33) | (((row >> 2) & 1) << 6) | (((row >> 3) & 1) << 2) | (((row >> 6) & 1) << 3);
+}
+
+// Asynchronous copy of 16 bytes per lane into LDS through a buffer resource of `nbytes` bytes
+// at `base` (wave-uniform): lane i reads base + voff, or 0 where voff >= nbytes, and writes
+// lds + 16 i; vmcnt counts completion.
+__device__ __forceinline__ void lds_copy16(const void* base, unsigned nbytes, unsigned voff, void* lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 // The lane's partner value after a permlane swap of `mine` (the pair holds both, in an order
 // that depends on the lane; equal values make either choice right).
 __device__ __forceinline__ unsigned partner_of(unsigned mine, unsigned p0, unsigned p1) {
@@ -100,19 +113,28 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     float* __restrict__ lse) {
   static_assert(!(PV8 && DIRECT_P), "Direct-P is defined for MXFP4 P");
   constexpr int MX_NT = 64 * mx_waves<D>(), MX_BQ = 16 * mx_waves<D>();
-  constexpr int KROW = D / 2 + 16;        // K code row pitch (bytes)
+  constexpr int NW = mx_waves<D>();       // waves per workgroup
   constexpr int VB = PV8 ? 128 : 64;      // V code bytes per channel and tile (128 slots)
-  constexpr int VROW = VB + 16;           // V code row pitch (bytes)
-  constexpr int VPIECES = D * VB / 16;    // 16-byte pieces of a V tile
-  constexpr int VPT = (VPIECES + MX_NT - 1) / MX_NT;  // pieces per thread
-  constexpr int NBD = D / 32;             // MXFP4 blocks along D
-  __shared__ __attribute__((aligned(16))) uint8_t sKc[KV_TILE * KROW];
+  constexpr int NBD = D / 32;             // MXFP4 blocks along D (16-byte chunks per K row)
+  // LDS tiles of the codes: dense rows (K: D/2 bytes per key, V: VB bytes per channel), so that
+  // one copy instruction of a wave fills 1 KB; chunk q of row r sits at slot q ^ swz(r), so that
+  // the 16 rows a lane group reads hit distinct bank groups. Two sets of buffers: tile kt is read
+  // from set kt mod 2 while tile kt + 1 streams into the other.
+  constexpr int KT_BYTES = KV_TILE * (D / 2), VT_BYTES = D * VB;
+  static_assert(KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "whole 1 KB copies");
+  __shared__ __attribute__((aligned(16))) uint8_t sKc0[KT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sKc1[KT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sVc0[VT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sVc1[VT_BYTES];
   // scale bytes, laid out so that lane (g, c) finds its eight per tile in one 8-byte word:
   // K: byte (4c + g) * 8 + t holds key 16t + c's block g; V: byte (4c + g) * 8 + dt holds
   // channel 16dt + c's block g (dt < D/16)
-  __shared__ __attribute__((aligned(16))) uint8_t sKs[KV_TILE * 4];
-  __shared__ __attribute__((aligned(16))) uint8_t sVc[D * VROW];
-  __shared__ __attribute__((aligned(16))) uint8_t sVs[16 * 4 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t sKs0[KV_TILE * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sKs1[KV_TILE * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sVs0[16 * 4 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t sVs1[16 * 4 * 8];
+  auto kswz = [](int r) { return D == 128 ? (r >> 1) & 3 : (r >> 2) & 1; };
+  auto vswz = [](int r) { return PV8 ? (r & 7) : (r >> 1) & 3; };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -142,73 +164,68 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
   const int ntiles = (int)(Np / KV_TILE);
   const int kt_end = CAUSAL ? min(ntiles, (q0 + MX_BQ - 1) / KV_TILE + 1) : ntiles;
 
-  // Staging: each thread owns a few 16-byte pieces of the K and V codes and exactly one K and one
-  // V scale byte, so every wave does the same staging work before the barrier. The next tile's
-  // pieces are loaded into registers once the current tile's scores are consumed, so the loads
-  // are in flight during the PV products and the barrier.
-  constexpr int TPK = D / 32;  // 16-byte pieces per key row
-  constexpr int KPIECES = KV_TILE * TPK;
-  constexpr int KPT = (KPIECES + MX_NT - 1) / MX_NT;
-  constexpr int VPR = VB / 16;  // 16-byte pieces per V channel row
+  // Staging: the next tile's codes are copied straight into the other LDS set (buffer loads into
+  // LDS, issued right after the current tile's barrier), so they stream in during the whole
+  // tile; its scale bytes come into registers with them and are written at the top of the next
+  // tile. One barrier per tile: set kt mod 2 was last read in tile kt - 2, before the barrier of
+  // tile kt - 1. Copy job j fills bytes [1024 j, +1024) of a tile; lane l takes the global chunk
+  // that belongs at its slot, so a lane's source offsets are the same from tile to tile. Key rows
+  // past N lie outside the copy's buffer range and read as zero codes (their scores are masked).
   static_assert(MX_NT == KV_TILE * NBD && MX_NT == 4 * D, "one K and one V scale byte per thread and tile");
+  constexpr int KJOBS = KT_BYTES / 1024, VJOBS = VT_BYTES / 1024;
+  constexpr int KPW = (KJOBS + NW - 1) / NW, VPW = (VJOBS + NW - 1) / NW;  // copies per wave
   const uint8_t* kc_h = kc + bh * N * (D / 2);
   const uint8_t* ks_h = ks + bh * N * NBD;
-  const int64_t vrow_bytes = PV8 ? Np : Np / 2;
-  // V codes are stored tile by tile ([Np/128][D][VB]): a tile's codes are one contiguous run of
-  // D*VB bytes, piece e of it channel e/VPR, bytes 16*(e%VPR) of the channel's VB
-  const uint8_t* vc_h = vc + bh * D * vrow_bytes;   // uniform base; per-thread offsets are 32-bit
+  // V codes and scales are stored tile by tile ([Np/128][D][VB] and [Np/128][D][4]): a tile's
+  // codes are one contiguous run of D*VB bytes, its scales one of 4*D bytes, byte tid of which is
+  // channel tid/4, block tid%4
+  const uint8_t* vc_h = vc + bh * D * (PV8 ? Np : Np / 2);
   const uint8_t* vs_h = vs + bh * D * (Np / 32);
-  // V scales are stored tile by tile, [Np/128][D][4]: byte tid of a tile is channel tid/4, block tid%4
-  const unsigned vs_off = (unsigned)tid;
-  uint4 rk[KPT], rv[VPT];
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known to be uniform
+  unsigned koff[KPW], voff[VPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int q = 64 * (NW * i + w) + lane, r = q / NBD, cs = q % NBD;  // LDS row and slot
+    koff[i] = (unsigned)((PV8 ? pv8_rho_inv(r) : r) * (D / 2) + 16 * (cs ^ kswz(r)));
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int q = 64 * (NW * i + w) + lane, r = q / (VB / 16), cs = q % (VB / 16);
+    voff[i] = (unsigned)(r * VB + 16 * (cs ^ vswz(r)));
+  }
   unsigned rks = 0, rvs = 0;
+  auto issue = [&](int kt, uint8_t* sKc, uint8_t* sVc) {
+    const uint8_t* kb = kc_h + (int64_t)kt * KV_TILE * (D / 2);
+    const unsigned kn = (unsigned)(min(N - kt * KV_TILE, KV_TILE) * (D / 2));
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) rk[i] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) rv[i] = make_uint4(0, 0, 0, 0);
-  auto prefetch = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = tid + MX_NT * i, j = kt * KV_TILE + e / TPK;
-      if (e < KPIECES) {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        if (j < N) rk[i] = *reinterpret_cast<const uint4*>(kc_h + (int64_t)j * (D / 2) + 16 * (e % TPK));
-      }
+    for (int i = 0; i < KPW; ++i) {
+      const int job = NW * i + wu;
+      if (job < KJOBS) lds_copy16(kb, kn, koff[i], sKc + 1024 * job);
     }
-    {
-      const int jj = kt * KV_TILE + tid / NBD;  // key of this thread's scale byte (block tid % NBD)
-      rks = jj < N ? ks_h[(int64_t)kt * KV_TILE * NBD + tid] : 0x7Fu;
-    }
+    const uint8_t* vb = vc_h + (int64_t)kt * (VB * D);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = tid + MX_NT * i;
-      if (e < VPIECES)
-        rv[i] = *reinterpret_cast<const uint4*>(vc_h + (unsigned)(16 * e) + (unsigned)kt * (unsigned)(VB * D));
+    for (int i = 0; i < VPW; ++i) {
+      const int job = NW * i + wu;
+      if (job < VJOBS) lds_copy16(vb, (unsigned)(VB * D), voff[i], sVc + 1024 * job);
     }
-    rvs = vs_h[vs_off + (unsigned)kt * (unsigned)(4 * D)];
+    const int jj = kt * KV_TILE + tid / NBD;  // key of this thread's scale byte (block tid % NBD)
+    rks = jj < N ? ks_h[(int64_t)kt * KV_TILE * NBD + tid] : 0x7Fu;
+    rvs = vs_h[(unsigned)tid + (unsigned)kt * (unsigned)(4 * D)];
   };
-  prefetch(0);
-  for (int kt = 0; kt < kt_end; ++kt) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = tid + MX_NT * i, key = e / TPK;
-      if (e < KPIECES) *reinterpret_cast<uint4*>(sKc + (PV8 ? pv8_rho(key) : key) * KROW + 16 * (e % TPK)) = rk[i];
-    }
+  // One key tile, from LDS set (sKc, sKs, sVc, sVs), copying the next one into (nKc, nVc). The
+  // sets are __restrict__ parameters: the compiler then knows that the copies and this tile's
+  // reads touch different memory, and puts no wait for the copies before the reads.
+  auto tile = [&](int kt, uint8_t* __restrict__ sKc, uint8_t* __restrict__ sKs, uint8_t* __restrict__ sVc,
+                  uint8_t* __restrict__ sVs, uint8_t* __restrict__ nKc, uint8_t* __restrict__ nVc) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and scale loads of tile kt have landed
     {
       const int r = PV8 ? pv8_rho(tid / NBD) : tid / NBD;  // LDS row of this thread's key
       sKs[((r & 15) * 4 + tid % NBD) * 8 + (r >> 4)] = (uint8_t)rks;
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = tid + MX_NT * i;
-      if (e < VPIECES) *reinterpret_cast<uint4*>(sVc + (e / VPR) * VROW + 16 * (e % VPR)) = rv[i];
-    }
-    {
       const int d = tid >> 2;  // channel d's block tid & 3
       sVs[((d & 15) * 4 + (tid & 3)) * 8 + (d >> 4)] = (uint8_t)rvs;
     }
-    __syncthreads();
+    __syncthreads();  // every wave's copies of tile kt have landed; every wave is done with kt - 1
+    if (kt + 1 < kt_end) issue(kt + 1, nKc, nVc);
 
     // ---- S^T = K Q^T: one scaled FP4 MFMA per 16-key subtile (K dimension 128 >= D)
     v4f S[8];
@@ -218,27 +235,27 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     for (int t = 0; t < 8; ++t) {
       v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
       if (g < NBD) {
-        const uint4 u = *reinterpret_cast<const uint4*>(sKc + (16 * t + c) * KROW + 16 * g);
+        const int r = 16 * t + c;
+        const uint4 u = *reinterpret_cast<const uint4*>(sKc + r * (D / 2) + 16 * (g ^ kswz(r)));
         a[0] = (int)u.x; a[1] = (int)u.y; a[2] = (int)u.z; a[3] = (int)u.w;
       }
       // the scale operand's byte t & 3 is selected by the instruction's op_sel bits
       S[t] = mfma_sel<4>(a, qf, v4f{0, 0, 0, 0}, t & 3, (int)(t < 4 ? ksw.x : ksw.y), qsc);
     }
-    // the next tile's loads: issued here, a softmax ahead of their use, for the Direct-P, FP8-PV
-    // and D = 64 instances (1-3% faster each, measured); after the softmax for plain MXFP4 at
-    // D = 128, where the registers they hold through the softmax cost more than the latency
-    constexpr bool EARLY = DIRECT_P || PV8 || D == 64;
-    if (EARLY && kt + 1 < kt_end) prefetch(kt + 1);
     const int kbase = kt * KV_TILE;
     if (kbase + KV_TILE > N || (CAUSAL && kbase + KV_TILE - 1 > q0)) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = kbase + (PV8 ? 64 * (g & 1) + 16 * (t & 3) + 8 * (t >> 2) + 4 * (g >> 1) + i
                                      : 16 * t + 4 * g + i);
           if (j >= N || (CAUSAL && j > qi)) S[t][i] = -INFINITY;
         }
+        // the masked scores leave the branch as they are (an empty asm that "modifies" them): the
+        // compiler would otherwise move the selects after the branch, into every tile's path
+        asm volatile("" : "+v"(S[t]));
+      }
     }
     // ---- online softmax in log2 units
     // bmx: the maximum of S over the lane's P block (PV8: over the block of its first half,
@@ -327,7 +344,6 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       }
       psc = keep ? X + 127 : 0;
     }
-    if (!EARLY && kt + 1 < kt_end) prefetch(kt + 1);
     if (!accept) esum = 0.0f;
     const float factor = accept ? __builtin_amdgcn_exp2f(R - T) : 1.0f;
     R = accept ? T : R;
@@ -346,12 +362,14 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       if (PV8) {
-        const uint4 u0 = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
-        const uint4 u1 = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 64 + 16 * g);
+        const int r = 16 * dt + c;
+        const uint4 u0 = *reinterpret_cast<const uint4*>(sVc + r * VB + 16 * (g ^ vswz(r)));
+        const uint4 u1 = *reinterpret_cast<const uint4*>(sVc + r * VB + 16 * ((4 + g) ^ vswz(r)));
         const v8i a = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
         O[dt] = mfma_sel<0>(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
       } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(sVc + (16 * dt + c) * VROW + 16 * g);
+        const int r = 16 * dt + c;
+        const uint4 u = *reinterpret_cast<const uint4*>(sVc + r * VB + 16 * (g ^ vswz(r)));
         const v8i a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
         O[dt] = mfma_sel<4>(a, pf, O[dt], dt & 3, (int)(dt < 4 ? vsw.x : vsw.y), psc);
       }
@@ -363,6 +381,12 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
       Lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, Lacc, 4, 4, 0, 127, 0, psc);
     }
+  };
+  issue(0, sKc0, sVc0);
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const bool odd = kt & 1;
+    tile(kt, odd ? sKc1 : sKc0, odd ? sKs1 : sKs0, odd ? sVc1 : sVc0, odd ? sVs1 : sVs0, odd ? sKc0 : sKc1,
+         odd ? sVc0 : sVc1);
   }
 
   const float L = DIRECT_P ? Lacc[0] : xg_sum(l);
