@@ -13,8 +13,9 @@ bounded sample of the same workload.
 `--sweep PATH` times the attention alone over the N sweep and workloads 3 and 4, every format and
 mask, appending one JSON line per entry to PATH and skipping entries already there.
 
-`--kv16` (NVFP4) makes the step quantise, dequantise K and V once to fp16 (sage_fp4_kv16_prep)
-and run sage_fp4_attn_fwd_kv16 on them; the prep is timed apart (`kv16_prep_ms`).
+`--kv16` (NVFP4) makes the step quantise K and V with sage_fp4_quant_kv16, which also writes
+their exact fp16 dequantisation in the same pass, and run sage_fp4_attn_fwd_kv16 on that buffer
+(outputs identical to the default step's, bit for bit).
 
 `--backward` times the 8-bit backward instead (sage_fp4_attn_bwd as its three stages, on the
 forward's FP4 Q/K, output and log-sum-exp): `value` = 10*B*H*N^2*D / (backward time), the
@@ -214,8 +215,8 @@ def main():
                     help="mx4_pv8: MXFP4 Q and K, MXFP8 P and V")
     ap.add_argument("--direct-p", action="store_true", help="time sage_fp4_attn_fwd_direct_p (mxfp4 only)")
     ap.add_argument("--kv16", action="store_true",
-                    help="nvfp4: the step dequantises K and V once (sage_fp4_kv16_prep) and runs "
-                         "sage_fp4_attn_fwd_kv16 on them")
+                    help="nvfp4: the step quantises K and V with sage_fp4_quant_kv16 (codes plus "
+                         "their fp16 dequantisation) and runs sage_fp4_attn_fwd_kv16 on them")
     ap.add_argument("--seq-len", type=int, default=WORKLOAD["N"],
                     help="N of the sweep at B=4 H=32 D=128 (default 4096)")
     ap.add_argument("--workload", type=int, choices=[2, 3, 4], default=2,
@@ -288,7 +289,7 @@ def main():
     stream = torch.cuda.current_stream()
     causal = args.causal
 
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
 
     def attention():
         if args.kv16:
@@ -300,17 +301,17 @@ def main():
         if i is not None:
             ev[i][0].record(stream)
         bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
-        bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
-        bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
+        if args.kv16:
+            bnd.quant_kv16_into(k, bnd.ROLE_K, *K, kv16)
+            bnd.quant_kv16_into(v, bnd.ROLE_V, *V, kv16)
+        else:
+            bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
+            bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
         if i is not None:
             ev[i][1].record(stream)
-        if args.kv16:
-            bnd.kv16_prep(K, V, shape, kv16)
-        if i is not None:
-            ev[i][2].record(stream)
         attention()
         if i is not None:
-            ev[i][3].record(stream)
+            ev[i][2].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -322,8 +323,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    prep_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.kv16 else None
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
 
     flops_formula = 4.0 * B * H * N * N * D
     flops = flops_formula / 2 if causal else flops_formula  # causal: masked work is skipped
@@ -339,7 +339,8 @@ def main():
     # peak of the MFMA the kernel actually runs on is reported beside it
     if fmt == bnd.NVFP4 and args.kv16:
         own_peak = FP16_PEAK_TFLOPS
-        kdesc = "attn_nvfp4_kernel, KV16 instance (fp16 MFMA; K-hat and V-hat read dequantised from the prep)"
+        kdesc = ("attn_nvfp4_kernel, KV16 instance (fp16 MFMA; K-hat and V-hat read dequantised, as the "
+                 "K and V quantisers wrote them)")
     elif fmt == bnd.NVFP4:
         own_peak, kdesc = FP16_PEAK_TFLOPS, "attn_nvfp4_kernel (fp16 MFMA on exactly dequantised NVFP4 operands)"
     elif fmt == bnd.MXFP4:
@@ -354,6 +355,8 @@ def main():
     blk = 16 if fmt == bnd.NVFP4 else 32
     v_code_bytes = 1.0 if fmt == bnd.MX4_PV8 else 0.5  # MXFP8 V: one byte per element
     quant_bytes = B * H * N * D * (2 * (2 + 0.5 + 1.0 / blk) + (2 + v_code_bytes + 1.0 / blk))
+    if args.kv16:  # K-hat and V-hat: 2 bytes per element of the padded rows
+        quant_bytes += bnd.sage_fp4_kv16_bytes(*shape)
     res = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -365,7 +368,6 @@ def main():
                    "kv_tile": bnd.sage_fp4_kv_tile(), "out_dtype": "f16"},
         "attn_kernel_ms": attn_ms, "attn_tops": attn_tops, "attn_frac_fp4_peak": attn_tops / FP4_PEAK_TOPS,
         "quant_ms_3_tensors": quant_ms, "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
-        "kv16_prep_ms": prep_ms,
         # not in counter runs: their one calibration copy must be the only copy kernel
         "copy_ceiling_gbs": None if args.calibrate_copy else copy_ceiling_gbs(torch),
         "flops_counted": flops, "flops_formula_4BHN2D": flops_formula,
@@ -471,7 +473,33 @@ def main():
                 extras["nvfp4_kv16_" + ("causal" if c2 else "noncausal")] = {
                     "attn_kernel_ms": ms, "attn_tops": t, "frac_fp4_peak": t / FP4_PEAK_TOPS,
                     "kv16_prep_ms": prep, "prep_plus_attn_ms": prep + ms}
-            del kv
+            # this step (same inputs and mask) with K and V quantised by sage_fp4_quant_kv16, which
+            # also writes the fp16 buffer in the same pass, and the attention reading that buffer
+            # (the --kv16 step); 10 steps back to back after warming up
+            Kf = bnd.alloc_quant(bnd.ROLE_K, bnd.NVFP4, *shape)
+            Vf = bnd.alloc_quant(bnd.ROLE_V, bnd.NVFP4, *shape)
+
+            def kv_quant():
+                bnd.quant_kv16_into(k, bnd.ROLE_K, *Kf, kv)
+                bnd.quant_kv16_into(v, bnd.ROLE_V, *Vf, kv)
+
+            def fused_step():
+                bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
+                kv_quant()
+                bnd.attn_fwd_kv16_into(Q, kv, shape, out, causal=causal)
+
+            timed = {}
+            for key, fn in (("ms_per_step", fused_step), ("kv_quant_ms", kv_quant)):
+                warm(fn, torch)
+                e0.record(stream)
+                for _ in range(10):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                timed[key] = e0.elapsed_time(e1) / 10
+            extras["nvfp4_kv16_step_" + ("causal" if causal else "noncausal")] = {
+                **timed, "value": flops / (timed["ms_per_step"] * 1e-3) / 1e12}
+            del kv, Kf, Vf
         res["extras"] = extras
 
     if not args.no_cpu_baseline:

@@ -2,7 +2,8 @@
 of the computation runs in the library's HIP kernels. PyTorch supplies device memory and streams.
 
 The functions named like the C entry points take raw pointers/ints; the convenience wrappers
-(`quant`, `attn_fwd`, `kv16_prep`, `attn_fwd_kv16_into`, `attn_bwd_into`) take torch tensors and
+(`quant`, `attn_fwd`, `kv16_prep`, `quant_kv16`, `quant_kv16_into`, `attn_fwd_kv16_into`,
+`attn_bwd_into`) take torch tensors and
 pass the current stream."""
 from __future__ import annotations
 
@@ -21,7 +22,8 @@ STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP", -7: "SAGE_ERR_WORKSPACE"}
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
-           "sage_fp4_attn_fwd_lse", "sage_fp4_kv16_bytes", "sage_fp4_kv16_prep", "sage_fp4_attn_fwd_kv16",
+           "sage_fp4_attn_fwd_lse", "sage_fp4_kv16_bytes", "sage_fp4_kv16_prep", "sage_fp4_quant_kv16",
+           "sage_fp4_attn_fwd_kv16",
            "sage_fp4_attn_bwd_workspace_bytes", "sage_fp4_attn_bwd",
            "sage_fp4_attn_bwd_stage", "sage_fp4_attn_bwd_noalloc", "sage_fp4_status_string"]
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGE_BWD_NOALLOC_SCRATCH_BYTES
@@ -58,6 +60,7 @@ def lib():
         L.sage_fp4_attn_fwd_lse.restype = I
         L.sage_fp4_kv16_bytes.argtypes = [I, I, I, I]; L.sage_fp4_kv16_bytes.restype = S
         L.sage_fp4_kv16_prep.argtypes = [P, P, P, P, I, I, I, I, P, S, P]; L.sage_fp4_kv16_prep.restype = I
+        L.sage_fp4_quant_kv16.argtypes = [I, P, I, I, I, I, P, P, P, S, P]; L.sage_fp4_quant_kv16.restype = I
         L.sage_fp4_attn_fwd_kv16.argtypes = [P, P, P, S, I, I, I, I, I, F, P, I, P, P]
         L.sage_fp4_attn_fwd_kv16.restype = I
         L.sage_fp4_attn_bwd_workspace_bytes.argtypes = [I, I, I, I]
@@ -128,6 +131,11 @@ def sage_fp4_kv16_bytes(B, H, N, D) -> int:
 
 def sage_fp4_kv16_prep(kc, ks, vc, vs, B, H, N, D, kv16_ptr, kv16_bytes, stream_ptr) -> int:
     return lib().sage_fp4_kv16_prep(kc, ks, vc, vs, B, H, N, D, kv16_ptr, kv16_bytes, stream_ptr)
+
+
+def sage_fp4_quant_kv16(role, x_ptr, B, H, N, D, codes_ptr, scales_ptr, kv16_ptr, kv16_bytes, stream_ptr) -> int:
+    return lib().sage_fp4_quant_kv16(role, x_ptr, B, H, N, D, codes_ptr, scales_ptr, kv16_ptr, kv16_bytes,
+                                     stream_ptr)
 
 
 def sage_fp4_attn_fwd_kv16(qc, qs, kv16_ptr, kv16_bytes, B, H, N, D, causal, sm_scale, out_ptr, out_dtype,
@@ -305,9 +313,51 @@ def kv16_prep(k, v, shape, kv16=None, stream=None):
     return kv16
 
 
+def quant_kv16_into(x, role, codes, scales, kv16, stream=None):
+    """x: fp16 CUDA tensor [B,H,N,D] (K for role ROLE_K, V for ROLE_V) -> its NVFP4 codes and
+    scales (as quant_into writes them) and its half of `kv16` (as kv16_prep writes it), by one
+    sage_fp4_quant_kv16 call."""
+    import torch
+    _check(x, torch.float16, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [B,H,N,D]")
+    if role not in (ROLE_K, ROLE_V):
+        raise ValueError("role must be ROLE_K or ROLE_V")
+    B, H, N, D = x.shape
+    _check_codes((codes, scales), role, NVFP4, (B, H, N, D), x.device, "output")
+    _check(kv16, torch.uint8, "kv16", x.device, min_numel=sage_fp4_kv16_bytes(B, H, N, D))
+    rc = sage_fp4_quant_kv16(role, C.c_void_p(x.data_ptr()), B, H, N, D, C.c_void_p(codes.data_ptr()),
+                             C.c_void_p(scales.data_ptr()), C.c_void_p(kv16.data_ptr()), kv16.numel(),
+                             _stream_ptr(stream))
+    if rc != 0:
+        raise SageError(rc, "sage_fp4_quant_kv16")
+    return codes, scales
+
+
+def quant_kv16(k, v, kv16=None, stream=None):
+    """k, v: fp16 CUDA tensors [B,H,N,D] -> (K pair, V pair, kv16): the NVFP4 (codes, scales) pairs
+    quant() would return and the buffer kv16_prep() would fill from them (allocated unless `kv16`
+    is given)."""
+    import torch
+    _check(k, torch.float16, "k")
+    if k.dim() != 4:
+        raise ValueError("k must be [B,H,N,D]")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+    B, H, N, D = k.shape
+    need = sage_fp4_kv16_bytes(B, H, N, D)
+    if need == 0:
+        raise SageError(-2, f"sage_fp4_kv16_bytes: shape {tuple(k.shape)}")
+    if kv16 is None:
+        kv16 = torch.empty(need, dtype=torch.uint8, device=k.device)
+    K = quant_kv16_into(k, ROLE_K, *alloc_quant(ROLE_K, NVFP4, B, H, N, D, device=k.device), kv16, stream)
+    V = quant_kv16_into(v, ROLE_V, *alloc_quant(ROLE_V, NVFP4, B, H, N, D, device=k.device), kv16, stream)
+    return K, V, kv16
+
+
 def attn_fwd_kv16_into(q, kv16, shape, out, causal=False, sm_scale=0.0, stream=None, lse=None):
-    """q: NVFP4 (codes, scales) pair; kv16: the buffer from kv16_prep; out [B,H,N,D] fp16 or fp32;
-    lse: None or float32 with B*H*N elements. Calls sage_fp4_attn_fwd_kv16."""
+    """q: NVFP4 (codes, scales) pair; kv16: the buffer from kv16_prep or quant_kv16; out [B,H,N,D]
+    fp16 or fp32; lse: None or float32 with B*H*N elements. Calls sage_fp4_attn_fwd_kv16."""
     import torch
     B, H, N, D = shape
     od = _out_code(out)

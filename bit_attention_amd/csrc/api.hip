@@ -9,7 +9,11 @@
 
 namespace sage {
 hipError_t launch_quant_rows(bool mx, const void* x, int64_t rows, int D, void* codes, void* scales, hipStream_t st);
-hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
+// vh: NULL, or (NVFP4) where V-hat goes; launch_quant_k_hat: NVFP4 K with K-hat at kh
+hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, void* vh,
+                          hipStream_t st);
+hipError_t launch_quant_k_hat(const void* x, int BH, int N, int D, void* codes, void* scales, void* kh,
+                              hipStream_t st);
 hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st);
 // lse: NULL, or [B*H*N] fp32 that receives each row's log-sum-exp
 // kv16: ptrs[2] and ptrs[4] are K-hat and V-hat in fp16 (sage_fp4_kv16_prep's layout)
@@ -88,7 +92,7 @@ int sage_fp4_quant(int role, int fmt, const void* x, int B, int H, int N, int D,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (role == SAGE_ROLE_V && fmt == SAGE_FMT_MX4_PV8) e = sage::launch_quant_v8(x, B * H, N, D, codes, scales, st);
-  else if (role == SAGE_ROLE_V) e = sage::launch_quant_v(mx, x, B * H, N, D, codes, scales, st);
+  else if (role == SAGE_ROLE_V) e = sage::launch_quant_v(mx, x, B * H, N, D, codes, scales, nullptr, st);
   else e = sage::launch_quant_rows(mx, x, (int64_t)B * H * N, D, codes, scales, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
@@ -174,6 +178,23 @@ int sage_fp4_kv16_prep(const void* k_codes, const void* k_scales, const void* v_
   if (kv16_bytes < sage_fp4_kv16_bytes(B, H, N, D)) return SAGE_ERR_WORKSPACE;
   const hipError_t e = sage::launch_kv16_prep(k_codes, k_scales, v_codes, v_scales, B * H, N, D, kv16,
                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_fp4_quant_kv16(int role, const void* x, int B, int H, int N, int D, void* codes, void* scales, void* kv16,
+                        size_t kv16_bytes, void* stream) {
+  if (role != SAGE_ROLE_K && role != SAGE_ROLE_V) return SAGE_ERR_ENUM;
+  if (!x || !codes || !scales || !kv16) return SAGE_ERR_NULL;
+  const int sh = check_shape(B, H, N, D);
+  if (sh != SAGE_OK) return sh;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(kv16)) return SAGE_ERR_ALIGN;
+  if (kv16_bytes < sage_fp4_kv16_bytes(B, H, N, D)) return SAGE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* kh = static_cast<uint8_t*>(kv16);
+  const hipError_t e =
+      role == SAGE_ROLE_K
+          ? sage::launch_quant_k_hat(x, B * H, N, D, codes, scales, kh, st)
+          : sage::launch_quant_v(false, x, B * H, N, D, codes, scales, kh + (size_t)2 * B * H * padded(N) * D, st);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

@@ -43,15 +43,6 @@ constexpr int NV_WAVES = 4;
 constexpr int NV_BQ = 32 * NV_WAVES;  // queries per workgroup
 constexpr float LOG2_2688 = 11.392317422778762f;  // log2(448 * 6)
 
-// Eight E2M1 codes (one dword) times an fp16 scale pair, exact.
-__device__ __forceinline__ v8h dequant8(unsigned w, v2h s) {
-  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // Four E4M3 scale bytes (one dword) -> fp16 values, exact (E4M3 fits fp16).
 __device__ __forceinline__ void scales4(unsigned sw, _Float16* h) {
   const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);

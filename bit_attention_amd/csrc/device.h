@@ -112,4 +112,19 @@ __device__ __forceinline__ v2h dequant2(unsigned byte2, float p2, v2h mu) {
   return h * mu;
 }
 
+// Eight E2M1 codes (one dword) times an fp16 scale pair, exact (an E4M3 scale times a code has at
+// most 6 significant bits and lies in the normal fp16 range or is zero).
+__device__ __forceinline__ v8h dequant8(unsigned w, v2h s) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E4M3 scale byte -> its value in fp16, exact (every E4M3 value is an fp16 value).
+__device__ __forceinline__ _Float16 e4m3_to_f16(unsigned b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false)[0];
+}
+
 }  // namespace sage

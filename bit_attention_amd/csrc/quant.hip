@@ -8,7 +8,8 @@
 // the quantisation kernel also produces the permuted key order the attention kernel's register
 // layout needs (section on the hardware implementation).
 //
-// Bound: HBM. One pass: 2 B/element read, 0.5 B codes + 1/16 (1/32) B scales written.
+// Bound: HBM. One pass: 2 B/element read, 0.5 B codes + 1/16 (1/32) B scales written; the NVFP4
+// K and V kernels that also write K-hat / V-hat (exact fp16 dequantisation) add 2 B/element.
 #include "device.h"
 
 namespace sage {
@@ -106,21 +107,18 @@ __device__ __forceinline__ void load_f16(const __half* p, float* v) {
   }
 }
 
-// Q and K: one thread per block of BLK consecutive channels. Blocks of consecutive threads are
-// contiguous in memory, so loads and stores coalesce.
+// One block of BLK consecutive channels at x: its codes and scale byte are stored at block index
+// b; the code words are also returned (for a caller that dequantises them) with the scale byte.
 template <int BLK, bool MX>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales, int64_t nblocks) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
+__device__ __forceinline__ unsigned quant_block(const __half* x, uint8_t* codes, uint8_t* scales, int64_t b,
+                                                unsigned (&words)[BLK / 8]) {
   float v[BLK];
-  load_f16<BLK>(x + b * BLK, v);
+  load_f16<BLK>(x, v);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < BLK; ++i) amax = fmaxf(amax, fabsf(v[i]));
   float s;
   const unsigned sb = MX ? mx_scale(amax, &s) : nv_scale(amax, &s);
-  unsigned words[BLK / 8];
   encode_block<BLK>([&](int u) { return v[u]; }, s, MX, words);
   if (BLK == 16) {
     reinterpret_cast<uint2*>(codes)[b] = make_uint2(words[0], words[1]);
@@ -128,6 +126,45 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
     reinterpret_cast<uint4*>(codes)[b] = make_uint4(words[0], words[1], words[BLK / 8 > 2 ? 2 : 0], words[BLK / 8 > 3 ? 3 : 0]);
   }
   scales[b] = (uint8_t)sb;
+  return sb;
+}
+
+// Q and K: one thread per block of BLK consecutive channels. Blocks of consecutive threads are
+// contiguous in memory, so loads and stores coalesce.
+template <int BLK, bool MX>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  unsigned words[BLK / 8];
+  quant_block<BLK, MX>(x + b * BLK, codes, scales, b, words);
+}
+
+// NVFP4 K together with K-hat, its exact fp16 dequantisation ([BH][Np][D], rows >= N zero), the
+// layout the attention copies K tiles from. Grid (ceil(Np*D/16 / 256), BH): one thread per
+// 16-channel block of a head's padded rows. Codes and scales are those of quant_rows_kernel;
+// each K-hat value is its code times the block's E4M3 scale.
+template <int D>
+__global__ __launch_bounds__(256) void quant_k_hat_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, int N, int64_t Np,
+                                                          _Float16* __restrict__ kh) {
+  constexpr int BPR = D / 16;  // blocks per row
+  const int64_t bh = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // block within the head's padded rows
+  if (i >= Np * BPR) return;
+  const int64_t j = i / BPR;
+  v8h lo = v8h{0, 0, 0, 0, 0, 0, 0, 0}, hi = lo;
+  if (j < N) {
+    const int64_t b = (bh * N + j) * BPR + i % BPR;
+    unsigned words[2];
+    const unsigned sb = quant_block<16, false>(x + b * 16, codes, scales, b, words);
+    const _Float16 sh = e4m3_to_f16(sb);
+    lo = dequant8(words[0], v2h{sh, sh});
+    hi = dequant8(words[1], v2h{sh, sh});
+  }
+  v8h* dst = reinterpret_cast<v8h*>(kh + bh * Np * D + i * 16);
+  dst[0] = lo;
+  dst[1] = hi;
 }
 
 // V: one workgroup of 2*D threads per (batch*head, run of `tpw` consecutive 128-token tiles).
@@ -146,10 +183,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __half* __restric
 // FMT 0: NVFP4 (16-slot blocks, E4M3 scale of amax/6); 1: MXFP4 (32-slot blocks, E8M0 scale;
 // codes are the E2M1 value nearest the exact quotient, ties to even); 2: MXFP8 (32-slot blocks;
 // codes the E4M3 value nearest x / 2^X, ties to even, clamped to +-448; sign the input's).
-template <int D, int FMT>
+// HAT (NVFP4 only): V-hat, each code times its block's E4M3 scale in fp16, is also stored in the
+// codes' layout ([B,H,Np/128,D,128] halves), from the code words and scale bytes just made.
+template <int D, int FMT, bool HAT = false>
 __global__ __launch_bounds__(2 * D, FMT == 2 ? 2 : 3) void quant_v_tile_kernel(const __half* __restrict__ x, uint8_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales, int N, int64_t Np, int tpw) {
+                                                             uint8_t* __restrict__ scales, int N, int64_t Np, int tpw,
+                                                             _Float16* __restrict__ vh) {
   constexpr bool F8 = FMT == 2, NV = FMT == 0;
+  static_assert(!HAT || NV, "V-hat is written for NVFP4 only");
   constexpr int NT = 2 * D;     // threads: one channel pair x one block (pair) each
   constexpr int PITCH = D + 8;  // halves
   constexpr int BLK = NV ? 16 : 32, NB = KV_TILE / BLK;
@@ -260,6 +301,20 @@ __global__ __launch_bounds__(2 * D, FMT == 2 ? 2 : 3) void quant_v_tile_kernel(c
         *reinterpret_cast<uint2*>(srun + 2 * dp * NB) = make_uint2(lo01 | (lo23 << 16), hi01 | (hi23 << 16));
       }
     }
+    if (HAT) {
+      // this lane's slots 32j..32j+31 of channels 2dp and 2dp+1: words 2ps, 2ps+1 of channel c
+      // belong to block 2j+ps, whose scale byte is byte c of sbp[ps]
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        v8h* dst = reinterpret_cast<v8h*>(vh + ((bh * ntiles + kt) * D + 2 * dp + c) * KV_TILE + 32 * j);
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+          const _Float16 sh = e4m3_to_f16((sbp[ps] >> (8 * c)) & 0xFFu);
+          dst[2 * ps] = dequant8(wd[c][2 * ps], v2h{sh, sh});
+          dst[2 * ps + 1] = dequant8(wd[c][2 * ps + 1], v2h{sh, sh});
+        }
+      }
+    }
   };
   // Two register buffers: tiles kt0 and kt0+1 are both in flight from the start, and each
   // buffer is refilled two tiles ahead as soon as it is staged.
@@ -299,25 +354,44 @@ hipError_t launch_quant_v8(const void* x, int BH, int N, int D, void* codes, voi
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE, nt = Np / KV_TILE;
   const int tpw = v_tiles_per_wg(nt, BH);
   const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(2 * D);
-  if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
-  else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw);
+  if (D == 64) quant_v_tile_kernel<64, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw, nullptr);
+  else quant_v_tile_kernel<128, 2><<<grid, block, 0, st>>>((const __half*)x, (uint8_t*)codes, (uint8_t*)scales, N, Np, tpw, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, hipStream_t st) {
+// vh: NULL, or (NVFP4 only) where V-hat goes
+hipError_t launch_quant_v(bool mx, const void* x, int BH, int N, int D, void* codes, void* scales, void* vh,
+                          hipStream_t st) {
   const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
   const __half* xp = (const __half*)x;
   uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
+  _Float16* h = (_Float16*)vh;
   const int64_t nt = Np / KV_TILE;
   const int tpw = v_tiles_per_wg(nt, BH);
   const dim3 grid((unsigned)((nt + tpw - 1) / tpw), (unsigned)BH), block(2 * D);
   if (mx) {
-    if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
-    else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
+    if (D == 64) quant_v_tile_kernel<64, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, nullptr);
+    else quant_v_tile_kernel<128, 1><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, nullptr);
+  } else if (h) {
+    if (D == 64) quant_v_tile_kernel<64, 0, true><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, h);
+    else quant_v_tile_kernel<128, 0, true><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, h);
   } else {
-    if (D == 64) quant_v_tile_kernel<64, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
-    else quant_v_tile_kernel<128, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw);
+    if (D == 64) quant_v_tile_kernel<64, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, nullptr);
+    else quant_v_tile_kernel<128, 0><<<grid, block, 0, st>>>(xp, c, s, N, Np, tpw, nullptr);
   }
+  return hipGetLastError();
+}
+
+// NVFP4 K codes and scales with K-hat at kh ([BH][Np][D] fp16)
+hipError_t launch_quant_k_hat(const void* x, int BH, int N, int D, void* codes, void* scales, void* kh,
+                              hipStream_t st) {
+  const int64_t Np = ((int64_t)N + KV_TILE - 1) / KV_TILE * KV_TILE;
+  const dim3 grid((unsigned)((Np * (D / 16) + 255) / 256), (unsigned)BH), block(256);
+  const __half* xp = (const __half*)x;
+  uint8_t *c = (uint8_t*)codes, *s = (uint8_t*)scales;
+  _Float16* h = (_Float16*)kh;
+  if (D == 64) quant_k_hat_kernel<64><<<grid, block, 0, st>>>(xp, c, s, N, Np, h);
+  else quant_k_hat_kernel<128><<<grid, block, 0, st>>>(xp, c, s, N, Np, h);
   return hipGetLastError();
 }
 

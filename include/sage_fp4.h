@@ -166,6 +166,20 @@ int sage_fp4_kv16_prep(const void* k_codes, const void* k_scales,
                        const void* v_codes, const void* v_scales,
                        int B, int H, int N, int D, void* kv16, size_t kv16_bytes, void* stream);
 
+/* NVFP4 quantisation of K or V that also fills that operand's part of the kv16 buffer, in the
+ * same pass over x (the DeepTech article, section on FP4 inference and its hardware
+ * implementation, for the operands): codes and scales are those sage_fp4_quant(role,
+ * SAGE_FMT_NVFP4, ...) writes, and the kv16 bytes those sage_fp4_kv16_prep writes from them, bit
+ * for bit. role SAGE_ROLE_K writes K-hat (the first half of kv16), SAGE_ROLE_V writes V-hat (the
+ * second half); the other half is left as it is, so one call per role fills the buffer.
+ *   role    SAGE_ROLE_K or SAGE_ROLE_V, else SAGE_ERR_ENUM.
+ *   kv16    device buffer of at least sage_fp4_kv16_bytes(B,H,N,D) bytes, caller-owned, 16-byte
+ *           aligned; a smaller kv16_bytes is SAGE_ERR_WORKSPACE.
+ * x, codes, scales, the shape, validation and errors as for sage_fp4_quant. Nothing is written
+ * when an error is returned before the launch. One kernel launch. */
+int sage_fp4_quant_kv16(int role, const void* x, int B, int H, int N, int D,
+                        void* codes, void* scales, void* kv16, size_t kv16_bytes, void* stream);
+
 /* NVFP4 attention forward with K and V from sage_fp4_kv16_prep's buffer: the same operation,
  * tiles and arithmetic as sage_fp4_attn_fwd(SAGE_FMT_NVFP4, ...) on the codes kv16 was made from,
  * and the same output bit for bit (and lse as sage_fp4_attn_fwd_lse). It reads 2 bytes per K and

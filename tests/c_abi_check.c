@@ -101,6 +101,9 @@ int main(void) {
     CHECK(sage_fp4_kv16_prep(fake, fake, fake, fake, 1, 1, 16, 64, fake, need - 1, NULL) == SAGE_ERR_WORKSPACE);
     CHECK(sage_fp4_kv16_prep(fake, fake, fake, NULL, 1, 1, 16, 64, fake, need, NULL) == SAGE_ERR_NULL);
     CHECK(sage_fp4_kv16_prep(fake, fake, fake, fake, 1, 1, 16, 64, mis, need, NULL) == SAGE_ERR_ALIGN);
+    CHECK(sage_fp4_quant_kv16(SAGE_ROLE_Q, fake, 1, 1, 16, 64, fake, fake, fake, need, NULL) == SAGE_ERR_ENUM);
+    CHECK(sage_fp4_quant_kv16(SAGE_ROLE_K, fake, 1, 1, 16, 64, fake, fake, fake, need - 1, NULL) == SAGE_ERR_WORKSPACE);
+    CHECK(sage_fp4_quant_kv16(SAGE_ROLE_V, fake, 1, 1, 16, 64, fake, fake, NULL, need, NULL) == SAGE_ERR_NULL);
     CHECK(sage_fp4_attn_fwd_kv16(fake, fake, fake, need - 1, 1, 1, 16, 64, 0, 0.0f, fake, SAGE_OUT_F32, NULL, NULL) ==
           SAGE_ERR_WORKSPACE);
     CHECK(sage_fp4_attn_fwd_kv16(fake, fake, fake, need, 1, 1, 16, 64, 0, 0.0f, fake, 3, NULL, NULL) == SAGE_ERR_ENUM);

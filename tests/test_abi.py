@@ -189,3 +189,13 @@ def test_kv16_bytes_and_validation():
     assert call(out=MIS) == -4
     assert call(lse=MIS) == -4
     assert call(kv=MIS) == -4
+    qk = bnd.sage_fp4_quant_kv16
+
+    def qcall(role=1, x=FAKE, c=FAKE, s=FAKE, kv=FAKE, kvb=need, D=64, N=16):
+        return qk(role, x, 1, 1, N, D, c, s, kv, kvb, None)
+
+    assert qcall(role=0) == -5 and qcall(role=3) == -5
+    assert qcall(kvb=need - 1) == -7 and qcall(role=2, kvb=need - 1) == -7
+    assert qcall(x=None) == -1 and qcall(c=None) == -1 and qcall(s=None) == -1 and qcall(kv=None) == -1
+    assert qcall(x=MIS) == -4 and qcall(s=MIS) == -4 and qcall(kv=MIS) == -4
+    assert qcall(D=96) == -3 and qcall(N=0) == -2

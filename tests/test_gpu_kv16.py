@@ -9,7 +9,10 @@ sage_fp4_attn_fwd_kv16) through the C ABI.
 - Against the oracle directly, every row of small shapes within 2e-3 (the bar of
   tests/test_gpu_attn.py; the slack is reported, not added).
 - Equal to the codes path at the C ABI's limits too: N = 2^20, and B*H = 65535.
-- A buffer smaller than sage_fp4_kv16_bytes is refused before any launch."""
+- A buffer smaller than sage_fp4_kv16_bytes is refused before any launch.
+- sage_fp4_quant_kv16 (K or V quantised with its half of the buffer in the same pass) writes the
+  codes and scales of sage_fp4_quant and the buffer bytes of sage_fp4_kv16_prep, byte for byte,
+  every byte of each (outputs pre-filled), and leaves the other role's half as it was."""
 import numpy as np
 import pytest
 
@@ -164,3 +167,90 @@ def test_limits_equal_to_codes_path(shape):
         say(f"kv16 limits shape={shape} causal={causal}")
         a, b = _both(Q, K, V, shape, causal)
         _bit_equal(a, b, f"limits {shape} causal {causal}")
+
+
+FUSED = [(1, 2, 300, 128), (2, 3, 129, 64), (1, 1, 1, 128), (1, 2, 256, 64), (1, 1, 640, 128), (3, 1, 1000, 64)]
+
+
+def _fused_equals_separate(k, v, what):
+    """quant_kv16 on pre-filled buffers against quant + kv16_prep, byte for byte."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    B, H, N, D = k.shape
+    need = bnd.sage_fp4_kv16_bytes(B, H, N, D)
+    K = bnd.quant(k, 1, NV)
+    V = bnd.quant(v, 2, NV)
+    ref = bnd.kv16_prep(K, V, k.shape)
+    kv = torch.full((need,), 0x7B, dtype=torch.uint8, device="cuda")
+    Kf, Vf, kv = bnd.quant_kv16(k, v, kv16=kv)
+    torch.cuda.synchronize()
+    for (a, b), name in (((K[0], Kf[0]), "K codes"), ((K[1], Kf[1]), "K scales"), ((V[0], Vf[0]), "V codes"),
+                         ((V[1], Vf[1]), "V scales"), ((ref, kv), "kv16 buffer")):
+        assert torch.equal(a, b), f"{what}: {name} differ at {int((a != b).sum())} bytes"
+
+
+@pytest.mark.parametrize("shape", FUSED)
+def test_quant_kv16_equals_quant_and_prep(shape):
+    import torch
+    B, H, N, D = shape
+    q, k, v = workload(3, B=B, H=H, N=N, D=D)
+    say(f"quant_kv16 shape={shape}")
+    _fused_equals_separate(to_gpu(k), to_gpu(v), f"shape {shape}")
+
+
+@pytest.mark.parametrize("wl", [2, 3, 4])
+def test_quant_kv16_full_size(wl):
+    q, k, v = workload(wl)
+    say(f"quant_kv16 full workload {wl} shape={q.shape}")
+    _fused_equals_separate(to_gpu(k), to_gpu(v), f"workload {wl}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1 << 20, 64), (1, 65535, 1, 128)])
+def test_quant_kv16_limits(shape):
+    """The K-hat grid's largest x (N = 2^20) and y (B*H = 65535) extents."""
+    rng = np.random.default_rng(991)
+    k, v = (to_gpu(rng.standard_normal(shape).astype(np.float16)) for _ in range(2))
+    say(f"quant_kv16 limits shape={shape}")
+    _fused_equals_separate(k, v, f"limits {shape}")
+
+
+def test_quant_kv16_one_role_leaves_other_half():
+    import ctypes as C
+    import torch
+    from bit_attention_amd import binding as bnd
+    shape = (2, 2, 300, 64)
+    B, H, N, D = shape
+    q, k, v = workload(1, B=B, H=H, N=N, D=D)
+    need = bnd.sage_fp4_kv16_bytes(*shape)
+    half = need // 2
+    for role, x, written in ((1, k, slice(0, half)), (2, v, slice(half, need))):
+        kv = torch.full((need,), 0x7B, dtype=torch.uint8, device="cuda")
+        codes, scales = bnd.alloc_quant(role, NV, *shape)
+        xg = to_gpu(x)
+        rc = bnd.sage_fp4_quant_kv16(role, C.c_void_p(xg.data_ptr()), *shape, C.c_void_p(codes.data_ptr()),
+                                     C.c_void_p(scales.data_ptr()), C.c_void_p(kv.data_ptr()), need, None)
+        assert rc == 0
+        torch.cuda.synchronize()
+        untouched = torch.ones(need, dtype=torch.bool, device="cuda")
+        untouched[written] = False
+        assert bool((kv[untouched] == 0x7B).all()), f"role {role} wrote outside its half"
+        assert not bool((kv[written] == 0x7B).all()), f"role {role} wrote nothing"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_from_quant_kv16_equals_codes_path(causal):
+    """The whole fused path (Q quantised as usual, K and V with their halves of the buffer, then
+    the attention from the buffer) against the codes path, bit for bit."""
+    import torch
+    from bit_attention_amd import binding as bnd
+    q, k, v = workload(2, B=1, H=4, N=1000, D=128)
+    shape = q.shape
+    say(f"quant_kv16 + attention causal={causal}")
+    Q = bnd.quant(to_gpu(q), 0, NV)
+    K, V, kv = bnd.quant_kv16(to_gpu(k), to_gpu(v))
+    o1 = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    o2 = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    bnd.attn_fwd_into(NV, Q, K, V, shape, o1, causal=causal)
+    bnd.attn_fwd_kv16_into(Q, kv, shape, o2, causal=causal)
+    torch.cuda.synchronize()
+    _bit_equal(o1.cpu().numpy(), o2.cpu().numpy(), f"fused path causal {causal}")
