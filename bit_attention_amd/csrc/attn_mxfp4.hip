@@ -100,6 +100,14 @@ __device__ __forceinline__ void lds_copy16(const void* base, unsigned nbytes, un
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// One byte per lane through a buffer resource of `nbytes` bytes at `base` (wave-uniform): lane i
+// reads base + voff, or 0 where voff >= nbytes. With the tile's base in the resource the lane's
+// offset stays the same from tile to tile, so no address arithmetic is repeated per tile.
+__device__ __forceinline__ unsigned load_byte(const void* base, unsigned nbytes, unsigned voff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, 0, 0);
+}
+
 // The lane's partner value after a permlane swap of `mine` (the pair holds both, in an order
 // that depends on the lane; equal values make either choice right).
 __device__ __forceinline__ unsigned partner_of(unsigned mine, unsigned p0, unsigned p1) {
@@ -208,9 +216,10 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       const int job = NW * i + wu;
       if (job < VJOBS) lds_copy16(vb, (unsigned)(VB * D), voff[i], sVc + 1024 * job);
     }
-    const int jj = kt * KV_TILE + tid / NBD;  // key of this thread's scale byte (block tid % NBD)
-    rks = jj < N ? ks_h[(int64_t)kt * KV_TILE * NBD + tid] : 0x7Fu;
-    rvs = vs_h[(unsigned)tid + (unsigned)kt * (unsigned)(4 * D)];
+    // this thread's scale bytes: K key kt*128 + tid/NBD, block tid%NBD (keys past N read 0, the
+    // E8M0 value 2^-127, times their zero codes: an exact 0 score, masked anyway); V byte tid
+    rks = load_byte(ks_h + (int64_t)kt * KV_TILE * NBD, kn / (D / 2) * NBD, (unsigned)tid);
+    rvs = load_byte(vs_h + (int64_t)kt * (4 * D), (unsigned)(4 * D), (unsigned)tid);
   };
   // One key tile, from LDS set (sKc, sKs, sVc, sVs), copying the next one into (nKc, nVc). The
   // sets are __restrict__ parameters: the compiler then knows that the copies and this tile's
