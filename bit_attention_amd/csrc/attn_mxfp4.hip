@@ -221,6 +221,11 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
     rks = load_byte(ks_h + (int64_t)kt * KV_TILE * NBD, kn / (D / 2) * NBD, (unsigned)tid);
     rvs = load_byte(vs_h + (int64_t)kt * (4 * D), (unsigned)(4 * D), (unsigned)tid);
   };
+  // Direct-P: a 16 x 128 tile of ones (E2M1 code 2 = 1.0 in every nibble), the A operand of the
+  // normaliser's MFMA. The empty asm makes its value opaque, so it stays in four VGPRs for the
+  // whole loop instead of being rebuilt from a constant in every tile.
+  unsigned one0 = 0x22222222u, one1 = one0, one2 = one0, one3 = one0;
+  if (DIRECT_P) asm volatile("" : "+v"(one0), "+v"(one1), "+v"(one2), "+v"(one3));
   // One key tile, from LDS set (sKc, sKs, sVc, sVs), copying the next one into (nKc, nVc). The
   // sets are __restrict__ parameters: the compiler then knows that the copies and this tile's
   // reads touch different memory, and puts no wait for the copies before the reads.
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(64 * mx_waves<D>(), 4) void attn_mxfp4_kernel(
       // Direct-P normaliser: the sum of the rounded P values, as one more MFMA of P against a
       // 16 x 128 tile of ones (E2M1 code 2 = 1.0, unit scale); all 16 rows of the product equal
       // the row sum, and C's layout hands each lane the sum of its own query qi.
-      const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+      const v8i ones = {(int)one0, (int)one1, (int)one2, (int)one3, 0, 0, 0, 0};
       Lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf, Lacc, 4, 4, 0, 127, 0, psc);
     }
   };

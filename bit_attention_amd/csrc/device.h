@@ -87,15 +87,24 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// max(a, b) in one v_max_f32. For operands that arrive as bit patterns (a lane swap) the compiler
+// quiets each one first (v_max x, x, x) in case it is a signalling NaN; scores and their maxima
+// never are NaN, so the plain instruction gives the same value.
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Max over the lane pair {l, l^16}, over {l, l^32}, and over the four lanes {l, l^16, l^32,
-// l^48} that share a column of a 16x16 MFMA tile.
+// l^48} that share a column of a 16x16 MFMA tile (operands never NaN).
 __device__ __forceinline__ float pair16_max(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
-  return fmaxf(as_f(p[0]), as_f(p[1]));
+  return max2f(as_f(p[0]), as_f(p[1]));
 }
 __device__ __forceinline__ float pair32_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
-  return fmaxf(as_f(r[0]), as_f(r[1]));
+  return max2f(as_f(r[0]), as_f(r[1]));
 }
 __device__ __forceinline__ float xg_max(float v) { return pair32_max(pair16_max(v)); }
 __device__ __forceinline__ float xg_sum(float v) {
