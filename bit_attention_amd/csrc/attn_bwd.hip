@@ -240,6 +240,16 @@ template <int D>
 __device__ __forceinline__ int swz16(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 __device__ __forceinline__ int swz8(int d) { return (d >> 2) & 3; }
 
+// Max over the four lanes {l, l^16, l^32, l^48} by fmaxf. The plain-instruction form the forward
+// kernels use (xg_max) gives the same values here, but with it the compiler spilled five VGPRs of
+// the causal D = 128 dK/dV kernel into scratch, reloaded in every tile.
+__device__ __forceinline__ float xg_fmax(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
+  v = fmaxf(as_f(p[0]), as_f(p[1]));
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
+  return fmaxf(as_f(r[0]), as_f(r[1]));
+}
+
 // Asynchronous copy of 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
 // lane i writes lds + 16 i, lds being the same for the whole wave; vmcnt counts completion.
 __device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
@@ -501,8 +511,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
         smax = fmaxf(smax, fabsf(dS[s][i]));
       }
     }
-    pmax = xg_max(pmax);
-    smax = xg_max(smax);
+    pmax = xg_fmax(pmax);
+    smax = xg_fmax(smax);
     const v4i aP = codes16(P, recip127(pmax));
     const v4i aS = codes16(dS, recip127(smax));
     const float sP = pmax * INV127, sS = smax * INV127;
@@ -657,7 +667,7 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
           smax = fmaxf(smax, fabsf(dS[s][i]));
         }
       }
-      smax = xg_max(smax);
+      smax = xg_fmax(smax);
       const v4i aS = codes16(dS, recip127(smax));
       const float sS = smax * INV127;
       float rS[4];
