@@ -231,6 +231,9 @@ struct BwdTile {
   static constexpr int T4 = BB * D / 2;   // bytes of an FP4 code tile (64 tokens x D / 2)
   static constexpr int W4 = T4 / 1024;    // ... its wave-wide copies
   static constexpr int TS = BB * D / 32;  // bytes of an MXFP4 scale table (64 tokens x D / 32)
+  // The FP4 codes and their table stand in for a 16-bit tile: the table is copied by a whole wave
+  // (lanes past TS bytes read zeros into the slack behind it), so the copy needs no lane branch
+  static_assert(T4 + 1024 <= T16, "room for a wave-wide copy of the scale table");
 };
 
 // LDS tiles carry no padding. An MFMA operand read has 16 lanes fetch one 16-byte chunk from
@@ -250,15 +253,36 @@ __device__ __forceinline__ float xg_fmax(float v) {
   return fmaxf(as_f(r[0]), as_f(r[1]));
 }
 
-// Asynchronous copy of 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
-// lane i writes lds + 16 i, lds being the same for the whole wave; vmcnt counts completion.
-__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// Asynchronous copy of 16 bytes per lane into LDS (buffer_load_dwordx4 ... lds) through a buffer
+// resource of `nbytes` bytes at `base`: lane i reads base + voff, or 0 where voff >= nbytes, and
+// writes lds + 16 i. base and lds are the same for the whole wave (base in SGPRs, so a lane's
+// address is one 32-bit offset); vmcnt counts completion.
+// base and nbytes go through readfirstlane: they are uniform, but the compiler may hold a value
+// they derive from in VGPRs (N, after a divergent branch of the prologue assigned it on both
+// sides), and a buffer resource in VGPRs costs a waterfall loop per copy. readfirstlane returns
+// an int: each half is taken back as unsigned before it is widened, so the low half is not
+// sign-extended into the high one.
+__device__ __forceinline__ void lds_copy16(const void* base, unsigned nbytes, unsigned voff, void* lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const int nu = __builtin_amdgcn_readfirstlane((int)nbytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), 0, nu, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Jobs [J0, J1) of a tile's copy schedule, dealt round-robin over NWAVE waves (job j to wave
+// j % NWAVE): f(j - J0) for this wave's. Each kind of copy gets a loop of its own, so no two kinds
+// share a call site whose buffer resource the compiler would merge into VGPRs.
+template <int J0, int J1, int NWAVE, typename F>
+__device__ __forceinline__ void wave_jobs(int wave, F f) {
+  for (int j = J0 + (wave - J0 % NWAVE + NWAVE) % NWAVE; j < J1; j += NWAVE) f(j - J0);
 }
 
 // Copy j of a 16-bit tile: rows [t0, t0 + 64) of one head of a [.., N, D] tensor starting at
-// `head`; a row past N reads row N - 1 (its results are masked).
+// `head` (t0 < N); a row past N reads zeros. Such rows only meet P = 0: queries past N carry the
+// lse padding (P underflows to exactly 0) and keys past N are masked.
 template <int D>
 __device__ __forceinline__ void copy16_job(int j, int lane, const uint8_t* head, int t0, int N, uint8_t* tile) {
   int r, cs;
@@ -269,14 +293,16 @@ __device__ __forceinline__ void copy16_job(int j, int lane, const uint8_t* head,
     r = 8 * j + (lane >> 3);
     cs = lane & 7;
   }
-  const int row = min(t0 + r, N - 1);
-  lds_copy16(head + (int64_t)row * (2 * D) + 16 * (cs ^ swz16<D>(r)), tile + 1024 * j);
+  lds_copy16(head + (int64_t)t0 * (2 * D), (unsigned)(N - t0) * (2 * D), (unsigned)(r * (2 * D) + 16 * (cs ^ swz16<D>(r))),
+             tile + 1024 * j);
 }
 
-// Copy j of an INT8 tile: 64 slots of every channel, starting at blk0 = codes + (bh D) Np + t0.
-__device__ __forceinline__ void copy8_job(int j, int lane, const int8_t* blk0, int Np, uint8_t* tile) {
+// Copy j of an INT8 tile: 64 slots of every channel, starting at blk0 = codes + (bh D) Np + t0
+// (the head's codes end D Np - t0 bytes later).
+template <int D>
+__device__ __forceinline__ void copy8_job(int j, int lane, const int8_t* blk0, int Np, int t0, uint8_t* tile) {
   const int d = 16 * j + (lane >> 2);
-  lds_copy16(blk0 + (int64_t)d * Np + 16 * ((lane & 3) ^ swz8(d)), tile + 1024 * j);
+  lds_copy16(blk0, (unsigned)(D * Np - t0), (unsigned)(d * Np + 16 * ((lane & 3) ^ swz8(d))), tile + 1024 * j);
 }
 
 // MFMA A operand (8 x 16 bits) of tile row r, channels 32 kk + 8 g .. + 7; sw = swz16(r), which
@@ -308,14 +334,13 @@ struct Fp4Ops {
 template <int D>
 __device__ __forceinline__ int swz4(int r) { return D == 128 ? (r >> 2) & 3 : (r >> 3) & 1; }
 
-// Copy j of an FP4 code tile: rows [t0, t0 + 64) of one head of a [.., N, D/2] code array; a row
-// past N reads row N - 1.
+// Copy j of an FP4 code tile: rows [t0, t0 + 64) of one head of a [.., N, D/2] code array
+// (t0 < N); a row past N reads zero codes (and only meets P = 0, as in copy16_job).
 template <int D>
 __device__ __forceinline__ void copy4_job(int j, int lane, const uint8_t* head, int t0, int N, uint8_t* tile) {
   constexpr int RB = D / 2, CPR = RB / 16, RPJ = 64 / CPR;  // row bytes, chunks per row, rows per copy
   const int r = RPJ * j + lane / CPR, cs = lane % CPR;
-  const int row = min(t0 + r, N - 1);
-  lds_copy16(head + (int64_t)row * RB + 16 * (cs ^ swz4<D>(r)), tile + 1024 * j);
+  lds_copy16(head + (int64_t)t0 * RB, (unsigned)(N - t0) * RB, (unsigned)(r * RB + 16 * (cs ^ swz4<D>(r))), tile + 1024 * j);
 }
 
 // FP4 MFMA A operand: the 16 code bytes of tile row r, K block g. At D = 64 the lane groups
@@ -398,8 +423,11 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
     Fp4Ops f) {
   using T = BwdTile<D>;
   constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
+  // the four fp32 runs (scales of Q8 and dO8, lse*log2e, D) get 1 KB slots each, so a whole wave
+  // copies each one (lanes past the run read zeros into its slot) and no copy needs a lane branch
+  static_assert(4 * D <= 1024 && 4 * BB <= 1024, "fp32 runs fit their 1 KB slots");
   constexpr int O_DO = T::T16, O_Q8 = 2 * T::T16, O_DO8 = O_Q8 + T::T8, O_QS = O_DO8 + T::T8;
-  constexpr int O_DOS = O_QS + 4 * D, O_L = O_DOS + 4 * D, O_D = O_L + 4 * BB, BUF = O_D + 4 * BB;
+  constexpr int O_DOS = O_QS + 1024, O_L = O_DOS + 1024, O_D = O_L + 1024, BUF = O_D + 1024;
   // copies of the Q tile: bf16 rows, or (MXS) FP4 codes and one copy of the scale table
   constexpr int JQ = MXS ? T::W4 + 1 : T::W16;
   constexpr int NJ = JQ + T::W16 + 2 * T::W8 + 4;
@@ -408,8 +436,10 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   const int nq = Np / BB;
   const int nkb = (N + WB - 1) / WB;
   const int w = xcd_work(blockIdx.x, BH * nkb);
-  const int64_t bh = w / nkb;
-  const int kb = w % nkb;  // causal: the heaviest key blocks (most query tiles) of a head first
+  // bh and kb are uniform; readfirstlane keeps them in SGPRs (the division runs on the VALU), so
+  // the copies' buffer resources built from them need no waterfall loop
+  const int64_t bh = __builtin_amdgcn_readfirstlane(w / nkb);
+  const int kb = __builtin_amdgcn_readfirstlane(w % nkb);  // causal: the heaviest key blocks first
   // the wave index is uniform across a wave: readfirstlane lets the copy schedule branch on scalars
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 4, col = l & 15;
@@ -446,30 +476,25 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dkdv_kernel(
   auto tile_of = [&](int it) { return CAUSAL ? nq - 1 - it : it; };
   auto issue = [&](int it, uint8_t* buf) {
     const int qt = tile_of(it), t0 = qt * BB;
-    for (int j = wave; j < NJ; j += NWAVE) {
-      if (j < JQ) {
-        if constexpr (MXS) {
-          if (j < T::W4) copy4_job<D>(j, l, f.qc + bh * N * (D / 2), t0, N, buf);
-          else if (l < T::TS / 16) lds_copy16(f.qt + (bh * nq + qt) * T::TS + 16 * l, buf + T::T4);
-        } else {
-          copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(qh + bh * N * D), t0, N, buf);
-        }
-      } else if (j < JQ + T::W16) {
-        copy16_job<D>(j - JQ, l, reinterpret_cast<const uint8_t*>(dout + bh * N * D), t0, N, buf + O_DO);
-      } else if (j < JQ + T::W16 + T::W8) {
-        copy8_job(j - JQ - T::W16, l, q8 + bh * D * Np + t0, Np, buf + O_Q8);
-      } else if (j < JQ + T::W16 + 2 * T::W8) {
-        copy8_job(j - JQ - T::W16 - T::W8, l, do8 + bh * D * Np + t0, Np, buf + O_DO8);
-      } else {
-        const int k = j - JQ - T::W16 - 2 * T::W8;  // scales of Q8, of dO8; lse * log2(e); D
-        const float* src = k == 0 ? q8s + (bh * nq + qt) * D
-                           : k == 1 ? do8s + (bh * nq + qt) * D
-                           : k == 2 ? l2 + bh * Np + t0
-                                    : dl + bh * Np + t0;
-        const int off = k == 0 ? O_QS : k == 1 ? O_DOS : k == 2 ? O_L : O_D;
-        if (l < (k < 2 ? D / 4 : BB / 4)) lds_copy16(src + 4 * l, buf + off);
-      }
+    constexpr int J8 = JQ + T::W16, JS = J8 + 2 * T::W8;  // first INT8 job, first fp32-run job
+    if constexpr (MXS) {
+      wave_jobs<0, T::W4, NWAVE>(wave, [&](int j) { copy4_job<D>(j, l, f.qc + bh * N * (D / 2), t0, N, buf); });
+      wave_jobs<T::W4, JQ, NWAVE>(wave, [&](int) { lds_copy16(f.qt + (bh * nq + qt) * T::TS, T::TS, 16 * l, buf + T::T4); });
+    } else {
+      wave_jobs<0, JQ, NWAVE>(wave, [&](int j) {
+        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(qh + bh * N * D), t0, N, buf);
+      });
     }
+    wave_jobs<JQ, J8, NWAVE>(wave, [&](int j) {
+      copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(dout + bh * N * D), t0, N, buf + O_DO);
+    });
+    wave_jobs<J8, J8 + T::W8, NWAVE>(wave, [&](int j) { copy8_job<D>(j, l, q8 + bh * D * Np + t0, Np, t0, buf + O_Q8); });
+    wave_jobs<J8 + T::W8, JS, NWAVE>(wave, [&](int j) { copy8_job<D>(j, l, do8 + bh * D * Np + t0, Np, t0, buf + O_DO8); });
+    // the fp32 runs: scales of Q8 and of dO8, lse * log2(e), D
+    wave_jobs<JS, JS + 1, NWAVE>(wave, [&](int) { lds_copy16(q8s + (bh * nq + qt) * D, 4 * D, 16 * l, buf + O_QS); });
+    wave_jobs<JS + 1, JS + 2, NWAVE>(wave, [&](int) { lds_copy16(do8s + (bh * nq + qt) * D, 4 * D, 16 * l, buf + O_DOS); });
+    wave_jobs<JS + 2, JS + 3, NWAVE>(wave, [&](int) { lds_copy16(l2 + bh * Np + t0, 4 * BB, 16 * l, buf + O_L); });
+    wave_jobs<JS + 3, NJ, NWAVE>(wave, [&](int) { lds_copy16(dl + bh * Np + t0, 4 * BB, 16 * l, buf + O_D); });
   };
 
   issue(0, lds[0]);
@@ -565,7 +590,7 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
     void* __restrict__ dq, Fp4Ops f) {
   using T = BwdTile<D>;
   constexpr int NWAVE = nwave<D>(), WB = wblock<D>();
-  constexpr int O_V = T::T16, O_K8 = 2 * T::T16, O_KS = O_K8 + T::T8, BUF = O_KS + 4 * D;
+  constexpr int O_V = T::T16, O_K8 = 2 * T::T16, O_KS = O_K8 + T::T8, BUF = O_KS + 1024;  // K8 scales: a 1 KB slot
   constexpr int JK = MXS ? T::W4 + 1 : T::W16;  // copies of the K tile (as in the dK/dV kernel)
   constexpr int NJ = JK + T::W16 + T::W8 + 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BUF];
@@ -573,8 +598,8 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
   const int nk = Np / BB;
   const int nqb = (N + WB - 1) / WB;
   const int w = xcd_work(blockIdx.x, BH * nqb);
-  const int64_t bh = w / nqb;
-  const int qb = CAUSAL ? nqb - 1 - w % nqb : w % nqb;  // causal: the heaviest query blocks first
+  const int64_t bh = __builtin_amdgcn_readfirstlane(w / nqb);  // uniform, kept in SGPRs (dK/dV kernel)
+  const int qb = __builtin_amdgcn_readfirstlane(CAUSAL ? nqb - 1 - w % nqb : w % nqb);  // heaviest first
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, g = l >> 4, col = l & 15;
   const int query = qb * WB + wave * 16 + col;
@@ -616,22 +641,20 @@ __global__ __launch_bounds__(64 * nwave<D>(), 1) void bwd_dq_kernel(
   auto tile_of = [&](int it) { return it; };
   auto issue = [&](int it, uint8_t* buf) {
     const int kt = tile_of(it), t0 = kt * BB;
-    for (int j = wave; j < NJ; j += NWAVE) {
-      if (j < JK) {
-        if constexpr (MXS) {
-          if (j < T::W4) copy4_job<D>(j, l, f.kc + bh * N * (D / 2), t0, N, buf);
-          else if (l < T::TS / 16) lds_copy16(f.kt + (bh * nk + kt) * T::TS + 16 * l, buf + T::T4);
-        } else {
-          copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(kh + bh * N * D), t0, N, buf);
-        }
-      } else if (j < JK + T::W16) {
-        copy16_job<D>(j - JK, l, reinterpret_cast<const uint8_t*>(v + bh * N * D), t0, N, buf + O_V);
-      } else if (j < JK + T::W16 + T::W8) {
-        copy8_job(j - JK - T::W16, l, k8 + bh * D * Np + t0, Np, buf + O_K8);
-      } else if (l < D / 4) {
-        lds_copy16(k8s + (bh * nk + kt) * D + 4 * l, buf + O_KS);
-      }
+    constexpr int J8 = JK + T::W16;  // first INT8 job
+    if constexpr (MXS) {
+      wave_jobs<0, T::W4, NWAVE>(wave, [&](int j) { copy4_job<D>(j, l, f.kc + bh * N * (D / 2), t0, N, buf); });
+      wave_jobs<T::W4, JK, NWAVE>(wave, [&](int) { lds_copy16(f.kt + (bh * nk + kt) * T::TS, T::TS, 16 * l, buf + T::T4); });
+    } else {
+      wave_jobs<0, JK, NWAVE>(wave, [&](int j) {
+        copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(kh + bh * N * D), t0, N, buf);
+      });
     }
+    wave_jobs<JK, J8, NWAVE>(wave, [&](int j) {
+      copy16_job<D>(j, l, reinterpret_cast<const uint8_t*>(v + bh * N * D), t0, N, buf + O_V);
+    });
+    wave_jobs<J8, J8 + T::W8, NWAVE>(wave, [&](int j) { copy8_job<D>(j, l, k8 + bh * D * Np + t0, Np, t0, buf + O_K8); });
+    wave_jobs<J8 + T::W8, NJ, NWAVE>(wave, [&](int) { lds_copy16(k8s + (bh * nk + kt) * D, 4 * D, 16 * l, buf + O_KS); });
   };
 
   issue(0, lds[0]);
