@@ -87,9 +87,10 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// max(a, b) in one v_max_f32. For operands that arrive as bit patterns (a lane swap) the compiler
-// quiets each one first (v_max x, x, x) in case it is a signalling NaN; scores and their maxima
-// never are NaN, so the plain instruction gives the same value.
+// max(a, b) in one v_max_f32. Without -fno-honor-nans the compiler quiets each operand that
+// arrives as a bit pattern (a lane swap) first (v_max x, x, x), in case it is a signalling NaN;
+// this form does not depend on that flag. Scores and their maxima never are NaN, so the plain
+// instruction gives the same value.
 __device__ __forceinline__ float max2f(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
