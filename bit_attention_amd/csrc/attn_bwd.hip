@@ -24,7 +24,7 @@
 //   - dK/dV kernel, one workgroup of 12 (D = 128) or 16 (D = 64) waves per (batch*head, block of
 //     192 or 256 keys): each wave owns 16 keys and keeps their K^ (bf16, or MXFP4 codes) and
 //     V (fp16) rows as MFMA B operands in registers while 64-query tiles stream into LDS by
-//     asynchronous global-to-LDS copies (global_load_lds), double-buffered, one barrier per
+//     asynchronous buffer loads into LDS (buffer_load ... lds), double-buffered, one barrier per
 //     tile. S = Q^ K^T and dP = dO V^T take 16x16x32 MFMAs (with MXFP4 Q and K, S takes one
 //     block-scaled FP4 16x16x128 MFMA per subtile on the codes themselves); a lane then holds 16
 //     (query, key) values of one key, at queries 16s + 4g + i
