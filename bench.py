@@ -237,7 +237,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+        print("bench.py: the benchmark runs on exactly one GPU; multi-GPU runs are not supported "
               "(every (batch, head) is independent, so heads would shard with no exchange).",
               file=sys.stderr)
         sys.exit(2)
