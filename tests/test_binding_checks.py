@@ -9,7 +9,8 @@ import torch
 from bit_attention_amd import binding as bnd
 
 LAUNCHING = ["sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p", "sage_fp4_attn_fwd_lse",
-             "sage_fp4_attn_bwd", "sage_fp4_attn_bwd_stage"]
+             "sage_fp4_attn_bwd", "sage_fp4_attn_bwd_stage", "sage_fp4_kv16_prep", "sage_fp4_quant_kv16",
+             "sage_fp4_attn_fwd_kv16"]
 
 
 @pytest.fixture(autouse=True)
@@ -77,3 +78,32 @@ def test_attn_bwd_rejects_small_workspace_and_bad_gradients():
         bnd.attn_bwd_into(bnd.NVFP4, q, k, v, o, do, lse[:-1], *grads, ws)
     with pytest.raises(ValueError, match="q codes"):
         bnd.attn_bwd_into(bnd.NVFP4, _pair(bnd.ROLE_Q, shrink=1), k, v, o, do, lse, *grads, ws)
+
+
+def test_kv16_wrappers_reject_short_buffers_and_bad_roles():
+    B, H, N, D = SHAPE
+    need = bnd.sage_fp4_kv16_bytes(*SHAPE)
+    k, v = _pair(bnd.ROLE_K), _pair(bnd.ROLE_V)
+    with pytest.raises(ValueError, match="kv16"):
+        bnd.kv16_prep(k, v, SHAPE, torch.zeros(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="v codes"):
+        bnd.kv16_prep(k, _pair(bnd.ROLE_V, shrink=16), SHAPE, torch.zeros(need, dtype=torch.uint8))
+    x = torch.zeros(SHAPE, dtype=torch.float16)
+    kv = torch.zeros(need, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="role"):
+        bnd.quant_kv16_into(x, bnd.ROLE_Q, *_pair(bnd.ROLE_Q), kv)
+    with pytest.raises(ValueError, match="kv16"):
+        bnd.quant_kv16_into(x, bnd.ROLE_K, *k, kv[:-1])
+    with pytest.raises(ValueError, match="codes"):
+        bnd.quant_kv16_into(x, bnd.ROLE_V, *_pair(bnd.ROLE_V, shrink=1), kv)
+    with pytest.raises(TypeError):
+        bnd.quant_kv16_into(x.float(), bnd.ROLE_K, *k, kv)
+    with pytest.raises(ValueError, match="shape"):
+        bnd.quant_kv16(x, torch.zeros(B, H, N + 1, D, dtype=torch.float16), kv16=kv)
+    q = _pair(bnd.ROLE_Q)
+    with pytest.raises(ValueError, match="kv16"):
+        bnd.attn_fwd_kv16_into(q, kv[:-1], SHAPE, torch.zeros(SHAPE))
+    with pytest.raises(ValueError, match="exactly"):
+        bnd.attn_fwd_kv16_into(q, kv, SHAPE, torch.zeros(B * H * N * D - 1))
+    with pytest.raises(ValueError, match="lse"):
+        bnd.attn_fwd_kv16_into(q, kv, SHAPE, torch.zeros(SHAPE), lse=torch.zeros(B * H * N - 1))

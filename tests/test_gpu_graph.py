@@ -58,10 +58,13 @@ def test_graph_replays_match_eager(fmt, direct_p, causal):
         assert bool(torch.isfinite(out).all())
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_graph_kv16_replays_match_eager(causal):
-    """Three quantisations, sage_fp4_kv16_prep and sage_fp4_attn_fwd_kv16 (with lse) captured as
-    one graph: every replay, with new inputs written between replays, equals the eager run."""
+def test_graph_kv16_replays_match_eager(causal, fused):
+    """The kv16 path captured as one graph: Q quantised, K and V either quantised and then
+    dequantised by sage_fp4_kv16_prep or quantised by sage_fp4_quant_kv16 (fused), then
+    sage_fp4_attn_fwd_kv16 with lse. Every replay, with new inputs written between replays, equals
+    the eager run."""
     B, H, N, D = 2, 3, 500, 64
     shape = (B, H, N, D)
     fmt = bnd.NVFP4
@@ -74,9 +77,13 @@ def test_graph_kv16_replays_match_eager(causal):
 
     def step():
         bnd.quant_into(q, bnd.ROLE_Q, fmt, *Q)
-        bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
-        bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
-        bnd.kv16_prep(K, V, shape, kv)
+        if fused:
+            bnd.quant_kv16_into(k, bnd.ROLE_K, *K, kv)
+            bnd.quant_kv16_into(v, bnd.ROLE_V, *V, kv)
+        else:
+            bnd.quant_into(k, bnd.ROLE_K, fmt, *K)
+            bnd.quant_into(v, bnd.ROLE_V, fmt, *V)
+            bnd.kv16_prep(K, V, shape, kv)
         bnd.attn_fwd_kv16_into(Q, kv, shape, out, causal=causal, lse=lse)
 
     side = torch.cuda.Stream()
@@ -99,7 +106,7 @@ def test_graph_kv16_replays_match_eager(causal):
         out.fill_(float("nan")); lse.fill_(float("nan")); kv.fill_(0x7B)
         step()
         torch.cuda.synchronize()
-        say(f"  kv16 replay {r}: causal={causal}")
+        say(f"  kv16 replay {r}: causal={causal} fused={fused}")
         assert torch.equal(got_out, out), f"replay {r}: output differs from eager"
         assert torch.equal(got_lse, lse), f"replay {r}: lse differs from eager"
         assert bool(torch.isfinite(out).all())
