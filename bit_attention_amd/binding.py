@@ -20,6 +20,7 @@ OUT_F16, OUT_F32 = 0, 1
 BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 STATUS = {0: "SAGE_OK", -1: "SAGE_ERR_NULL", -2: "SAGE_ERR_SHAPE", -3: "SAGE_ERR_HEAD_DIM",
           -4: "SAGE_ERR_ALIGN", -5: "SAGE_ERR_ENUM", -6: "SAGE_ERR_HIP", -7: "SAGE_ERR_WORKSPACE"}
+ERR_SHAPE = -2  # SAGE_ERR_SHAPE: raised here when a size query returns 0 for the shape
 EXPORTS = ["sage_fp4_version", "sage_fp4_kv_tile", "sage_fp4_slot_token", "sage_fp4_codes_bytes",
            "sage_fp4_scales_bytes", "sage_fp4_quant", "sage_fp4_attn_fwd", "sage_fp4_attn_fwd_direct_p",
            "sage_fp4_attn_fwd_lse", "sage_fp4_kv16_bytes", "sage_fp4_kv16_prep", "sage_fp4_quant_kv16",
@@ -209,7 +210,7 @@ def _check_codes(pair, role, fmt, shape, device, what):
     B, H, N, D = shape
     nc, ns = _sizes(role, fmt, B, H, N, D)
     if nc == 0 or ns == 0:
-        raise SageError(-2, f"{what}: shape {shape}")
+        raise SageError(ERR_SHAPE, f"{what}: shape {shape}")
     _check(pair[0], torch.uint8, f"{what} codes", device, min_numel=nc)
     _check(pair[1], torch.uint8, f"{what} scales", device, min_numel=ns)
 
@@ -219,7 +220,7 @@ def alloc_quant(role, fmt, B, H, N, D, device="cuda"):
     nc = sage_fp4_codes_bytes(role, fmt, B, H, N, D)
     ns = sage_fp4_scales_bytes(role, fmt, B, H, N, D)
     if nc == 0 or ns == 0:
-        raise SageError(-2, "sage_fp4_codes_bytes")
+        raise SageError(ERR_SHAPE, "sage_fp4_codes_bytes")
     return (torch.empty(nc, dtype=torch.uint8, device=device),
             torch.empty(ns, dtype=torch.uint8, device=device))
 
@@ -347,7 +348,7 @@ def quant_kv16(k, v, kv16=None, stream=None):
     B, H, N, D = k.shape
     need = sage_fp4_kv16_bytes(B, H, N, D)
     if need == 0:
-        raise SageError(-2, f"sage_fp4_kv16_bytes: shape {tuple(k.shape)}")
+        raise SageError(ERR_SHAPE, f"sage_fp4_kv16_bytes: shape {tuple(k.shape)}")
     if kv16 is None:
         kv16 = torch.empty(need, dtype=torch.uint8, device=k.device)
     K = quant_kv16_into(k, ROLE_K, *alloc_quant(ROLE_K, NVFP4, B, H, N, D, device=k.device), kv16, stream)
@@ -381,7 +382,7 @@ def alloc_bwd_workspace(B, H, N, D, device="cuda"):
     import torch
     n = sage_fp4_attn_bwd_workspace_bytes(B, H, N, D)
     if n == 0:
-        raise SageError(-2, "sage_fp4_attn_bwd_workspace_bytes")
+        raise SageError(ERR_SHAPE, "sage_fp4_attn_bwd_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
